@@ -1,0 +1,269 @@
+"""CPU oracle for DSA token selection and attention over the selected tokens.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the package entry
+point and the CPU-baseline leg of the benchmark may import or call this module.
+The GPU product path never does, and nothing here is shared with it.
+
+Every step is written in float64 NumPy in the order the method states it, one
+output at a time where that is clearest, with no blocking, fusion or reordering.
+Results are rounded once, round-to-nearest-even, to the stored output dtype.
+
+Sources (the "GLM-5.3 DSA" API pages):
+  [DSA]   page "Module glm5next_dsa" (GLM-5.3-Flash DSA production surface):
+          sections "Shape of the pipeline", "Traps carried from Slice 8",
+          "Constants" (KERNEL_MAX_KPOOL).
+  [TP]    page "Module tp" (GLM-5.3 DSA tensor-parallel shard plan):
+          section "Why the indexer is REPLICATED, not sharded".
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes of the repository):
+  R1  k_norm is applied to the pooled keys, inside the score step.
+  R2  LayerNorm epsilon is an argument (1e-5 in the workloads), variance biased.
+  R3  ape is [kpool, D], one row per slot; gate is per token and channel.
+  R4  w is [Q, H] (one weight per query row and head).
+  R5  A pool is a candidate for row q iff it is valid and its last token is at
+      or before the row's own position (pool_start + kpool - 1 <= row_pos[q]).
+  R6  "Candidate validity" is carried as -inf in the score tensor.
+  R7  The selected list is ordered by (score descending, pool index ascending);
+      rows with fewer candidates than select_k are padded with -1.  +0 and -0 tie.
+  R8  Expansion is pool-major in selection order, slots ascending; token ids
+      are absolute positions in the sequence's row; every column past
+      select_k*kpool is -1.
+  R9  A pool that contains an invalid token (a hole) is not valid; the anchor is
+      still the first valid token.
+  R10 The sparse attention attends to the listed token ids only (entries -1 are
+      skipped); with none it returns 0 and lse = -inf.  The softmax scale is an
+      argument.
+  R11 Pools p >= n_pools (and every pool of a sequence with no valid token) are
+      written as k_pool = 0, pool_start = -1, pool_valid = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# [DSA] "Constants", KERNEL_MAX_KPOOL: the most pool slots the reference
+# compression kernel holds.  Larger values are refused, never truncated.
+MAX_KPOOL = 8
+
+
+# --------------------------------------------------------------------------
+# rounding of a float64 result to its stored dtype
+# --------------------------------------------------------------------------
+def round_f32(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32, round-to-nearest-even (one rounding)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (RNE, one rounding), returned as float32.
+
+    bfloat16 keeps 8 significant bits.  With x = m * 2**e (0.5 <= |m| < 1), the
+    spacing of bf16 values around x is 2**(e-8); x / spacing is exact in
+    float64 and np.rint rounds half to even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    _, e = np.frexp(x[nz])
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))   # bf16 subnormal spacing is 2**-133
+    out[nz] = np.rint(x[nz] / q) * q
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out.astype(np.float32)
+
+
+def f64(t) -> np.ndarray:
+    """Any tensor/array (fp32, bf16, int) -> exact float64 NumPy copy."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            return t.detach().to(torch.float64).cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(t, dtype=np.float64)
+
+
+def _i(t) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            return t.detach().cpu().numpy().astype(np.int64)
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(t).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# kpool_compress   [DSA] "Shape of the pipeline" (k, gate, valid, ape ->
+# pool keys / indices / valid) and "Traps": softmax over the pool-slot axis per
+# channel; pooling anchored at the first valid token; a pool counts only if
+# every slot is valid (a trailing partial pool is not a pool); kpool <= 8.
+# --------------------------------------------------------------------------
+def anchor(valid_row: np.ndarray, T_b: int, kp: int) -> tuple[int, int]:
+    """(first valid token f_b, number of whole pools after it).
+
+    f_b is the first valid token among the first T_b; with no valid token the
+    sequence has no pools (f_b is reported as T_b).  The pools are the whole
+    runs of kp tokens starting at f_b that end inside [0, T_b).
+    """
+    idx = np.flatnonzero(np.asarray(valid_row[:T_b]) != 0)
+    if idx.size == 0:
+        return T_b, 0
+    f_b = int(idx[0])
+    return f_b, (T_b - f_b) // kp
+
+
+def kpool_compress(k, gate, valid, ape, seq_len, kp: int, P_max: int) -> dict:
+    """Pooled index keys.
+
+    k, gate: [B, T_max, D]; valid: [B, T_max] (nonzero = valid token);
+    ape: [kp, D]; seq_len: [B].  Returns float64 arrays
+    k_pool [B, P_max, D], int64 pool_start / n_pools / first_valid, bool pool_valid.
+
+    For pool p of sequence b, slots s = 0..kp-1 are tokens t_s = f_b + p*kp + s.
+    Per channel c the slot logits are l_s = gate[b,t_s,c] + ape[s,c]; the weights
+    a_s are the softmax of l over s; k_pool[b,p,c] = sum_s a_s * k[b,t_s,c].
+    """
+    if not (1 <= kp <= MAX_KPOOL):
+        raise ValueError(f"kpool {kp} outside [1, {MAX_KPOOL}]")
+    k = f64(k); gate = f64(gate); ape = f64(ape)
+    valid = _i(valid); seq_len = _i(seq_len)
+    B, T_max, D = k.shape
+    if P_max < T_max // kp:
+        raise ValueError("P_max smaller than T_max // kpool")
+    k_pool = np.zeros((B, P_max, D))
+    pool_start = np.full((B, P_max), -1, dtype=np.int64)
+    pool_valid = np.zeros((B, P_max), dtype=bool)
+    n_pools = np.zeros(B, dtype=np.int64)
+    first_valid = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        T_b = int(seq_len[b])
+        f_b, n = anchor(valid[b], T_b, kp)
+        first_valid[b] = f_b
+        n_pools[b] = n
+        for p0 in range(0, n, 8192):                   # pools in chunks (memory only)
+            p = np.arange(p0, min(n, p0 + 8192))
+            t = f_b + p[:, None] * kp + np.arange(kp)[None, :]   # [np, kp] slot tokens
+            logits = gate[b][t] + ape[None, :, :]       # [np, kp, D]
+            m = logits.max(axis=1, keepdims=True)       # per pool and channel
+            e = np.exp(logits - m)
+            a = e / e.sum(axis=1, keepdims=True)        # softmax over the slot axis
+            k_pool[b, p, :] = (a * k[b][t]).sum(axis=1)
+            pool_start[b, p] = t[:, 0]
+            pool_valid[b, p] = np.all(valid[b][t] != 0, axis=1)
+    return dict(k_pool=k_pool, pool_start=pool_start, pool_valid=pool_valid,
+                n_pools=n_pools, first_valid=first_valid)
+
+
+# --------------------------------------------------------------------------
+# index_scores   [DSA] "Shape of the pipeline" (-> [Q, P] scores + candidate
+# validity) and "Traps" (k_norm is nn.LayerNorm: mean-subtracting, with bias);
+# [TP] "Why the indexer is REPLICATED": the score is a plain sum over heads of
+# weights[h] * relu(scale * dot).
+# --------------------------------------------------------------------------
+def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis with biased variance, scale gamma and bias beta."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def candidates(pool_start_b, pool_valid_b, kp: int, row_pos: int) -> np.ndarray:
+    """Pools row q may select: valid, and ending at or before the row's position."""
+    return np.asarray(pool_valid_b, dtype=bool) & (np.asarray(pool_start_b) + kp - 1 <= row_pos)
+
+
+def index_scores(q, w, scale: float, k_pool, pool_start, pool_valid, gamma, beta, eps: float,
+                 row_seq, row_pos, kp: int, rows=None) -> np.ndarray:
+    """scores[q, p] = sum_h w[q,h] * max(0, scale * <q[q,h,:], LN(k_pool[b,p,:])>)
+    for candidate pools, -inf otherwise; b = row_seq[q].  Returns float32 [len(rows), P_max].
+    """
+    q = f64(q); w = f64(w); k_pool = f64(k_pool); gamma = f64(gamma); beta = f64(beta)
+    pool_start = _i(pool_start); pool_valid = _i(pool_valid)
+    row_seq = _i(row_seq); row_pos = _i(row_pos)
+    Q = q.shape[0]
+    rows = range(Q) if rows is None else list(rows)
+    P_max = k_pool.shape[1]
+    out = np.empty((len(rows), P_max), dtype=np.float32)
+    normed = {}
+    for i, r in enumerate(rows):
+        b = int(row_seq[r])
+        if b not in normed:
+            normed[b] = layer_norm(k_pool[b], gamma, beta, eps)     # [P_max, D]
+        kn = normed[b]
+        dots = kn @ q[r].T                                         # [P_max, H]
+        s = (w[r][None, :] * np.maximum(0.0, scale * dots)).sum(axis=1)
+        cand = candidates(pool_start[b], pool_valid[b], kp, int(row_pos[r]))
+        out[i] = np.where(cand, round_f32(s), np.float32(-np.inf))
+    return out
+
+
+# --------------------------------------------------------------------------
+# topk_pools   [DSA] "Shape of the pipeline" (-> [Q, select_k] pool ids);
+# [TP] "Why the indexer is REPLICATED": deterministic tiebreak, higher score
+# first, then the smaller pool index.
+# --------------------------------------------------------------------------
+def topk_pools(scores, K: int) -> np.ndarray:
+    """pool_ids[q, j] = j-th candidate of row q in (score desc, index asc) order,
+    -1 when the row has fewer than K candidates.  Scores are compared as IEEE
+    values (so +0 == -0); -inf marks a non-candidate; NaN is not allowed."""
+    s = np.asarray(scores, dtype=np.float32)
+    if np.isnan(s).any():
+        raise ValueError("NaN score")
+    Q, P = s.shape
+    out = np.full((Q, K), -1, dtype=np.int32)
+    for r in range(Q):
+        cand = np.flatnonzero(s[r] != -np.inf)
+        vals = s[r, cand].astype(np.float64)
+        vals = np.where(vals == 0.0, 0.0, vals)              # -0 ties with +0
+        order = np.lexsort((cand, -vals))                    # primary: -score; then index
+        take = cand[order[:K]]
+        out[r, :take.size] = take
+    return out
+
+
+# --------------------------------------------------------------------------
+# expand_selection   [DSA] "Shape of the pipeline" (-> [Q, out_width] token
+# ids, -1 = invalid) and "Traps": the -1 sentinel destination is fully written.
+# --------------------------------------------------------------------------
+def expand_selection(pool_ids, row_seq, pool_start, kp: int, W: int) -> np.ndarray:
+    pool_ids = _i(pool_ids); row_seq = _i(row_seq); pool_start = _i(pool_start)
+    Q, K = pool_ids.shape
+    if W < K * kp:
+        raise ValueError("out_width smaller than select_k * kpool")
+    tok = np.full((Q, W), -1, dtype=np.int32)
+    for r in range(Q):
+        b = int(row_seq[r])
+        for j in np.flatnonzero(pool_ids[r] >= 0):
+            p = pool_ids[r, j]
+            tok[r, j * kp:(j + 1) * kp] = pool_start[b, p] + np.arange(kp)
+    return tok
+
+
+# --------------------------------------------------------------------------
+# sparse MLA decode   [DSA] "Shape of the pipeline" (NoPE MLA restricted to
+# the selected tokens) and "Traps" (NoPE: the rotary slice is zero-width);
+# [TP] "Traps": kv_a_proj_with_mqa yields one shared latent per token, no head
+# axis -- so the cache is [B, T, Dl] and, absorbed, keys = values = latent.
+# --------------------------------------------------------------------------
+def sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, rows=None):
+    """out[q,h,:] = sum_j softmax_j(sm_scale * <q_lat[q,h], kv[b,j]>) kv[b,j]
+    over the listed ids j >= 0 of row q (b = row_seq[q]); lse[q,h] = log-sum-exp
+    of those logits.  Returns float64 (out [R, Hm, Dl], lse [R, Hm])."""
+    q_lat = f64(q_lat); row_seq = _i(row_seq); token_ids = _i(token_ids)
+    Q, Hm, Dl = q_lat.shape
+    rows = range(Q) if rows is None else list(rows)
+    out = np.zeros((len(rows), Hm, Dl))
+    lse = np.full((len(rows), Hm), -np.inf)
+    for i, r in enumerate(rows):
+        b = int(row_seq[r])
+        ids = token_ids[r][token_ids[r] >= 0]
+        if ids.size == 0:
+            continue
+        V = f64(kv[b, ids])                                   # [n, Dl] gathered latents
+        logits = sm_scale * (q_lat[r] @ V.T)                  # [Hm, n]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        l = e.sum(axis=1, keepdims=True)
+        out[i] = (e @ V) / l
+        lse[i] = (m + np.log(l))[:, 0]
+    return out, lse
