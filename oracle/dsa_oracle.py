@@ -28,7 +28,8 @@ design notes of the repository):
       rows with fewer candidates than select_k are padded with -1.  +0 and -0 tie.
   R8  Expansion is pool-major in selection order, slots ascending; token ids
       are absolute positions in the sequence's row; every column past
-      select_k*kpool is -1.
+      select_k*kpool is -1, and so are the slots of a selected id that names
+      no pool (pool_start = -1).
   R9  A pool that contains an invalid token (a hole) is not valid; the anchor is
       still the first valid token.
   R10 The sparse attention attends to the listed token ids only (entries -1 are
@@ -235,6 +236,8 @@ def expand_selection(pool_ids, row_seq, pool_start, kp: int, W: int) -> np.ndarr
         b = int(row_seq[r])
         for j in np.flatnonzero(pool_ids[r] >= 0):
             p = pool_ids[r, j]
+            if pool_start[b, p] < 0:                # an id that names no pool is invalid
+                continue
             tok[r, j * kp:(j + 1) * kp] = pool_start[b, p] + np.arange(kp)
     return tok
 

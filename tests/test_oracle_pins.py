@@ -399,3 +399,9 @@ def test_mla_rows_use_their_own_sequence():
     only0, _ = O.sparse_mla_decode(q[1:], kv[:1], [0], ids[:1], 0.4)
     np.testing.assert_array_equal(both[0], only1[0])
     np.testing.assert_array_equal(both[1], only0[0])
+
+
+def test_expand_id_naming_no_pool_gives_sentinel():
+    pool_start = np.array([[2, 6, -1, -1]])
+    tok = O.expand_selection(np.array([[1, 2, -1]]), [0], pool_start, 4, 14)
+    assert tok.tolist() == [[6, 7, 8, 9] + [-1] * 10]
