@@ -1,0 +1,244 @@
+"""DSA decode step benchmark on one MI355X.
+
+A step is one decode token for every sequence of the batch through the whole
+hot path: dsa_index_scores -> dsa_topk_pools -> dsa_expand_selection ->
+dsa_sparse_mla_decode, on the long-context workload (4 sequences of 262144
+tokens, kpool 4 -> 65536 pools each, 32 index heads x 128, select_k 512 pools =
+2048 tokens, 64-head absorbed MLA over a 512-wide latent, bf16).  The pooled-key
+cache comes from an untimed dsa_kpool_compress over synthetic tokens.
+
+Inputs are resident in HBM before the timed region.  Eight replicas of the
+pool cache and of the latent cache (about 8.5 GiB) rotate from step to step, so
+the 256 MB last-level cache cannot serve a step from the previous one.  Each
+step is replayed from HIP graphs captured per replica (one graph holding the
+score kernel, one the rest); HIP events on the same stream bracket the score
+graph of every timed step, which gives that kernel's per-launch time for the
+roofline line.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode steps/s (indexer+top-k+sparse MLA) @262K ctx; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+REPLICAS = 8
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
+    return ap.parse_args()
+
+
+def score_bytes_per_pool() -> int:
+    # key row (128 bf16) + pool_valid (u8) + pool_start (i32) read, score (fp32) written
+    return 128 * 2 + 1 + 4 + 4
+
+
+def main() -> int:
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path is not "
+              "sharded across GPUs", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from dsa_decode_amd import _lib, ops, synth
+
+    _lib.load()
+    torch.cuda.set_device(0)
+    dev = lambda t: t.contiguous().cuda()
+
+    wl = synth.workload("long")
+    Q, P, K, W = wl.Q, wl.P_max, wl.K, wl.W
+    ti = synth.token_inputs(wl)
+    ip = synth.index_params(wl)
+    mi = synth.mla_inputs(wl)
+
+    # pool cache: one compress on the GPU, then replicas
+    comp = ops.dsa_kpool_compress(dev(ti["k"]), dev(ti["gate"]), dev(ti["valid"]), dev(ti["ape"]),
+                                  dev(ti["seq_len"]), wl.kp, P)
+    del ti
+    kv0 = dev(mi["kv"])
+    reps = []
+    for i in range(REPLICAS):
+        reps.append(dict(k_pool=comp["k_pool"].clone(), pool_start=comp["pool_start"].clone(),
+                         pool_valid=comp["pool_valid"].clone(), kv=kv0 if i == 0 else kv0.clone(),
+                         scores=torch.empty((Q, P), dtype=torch.float32, device="cuda"),
+                         ids=torch.empty((Q, K), dtype=torch.int32, device="cuda"),
+                         tok=torch.empty((Q, W), dtype=torch.int32, device="cuda"),
+                         out=torch.empty((Q, wl.Hm, wl.Dl), dtype=torch.bfloat16, device="cuda"),
+                         lse=torch.empty((Q, wl.Hm), dtype=torch.float32, device="cuda")))
+    q, w, gamma, beta = dev(ip["q"]), dev(ip["w"]), dev(ip["gamma"]), dev(ip["beta"])
+    row_seq, row_pos = dev(ip["row_seq"]), dev(ip["row_pos"])
+    q_lat = dev(mi["q_lat"])
+    tk_ws = torch.empty(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    mla_ws = torch.empty(max(1, ops.dsa_sparse_mla_workspace_bytes(Q, wl.Hm, wl.Dl, W, ops.DSA_BF16)),
+                         dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def scores_stage(r):
+        ops.dsa_index_scores(q, w, ip["scale"], r["k_pool"], r["pool_start"], r["pool_valid"], gamma, beta,
+                             ip["eps"], row_seq, row_pos, wl.kp, scores=r["scores"])
+
+    def rest_stages(r):
+        ops.dsa_topk_pools(r["scores"], K, pool_ids=r["ids"], workspace=tk_ws)
+        ops.dsa_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, W, token_ids=r["tok"])
+        ops.dsa_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], out=r["out"], lse=r["lse"],
+                                  workspace=mla_ws)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    if args.mode == "graph":
+        g_scores, g_rest = [], []
+        with torch.cuda.stream(stream):
+            for r in reps:  # one eager pass on the capture stream first
+                scores_stage(r)
+                rest_stages(r)
+        stream.synchronize()
+        for r in reps:
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga, stream=stream):
+                scores_stage(r)
+            with torch.cuda.graph(gb, stream=stream):
+                rest_stages(r)
+            g_scores.append(ga)
+            g_rest.append(gb)
+        run_scores = lambda i: g_scores[i].replay()
+        run_rest = lambda i: g_rest[i].replay()
+    else:
+        run_scores = lambda i: scores_stage(reps[i])
+        run_rest = lambda i: rest_stages(reps[i])
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            run_scores(i % REPLICAS)
+            run_rest(i % REPLICAS)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            j = i % REPLICAS
+            ev[i][0].record(stream)
+            run_scores(j)
+            ev[i][1].record(stream)
+            run_rest(j)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    score_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    score_us_mean = float(np.mean(score_us))
+
+    # per-stage breakdown (separate instrumented pass, eager launches, events around each stage)
+    stage_names = ["index_scores", "topk_pools", "expand_selection", "sparse_mla_decode"]
+    stage_t = {n: [] for n in stage_names}
+    with torch.cuda.stream(stream):
+        for i in range(min(64, args.steps)):
+            r = reps[i % REPLICAS]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[0].record(stream)
+            scores_stage(r)
+            e[1].record(stream)
+            ops.dsa_topk_pools(r["scores"], K, pool_ids=r["ids"], workspace=tk_ws)
+            e[2].record(stream)
+            ops.dsa_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, W, token_ids=r["tok"])
+            e[3].record(stream)
+            ops.dsa_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], out=r["out"],
+                                      lse=r["lse"], workspace=mla_ws)
+            e[4].record(stream)
+            stream.synchronize()
+            for k, n in enumerate(stage_names):
+                stage_t[n].append(e[k].elapsed_time(e[k + 1]) * 1e3)
+    stages_us = {n: round(float(np.median(v)), 2) for n, v in stage_t.items()}
+
+    bytes_per_launch = score_bytes_per_pool() * Q * P + q.numel() * 2 + w.numel() * 4 + 2 * 128 * 4
+    achieved = bytes_per_launch / (score_us_mean * 1e-6) / 1e9
+    steps_per_s = 1e3 / ms_per_step
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ip, mi, comp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long-context decode: batch 4 x 262144 tokens, kpool 4 (65536 pools/seq), "
+                               "32 index heads x 128, select_k 512 pools (2048 tokens), absorbed NoPE MLA "
+                               "64 heads x 512 latent, bf16",
+                   "batch": Q, "context": wl.T_max, "kpool": wl.kp, "select_k": K, "mode": args.mode,
+                   "replicas": REPLICAS},
+        "tokens_per_s": round(steps_per_s * Q, 1),
+        "stages_us": stages_us,
+        "roofline": {"bound": "hbm", "kernel": "index_scores_mfma", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launch_us": round(score_us_mean, 3),
+                     "algorithmic_bytes": bytes_per_launch},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
+    """The oracle (as it is) on a bounded sample of the same step: decode rows of
+    the same workload, each through scores -> top-k -> expand -> sparse MLA,
+    repeated until about budget_s of CPU work; scaled to steps/s (4 rows/step)."""
+    import numpy as np
+    import torch
+    from oracle import dsa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    pc = dict(k_pool=comp["k_pool"].cpu(), pool_start=comp["pool_start"].cpu(), pool_valid=comp["pool_valid"].cpu())
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        r = rows_done % wl.Q
+        s = O.index_scores(ip["q"], ip["w"], ip["scale"], pc["k_pool"], pc["pool_start"], pc["pool_valid"],
+                           ip["gamma"], ip["beta"], ip["eps"], ip["row_seq"], ip["row_pos"], wl.kp, rows=[r])
+        ids = O.topk_pools(s, wl.K)
+        tok = O.expand_selection(ids, ip["row_seq"].numpy()[[r]], pc["pool_start"].numpy(), wl.kp, wl.W)
+        O.sparse_mla_decode(mi["q_lat"][[r]], mi["kv"], ip["row_seq"][[r]], tok, mi["sm_scale"])
+        rows_done += 1
+        if time.perf_counter() - t0 >= budget_s and rows_done >= 1:
+            break
+    el = time.perf_counter() - t0
+    steps = rows_done / wl.Q
+    return {"value": round(steps / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} decode rows of the same workload (scores over 65536 pools, top-k, "
+                      f"expand, sparse MLA per row) in {el:.1f} s; 4 rows = 1 step"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

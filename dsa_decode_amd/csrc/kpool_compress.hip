@@ -1,0 +1,160 @@
+// kpool_compress: pooled index keys (page "Module glm5next_dsa", "Shape of the
+// pipeline" and "Traps carried from Slice 8": slot-axis softmax per channel,
+// anchored at the first valid token, full pools only; kpool <= 8 per
+// "Constants", KERNEL_MAX_KPOOL).
+//
+// Two launches: an anchor kernel (one workgroup per sequence finds the first
+// valid token and the number of whole pools), then a pool kernel with one
+// thread per (pool, 8-channel group).  The pool kernel is HBM-bound: it reads
+// kpool token rows of k and gate (2 * kpool * 2 B per channel for bf16) and
+// writes one pooled row; the kpool <= 8 slot logits of each channel live in
+// registers.
+#include "dsa_common.hpp"
+#include "dsa_host.hpp"
+
+namespace dsa {
+
+constexpr int kAnchorThreads = 256;
+constexpr int kAnchorBytes = 16;  // valid bytes examined per thread per window
+
+__global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const uint8_t* __restrict__ valid,
+                                                                const int32_t* __restrict__ seq_len,
+                                                                int T_max, int kp,
+                                                                int32_t* __restrict__ n_pools,
+                                                                int32_t* __restrict__ first_valid) {
+  const int b = blockIdx.x;
+  int L = seq_len[b];
+  L = L < 0 ? 0 : (L > T_max ? T_max : L);
+  const uint8_t* v = valid + size_t(b) * T_max;
+  __shared__ int s_first;
+  if (threadIdx.x == 0) s_first = L;
+  __syncthreads();
+  // Windows of kAnchorThreads * kAnchorBytes tokens, front to back; stop at the
+  // first window that holds a valid token (the smallest index in it wins).
+  for (int base = 0; base < L; base += kAnchorThreads * kAnchorBytes) {
+    const int t0 = base + threadIdx.x * kAnchorBytes;
+    int found = L;
+    for (int i = 0; i < kAnchorBytes; ++i) {
+      const int t = t0 + i;
+      if (t < L && v[t] != 0) { found = t; break; }
+    }
+    if (found < L) atomicMin(&s_first, found);
+    __syncthreads();
+    const int f = s_first;
+    __syncthreads();
+    if (f < L) break;  // uniform: every thread read the same value
+  }
+  if (threadIdx.x == 0) {
+    const int f = s_first;
+    first_valid[b] = f;
+    n_pools[b] = f < L ? (L - f) / kp : 0;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kernel(
+    const T* __restrict__ k, const T* __restrict__ gate, const uint8_t* __restrict__ valid,
+    const float* __restrict__ ape, int T_max, int D, int kp, int P_max,
+    const int32_t* __restrict__ n_pools, const int32_t* __restrict__ first_valid,
+    T* __restrict__ k_pool, int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid) {
+  const int b = blockIdx.y;
+  const int groups = D >> 3;
+  const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= long(P_max) * groups) return;
+  const int p = int(gid / groups);
+  const int c0 = int(gid % groups) * 8;
+  const int n = n_pools[b];
+  T* dst = k_pool + (size_t(b) * P_max + p) * D + c0;
+  float acc[8];
+  if (p >= n) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    store8(dst, acc);
+    if (c0 == 0) {
+      pool_start[size_t(b) * P_max + p] = -1;
+      pool_valid[size_t(b) * P_max + p] = 0;
+    }
+    return;
+  }
+  const int t0 = first_valid[b] + p * kp;
+  const size_t row0 = size_t(b) * T_max + t0;
+  // slot logits gate + ape, per channel; max over the slot axis
+  float lg[DSA_MAX_KPOOL][8];
+  float mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx[e] = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+    if (s < kp) {
+      float g[8], a[8];
+      load8(gate + (row0 + s) * D + c0, g);
+      load8(ape + size_t(s) * D + c0, a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lg[s][e] = g[e] + a[e];
+        mx[e] = fmaxf(mx[e], lg[s][e]);
+      }
+    }
+  }
+  float den[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { den[e] = 0.f; acc[e] = 0.f; }
+#pragma unroll
+  for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
+    if (s < kp) {
+      float kv[8];
+      load8(k + (row0 + s) * D + c0, kv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = expf(lg[s][e] - mx[e]);
+        den[e] += w;
+        acc[e] = fmaf(w, kv[e], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = acc[e] / den[e];
+  store8(dst, acc);
+  if (c0 == 0) {
+    int all = 1;
+    for (int s = 0; s < kp; ++s) all &= (valid[row0 + s] != 0);
+    pool_start[size_t(b) * P_max + p] = t0;
+    pool_valid[size_t(b) * P_max + p] = uint8_t(all);
+  }
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" int dsa_kpool_compress(const void* k, const void* gate, const uint8_t* valid,
+                                  const float* ape, const int32_t* seq_len, int B, int T_max,
+                                  int D, int kpool, int P_max, int dtype, void* k_pool,
+                                  int32_t* pool_start, uint8_t* pool_valid, int32_t* n_pools,
+                                  int32_t* first_valid, void* stream) {
+  if (!k || !gate || !valid || !ape || !seq_len || !k_pool || !pool_start || !pool_valid ||
+      !n_pools || !first_valid)
+    return DSA_ERR_NULL;
+  if (B <= 0 || T_max <= 0 || D <= 0 || kpool <= 0 || P_max <= 0) return DSA_ERR_SHAPE;
+  if (P_max < T_max / kpool) return DSA_ERR_SHAPE;
+  if (kpool > DSA_MAX_KPOOL) return DSA_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || D > 1024) return DSA_ERR_UNSUPPORTED;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+  if (long(B) > 65535) return DSA_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(anchor_kernel, dim3(B), dim3(kAnchorThreads), 0, s, valid, seq_len, T_max,
+                     kpool, n_pools, first_valid);
+  int st = launch_status();
+  if (st) return st;
+  const long work = long(P_max) * (D / 8);
+  dim3 grid(ceil_div(work, 256), B);
+  if (dtype == DSA_BF16)
+    hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)k,
+                       (const uint16_t*)gate, valid, ape, T_max, D, kpool, P_max, n_pools,
+                       first_valid, (uint16_t*)k_pool, pool_start, pool_valid);
+  else
+    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s, (const float*)k,
+                       (const float*)gate, valid, ape, T_max, D, kpool, P_max, n_pools,
+                       first_valid, (float*)k_pool, pool_start, pool_valid);
+  return launch_status();
+}

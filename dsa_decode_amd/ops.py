@@ -1,0 +1,146 @@
+"""Thin PyTorch binding of libdsa.so: same names as the C ABI (include/dsa.h).
+
+Each function checks that the tensors are contiguous device tensors of the
+right dtype, passes their device pointers and the current HIP stream, and
+raises DsaError on a non-zero status.  Outputs may be passed in or are
+allocated with torch.empty (every stage writes its whole output).  All
+arithmetic runs in the library's kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import DSA_BF16, DSA_F32, DsaError, check  # noqa: F401
+
+_ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _act_code(t: torch.Tensor) -> int:
+    if t.dtype not in _ACT:
+        raise ValueError(f"activation dtype {t.dtype} not supported")
+    return _ACT[t.dtype]
+
+
+def dsa_kpool_compress(k, gate, valid, ape, seq_len, kpool: int, P_max: int, out=None):
+    """-> dict(k_pool [B,P_max,D], pool_start, pool_valid [B,P_max], n_pools, first_valid [B])."""
+    B, T_max, D = k.shape
+    if out is None:
+        dev = k.device
+        out = dict(k_pool=torch.empty((B, P_max, D), dtype=k.dtype, device=dev),
+                   pool_start=torch.empty((B, P_max), dtype=torch.int32, device=dev),
+                   pool_valid=torch.empty((B, P_max), dtype=torch.uint8, device=dev),
+                   n_pools=torch.empty((B,), dtype=torch.int32, device=dev),
+                   first_valid=torch.empty((B,), dtype=torch.int32, device=dev))
+    st = _lib.load().dsa_kpool_compress(
+        _dev(k, "k", k.dtype), _dev(gate, "gate", k.dtype), _dev(valid, "valid", torch.uint8),
+        _dev(ape, "ape", torch.float32), _dev(seq_len, "seq_len", torch.int32),
+        B, T_max, D, kpool, P_max, _act_code(k),
+        _dev(out["k_pool"], "k_pool", k.dtype), _dev(out["pool_start"], "pool_start", torch.int32),
+        _dev(out["pool_valid"], "pool_valid", torch.uint8), _dev(out["n_pools"], "n_pools", torch.int32),
+        _dev(out["first_valid"], "first_valid", torch.int32), _stream())
+    check("dsa_kpool_compress", st)
+    return out
+
+
+def dsa_index_scores(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamma, ln_beta,
+                     ln_eps: float, row_seq, row_pos, kpool: int, scores=None):
+    """-> scores [Q, P_max] fp32 (-inf = not a candidate)."""
+    Q, H, D = q.shape
+    B, P_max, D2 = k_pool.shape
+    if D2 != D:
+        raise ValueError("q and k_pool disagree on D")
+    if scores is None:
+        scores = torch.empty((Q, P_max), dtype=torch.float32, device=q.device)
+    st = _lib.load().dsa_index_scores(
+        _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale),
+        _dev(k_pool, "k_pool"), _dev(pool_start, "pool_start", torch.int32),
+        _dev(pool_valid, "pool_valid", torch.uint8), _dev(ln_gamma, "ln_gamma", torch.float32),
+        _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps), _dev(row_seq, "row_seq", torch.int32),
+        _dev(row_pos, "row_pos", torch.int32), Q, H, D, B, P_max, kpool, _act_code(k_pool),
+        _dev(scores, "scores", torch.float32), _stream())
+    check("dsa_index_scores", st)
+    return scores
+
+
+def dsa_topk_workspace_bytes(Q: int, P: int, K: int) -> int:
+    return int(_lib.load().dsa_topk_workspace_bytes(Q, P, K))
+
+
+def dsa_topk_pools(scores, K: int, pool_ids=None, workspace=None):
+    """-> pool_ids [Q, K] int32, (score desc, index asc), -1 padded."""
+    Q, P = scores.shape
+    if pool_ids is None:
+        pool_ids = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
+    need = dsa_topk_workspace_bytes(Q, P, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dsa_topk_pools(_dev(scores, "scores", torch.float32), Q, P, K,
+                                    _dev(pool_ids, "pool_ids", torch.int32), ws_ptr, ws_bytes, _stream())
+    check("dsa_topk_pools", st)
+    return pool_ids
+
+
+def dsa_expand_selection(pool_ids, row_seq, pool_start, kpool: int, W: int, token_ids=None):
+    """-> token_ids [Q, W] int32 (-1 = invalid, every column written)."""
+    Q, K = pool_ids.shape
+    B, P_max = pool_start.shape
+    if token_ids is None:
+        token_ids = torch.empty((Q, W), dtype=torch.int32, device=pool_ids.device)
+    st = _lib.load().dsa_expand_selection(
+        _dev(pool_ids, "pool_ids", torch.int32), Q, K, _dev(row_seq, "row_seq", torch.int32),
+        _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool,
+        _dev(token_ids, "token_ids", torch.int32), W, _stream())
+    check("dsa_expand_selection", st)
+    return token_ids
+
+
+def dsa_sparse_mla_workspace_bytes(Q: int, Hm: int, Dl: int, W: int, dtype: int) -> int:
+    return int(_lib.load().dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype))
+
+
+def dsa_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, out=None, lse=None,
+                          workspace=None, want_lse: bool = True):
+    """-> (out [Q, Hm, Dl] act, lse [Q, Hm] fp32 or None)."""
+    Q, Hm, Dl = q_lat.shape
+    B, T_max, Dl2 = kv.shape
+    if Dl2 != Dl:
+        raise ValueError("q_lat and kv disagree on Dl")
+    W = token_ids.shape[1]
+    code = _act_code(kv)
+    if out is None:
+        out = torch.empty((Q, Hm, Dl), dtype=kv.dtype, device=kv.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Q, Hm), dtype=torch.float32, device=kv.device)
+    need = dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, code)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=kv.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dsa_sparse_mla_decode(
+        _dev(q_lat, "q_lat", kv.dtype), _dev(kv, "kv"), _dev(row_seq, "row_seq", torch.int32),
+        _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, T_max, W, float(sm_scale), code,
+        _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
+        ws_ptr, ws_bytes, _stream())
+    check("dsa_sparse_mla_decode", st)
+    return out, lse

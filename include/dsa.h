@@ -1,0 +1,199 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: DeepSeek-Sparse-Attention token selection and
+ * attention over the selected tokens for one GLM-5.3 DSA layer, on one
+ * MI355X (gfx950) GPU.
+ *
+ * The five stage entry points follow the pipeline on the "Module
+ * glm5next_dsa" API page, section "Shape of the pipeline":
+ *
+ *   k, gate, valid, ape -> dsa_kpool_compress   -> pool keys / starts / valid
+ *                       -> dsa_index_scores     -> [Q, P] scores + candidate validity
+ *                       -> dsa_topk_pools       -> [Q, select_k] pool ids
+ *                       -> dsa_expand_selection -> [Q, out_width] token ids (-1 = invalid)
+ *                       -> dsa_sparse_mla_decode (NoPE MLA restricted to those tokens)
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a caller-owned DEVICE pointer to a dense,
+ *     row-major array (innermost index last, no padding).  Scalars are by value.
+ *   - The library allocates nothing and keeps no pointer after it returns.
+ *     Calls that need scratch take a caller-sized workspace (device memory);
+ *     its size comes from the matching *_workspace_bytes function, which is a
+ *     pure host computation.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream) and
+ *     the call returns without synchronising the host.  Calls keep no state and
+ *     may run concurrently on different streams with disjoint outputs.
+ *   - Geometry is never defaulted: every dimension is an argument.
+ *   - Every call checks its arguments on the host first.  On a negative status
+ *     nothing was launched and no output was touched.
+ *   - `dtype` selects the activation type (DSA_F32 or DSA_BF16) of the tensors
+ *     marked "act"; parameters (ape, w, gamma, beta) and scores are always fp32.
+ *   - Preconditions NOT checked on the device (callers guarantee them):
+ *     finite inputs; row_seq[q] in [0, B); token ids < T_max; pool ids < P_max.
+ *     Kernels still bounds-check indices they dereference, so a violation gives
+ *     a wrong value (-1 / -inf / zero), never an out-of-bounds access.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DSA_OK                0
+#define DSA_ERR_NULL         -1  /* a required pointer is NULL */
+#define DSA_ERR_SHAPE        -2  /* a dimension is non-positive or inconsistent */
+#define DSA_ERR_UNSUPPORTED  -3  /* a dimension outside what the kernels implement */
+#define DSA_ERR_WORKSPACE    -4  /* workspace missing or too small */
+#define DSA_ERR_HIP          -5  /* the HIP runtime reported an error at launch */
+
+/* activation dtypes */
+#define DSA_F32   0
+#define DSA_BF16  1
+
+/* Most pool slots (kpool) accepted.  The "Module glm5next_dsa" page, section
+ * "Constants" (KERNEL_MAX_KPOOL), states that the reference compression kernel
+ * holds at most 8 slots and silently truncates more; here a larger kpool is
+ * refused with DSA_ERR_UNSUPPORTED. */
+#define DSA_MAX_KPOOL 8
+
+/* Largest select_k accepted by dsa_topk_pools. */
+#define DSA_MAX_SELECT_K 2048
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* dsa_status_string(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+int dsa_abi_version(void);
+#define DSA_ABI_VERSION 1
+
+/*
+ * dsa_kpool_compress -- pooled index keys.
+ * "Module glm5next_dsa", "Shape of the pipeline" (k, gate, valid, ape ->
+ * pool keys / indices / valid) and "Traps carried from Slice 8": the pool
+ * softmax runs over the pool-slot axis, per channel; pooling starts at the
+ * first valid token (left padding is skipped, not pooled); a pool counts only
+ * if every kpool slot is valid (a trailing partial pool is not a pool).
+ *
+ * For sequence b with first valid token f_b (among its first seq_len[b]
+ * tokens), pool p < n_pools[b] = (seq_len[b] - f_b) / kpool covers tokens
+ * t_s = f_b + p*kpool + s, s < kpool, and per channel c
+ *     a_s = softmax_s(gate[b,t_s,c] + ape[s,c]),  k_pool[b,p,c] = sum_s a_s k[b,t_s,c].
+ * pool_valid[b,p] = 1 iff all kpool slot tokens are valid (a hole invalidates
+ * its pool).  Rows p >= n_pools[b] are written as k_pool = 0,
+ * pool_start = -1, pool_valid = 0: the whole output is written.  A sequence
+ * with no valid token gets n_pools = 0 and first_valid = seq_len[b].
+ *
+ *   k, gate      [B, T_max, D] act        valid [B, T_max] uint8 (nonzero = valid)
+ *   ape          [kpool, D] fp32          seq_len [B] int32, each in [0, T_max]
+ *   k_pool       [B, P_max, D] act (out)  pool_start [B, P_max] int32 (out)
+ *   pool_valid   [B, P_max] uint8 (out)   n_pools, first_valid [B] int32 (out)
+ * Requires 1 <= kpool <= DSA_MAX_KPOOL, D % 8 == 0 and D <= 1024,
+ * P_max >= T_max / kpool.  Computes in fp32; bf16 outputs are rounded to
+ * nearest even once.
+ */
+int dsa_kpool_compress(const void* k, const void* gate, const uint8_t* valid, const float* ape,
+                       const int32_t* seq_len, int B, int T_max, int D, int kpool, int P_max,
+                       int dtype, void* k_pool, int32_t* pool_start, uint8_t* pool_valid,
+                       int32_t* n_pools, int32_t* first_valid, void* stream);
+
+/*
+ * dsa_index_scores -- indexer scores with candidate validity.
+ * "Module glm5next_dsa", "Shape of the pipeline" (-> [Q, P] scores + candidate
+ * validity) and "Traps carried from Slice 8" (indexer.k_norm is a LayerNorm:
+ * mean-subtracting, with bias); "Module tp", "Why the indexer is REPLICATED,
+ * not sharded" (the score is a plain sum over heads of w[h]*relu(scale*dot)).
+ *
+ * For row q of sequence b = row_seq[q] and pool p:
+ *   kn = LayerNorm(k_pool[b,p,:]; gamma, beta, eps)   (biased variance)
+ *   scores[q,p] = sum_h w[q,h] * max(0, scale * <q[q,h,:], kn>)
+ * when p is a candidate -- pool_valid[b,p] != 0 and
+ * pool_start[b,p] + kpool - 1 <= row_pos[q] (causal: the pool ends at or
+ * before the row's position) -- and -inf otherwise.  All Q*P_max scores are
+ * written.
+ *
+ *   q [Q, H, D] act     w [Q, H] fp32     gamma, beta [D] fp32
+ *   k_pool [B, P_max, D] act              pool_start [B, P_max] int32
+ *   pool_valid [B, P_max] uint8           row_seq, row_pos [Q] int32
+ *   scores [Q, P_max] fp32 (out)
+ * Requires D in {32, 64, 128} and 1 <= H <= 64.
+ */
+int dsa_index_scores(const void* q, const float* w, float scale, const void* k_pool,
+                     const int32_t* pool_start, const uint8_t* pool_valid, const float* ln_gamma,
+                     const float* ln_beta, float ln_eps, const int32_t* row_seq,
+                     const int32_t* row_pos, int Q, int H, int D, int B, int P_max, int kpool,
+                     int dtype, float* scores, void* stream);
+
+/*
+ * dsa_topk_pools -- deterministic per-row top-k of the scores.
+ * "Module glm5next_dsa", "Shape of the pipeline" (-> [Q, select_k] pool ids);
+ * "Module tp", "Why the indexer is REPLICATED, not sharded" (tiebreak: higher
+ * score first, then the smaller pool index).
+ *
+ * Candidates of row q are the p with scores[q,p] != -inf.  pool_ids[q,j] is
+ * the j-th candidate in (score descending, pool index ascending) order, with
+ * +0.0 and -0.0 comparing equal; when a row has fewer than K candidates the
+ * rest of its row is -1.  The whole [Q, K] output is written.  Scores must not
+ * be NaN.
+ *
+ *   scores [Q, P] fp32     pool_ids [Q, K] int32 (out)
+ *   workspace: device buffer of dsa_topk_workspace_bytes(Q, P, K) bytes
+ *              (may be NULL when that is 0).
+ * Requires 1 <= K <= DSA_MAX_SELECT_K and P <= 524288.
+ */
+size_t dsa_topk_workspace_bytes(int Q, int P, int K);
+int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_expand_selection -- pool ids to token ids.
+ * "Module glm5next_dsa", "Shape of the pipeline" (-> [Q, out_width] token ids,
+ * -1 = invalid) and "Traps carried from Slice 8" (the -1 sentinel destination
+ * must be fully written).
+ *
+ * token_ids[q, j*kpool + s] = pool_start[b, pool_ids[q,j]] + s for j < K,
+ * s < kpool, b = row_seq[q]; it is -1 where pool_ids[q,j] is -1 or names a
+ * pool that does not exist (pool_start = -1), and every column >= K*kpool is -1.
+ *
+ *   pool_ids [Q, K] int32    row_seq [Q] int32    pool_start [B, P_max] int32
+ *   token_ids [Q, W] int32 (out)
+ * Requires W >= K*kpool and 1 <= kpool <= DSA_MAX_KPOOL.
+ */
+int dsa_expand_selection(const int32_t* pool_ids, int Q, int K, const int32_t* row_seq,
+                         const int32_t* pool_start, int B, int P_max, int kpool,
+                         int32_t* token_ids, int W, void* stream);
+
+/*
+ * dsa_sparse_mla_decode -- absorbed NoPE MLA decode over the selected tokens.
+ * "Module glm5next_dsa", "Shape of the pipeline" (NoPE MLA restricted to the
+ * selected tokens) and "Traps carried from Slice 8" (NoPE: the rotary slice is
+ * zero-width); "Module tp", "Traps this module encodes" (kv_a_proj_with_mqa
+ * yields one shared latent per token with no head axis, so the cache is
+ * [B, T_max, Dl] and, absorbed, keys and values are the latent itself).
+ *
+ * For row q (b = row_seq[q]) and head h, over the ids j = token_ids[q,c] >= 0:
+ *   l_j = sm_scale * <q_lat[q,h,:], kv[b,j,:]>
+ *   out[q,h,:] = sum_j softmax(l)_j kv[b,j,:],   lse[q,h] = log sum_j exp(l_j)
+ * A row with no id gets out = 0 and lse = -inf.  Ids are expected unique
+ * (dsa_expand_selection produces unique ids); each listed entry is one term.
+ *
+ *   q_lat [Q, Hm, Dl] act    kv [B, T_max, Dl] act    token_ids [Q, W] int32
+ *   out [Q, Hm, Dl] act (out)    lse [Q, Hm] fp32 (out, may be NULL)
+ *   workspace: dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype) bytes.
+ * Requires Dl in {64, 128, 256, 512} and 1 <= Hm <= 128; the bf16 MFMA path
+ * is taken for Dl == 512 with Hm % 16 == 0.
+ */
+size_t dsa_sparse_mla_workspace_bytes(int Q, int Hm, int Dl, int W, int dtype);
+int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_seq,
+                          const int32_t* token_ids, int Q, int Hm, int Dl, int B, int T_max,
+                          int W, float sm_scale, int dtype, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

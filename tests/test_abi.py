@@ -1,0 +1,112 @@
+"""The C-ABI library: it loads, exports every entry point include/dsa.h
+declares, and its host-side argument checks refuse bad calls before any
+launch (no GPU work happens in these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+FAKE = ctypes.c_void_p(256)  # a non-NULL pointer that is never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"dsa_kpool_compress", "dsa_index_scores", "dsa_topk_pools", "dsa_expand_selection",
+            "dsa_sparse_mla_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_signatures_cover_header(lib):
+    from dsa_decode_amd import _lib
+    assert set(_declared()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dsa_abi_version() == 1
+    for code in range(0, -6, -1):
+        assert lib.dsa_status_string(code)
+    assert lib.dsa_status_string(0) == b"ok"
+
+
+def _compress(lib, **kw):
+    a = dict(k=FAKE, gate=FAKE, valid=FAKE, ape=FAKE, seq_len=FAKE, B=1, T_max=64, D=32, kpool=4,
+             P_max=16, dtype=0, k_pool=FAKE, pool_start=FAKE, pool_valid=FAKE, n_pools=FAKE,
+             first_valid=FAKE, stream=None)
+    a.update(kw)
+    return lib.dsa_kpool_compress(*a.values())
+
+
+def test_compress_refuses_bad_arguments(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED
+    assert _compress(lib, k=None) == DSA_ERR_NULL
+    assert _compress(lib, first_valid=None) == DSA_ERR_NULL
+    assert _compress(lib, B=0) == DSA_ERR_SHAPE
+    assert _compress(lib, P_max=15) == DSA_ERR_SHAPE          # P_max < T_max / kpool
+    # kpool above the pages' limit of 8 slots is refused, never truncated
+    assert _compress(lib, kpool=9, P_max=64) == DSA_ERR_UNSUPPORTED
+    assert _compress(lib, D=36) == DSA_ERR_UNSUPPORTED
+    assert _compress(lib, dtype=7) == DSA_ERR_UNSUPPORTED
+
+
+def _scores(lib, **kw):
+    a = dict(q=FAKE, w=FAKE, scale=0.1, k_pool=FAKE, pool_start=FAKE, pool_valid=FAKE, g=FAKE, b=FAKE,
+             eps=1e-5, row_seq=FAKE, row_pos=FAKE, Q=1, H=4, D=32, B=1, P_max=16, kpool=4, dtype=0,
+             scores=FAKE, stream=None)
+    a.update(kw)
+    return lib.dsa_index_scores(*a.values())
+
+
+def test_scores_refuse_bad_arguments(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED
+    assert _scores(lib, scores=None) == DSA_ERR_NULL
+    assert _scores(lib, Q=0) == DSA_ERR_SHAPE
+    assert _scores(lib, D=48) == DSA_ERR_UNSUPPORTED
+    assert _scores(lib, H=65) == DSA_ERR_UNSUPPORTED
+    assert _scores(lib, kpool=9) == DSA_ERR_UNSUPPORTED
+
+
+def test_topk_refuses_bad_arguments_and_sizes_workspace(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
+    assert lib.dsa_topk_pools(None, 1, 64, 8, FAKE, None, 0, None) == DSA_ERR_NULL
+    assert lib.dsa_topk_pools(FAKE, 1, 64, 0, FAKE, None, 0, None) == DSA_ERR_SHAPE
+    assert lib.dsa_topk_pools(FAKE, 1, 64, 2049, FAKE, None, 0, None) == DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_pools(FAKE, 1, 16 * 32768 + 1, 8, FAKE, None, 0, None) == DSA_ERR_UNSUPPORTED
+    # a long row is split and needs a workspace
+    need = lib.dsa_topk_workspace_bytes(4, 65536, 512)
+    assert need >= 4 * 512 * 8
+    assert lib.dsa_topk_pools(FAKE, 4, 65536, 512, FAKE, None, 0, None) == DSA_ERR_WORKSPACE
+    assert lib.dsa_topk_pools(FAKE, 4, 65536, 512, FAKE, FAKE, need - 1, None) == DSA_ERR_WORKSPACE
+    assert lib.dsa_topk_workspace_bytes(4096, 32768, 512) == 0
+
+
+def test_expand_refuses_bad_arguments(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED
+    assert lib.dsa_expand_selection(None, 1, 8, FAKE, FAKE, 1, 64, 4, FAKE, 32, None) == DSA_ERR_NULL
+    assert lib.dsa_expand_selection(FAKE, 1, 8, FAKE, FAKE, 1, 64, 4, FAKE, 31, None) == DSA_ERR_SHAPE
+    assert lib.dsa_expand_selection(FAKE, 1, 8, FAKE, FAKE, 1, 64, 9, FAKE, 72, None) == DSA_ERR_UNSUPPORTED
+
+
+def test_mla_refuses_bad_arguments_and_sizes_workspace(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
+    call = lambda **kw: lib.dsa_sparse_mla_decode(*dict(dict(
+        q=FAKE, kv=FAKE, rs=FAKE, ids=FAKE, Q=4, Hm=64, Dl=512, B=4, T=1024, W=2048, sc=0.04, dt=1,
+        out=FAKE, lse=None, ws=None, wsb=0, stream=None), **kw).values())
+    assert call(out=None) == DSA_ERR_NULL
+    assert call(W=0) == DSA_ERR_SHAPE
+    assert call(Dl=96) == DSA_ERR_UNSUPPORTED
+    assert call(Hm=129) == DSA_ERR_UNSUPPORTED
+    need = lib.dsa_sparse_mla_workspace_bytes(4, 64, 512, 2048, 1)
+    assert need > 0
+    assert call() == DSA_ERR_WORKSPACE
+    assert call(ws=FAKE, wsb=need - 1) == DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_mla_workspace_bytes(1, 4, 64, 32, 0) == 0   # fp32 path: no split

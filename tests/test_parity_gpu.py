@@ -1,0 +1,393 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same
+seeded inputs, through the C ABI (dsa_decode_amd.ops marshals arguments only).
+
+Per stage, the inputs of both sides are identical: token inputs come from the
+synthetic generators, and the inputs of later stages come from the oracle's
+own earlier stages (never from a GPU result).  Bars:
+  compress   one bf16 spacing (bf16 only) + 1e-5 * sum a|k|; bf16 >= 98% bit-equal
+  scores     |g - o| <= 1e-3 |o| + 1e-5 A (A = forward-error scale), -inf exact
+  top-k      bit-exact
+  expand     bit-exact, every column written
+  sparse MLA bf16: 2e-2 absolute; fp32: 1e-4 absolute; lse 2e-3 (bf16) / 1e-5 (fp32)
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_decode_amd import synth
+from oracle import dsa_oracle as O
+from tests.helpers import (act_from_f64, assert_compress_close, assert_scores_close,
+                           assert_topk_property, dev, pool_cache_from_oracle, score_scale)
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from dsa_decode_amd import ops as _ops
+    return _ops
+
+
+# ------------------------------------------------------------------ per-workload data
+_CACHE: dict = {}
+
+
+def wl_data(name: str) -> dict:
+    """Synthetic inputs + the oracle's compress of them (cached per workload)."""
+    if name in _CACHE:
+        return _CACHE[name]
+    wl = synth.workload(name)
+    ti = synth.token_inputs(wl)
+    comp = O.kpool_compress(ti["k"], ti["gate"], ti["valid"], ti["ape"], ti["seq_len"], wl.kp, wl.P_max)
+    d = dict(wl=wl, ti=ti, comp=comp, ip=synth.index_params(wl))
+    _CACHE[name] = d
+    return d
+
+
+def _absk_pool(d):
+    ti, wl = d["ti"], d["wl"]
+    return O.kpool_compress(ti["k"].abs(), ti["gate"], ti["valid"], ti["ape"], ti["seq_len"], wl.kp,
+                            wl.P_max)["k_pool"]
+
+
+def run_compress(d):
+    ti, wl = d["ti"], d["wl"]
+    return ops().dsa_kpool_compress(dev(ti["k"]), dev(ti["gate"]), dev(ti["valid"]), dev(ti["ape"]),
+                                    dev(ti["seq_len"]), wl.kp, wl.P_max)
+
+
+def check_compress(d):
+    wl, comp = d["wl"], d["comp"]
+    out = run_compress(d)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["n_pools"].cpu().numpy(), comp["n_pools"])
+    np.testing.assert_array_equal(out["first_valid"].cpu().numpy(), comp["first_valid"])
+    np.testing.assert_array_equal(out["pool_start"].cpu().numpy(), comp["pool_start"])
+    np.testing.assert_array_equal(out["pool_valid"].cpu().numpy().astype(bool), comp["pool_valid"])
+    absk = _absk_pool(d)
+    assert_compress_close(out["k_pool"], comp["k_pool"], absk, wl.torch_dtype)
+
+
+def scores_inputs(d, k_pool_override=None):
+    wl = d["wl"]
+    pc = pool_cache_from_oracle(d["comp"], wl.torch_dtype)
+    if k_pool_override is not None:
+        pc["k_pool"] = k_pool_override
+    return pc
+
+
+def run_scores(d, pc):
+    ip, wl = d["ip"], d["wl"]
+    return ops().dsa_index_scores(dev(ip["q"]), dev(ip["w"]), ip["scale"], dev(pc["k_pool"]),
+                                  dev(pc["pool_start"]), dev(pc["pool_valid"]), dev(ip["gamma"]),
+                                  dev(ip["beta"]), ip["eps"], dev(ip["row_seq"]), dev(ip["row_pos"]),
+                                  wl.kp)
+
+
+def oracle_scores(d, pc, rows=None):
+    ip, wl = d["ip"], d["wl"]
+    return O.index_scores(ip["q"], ip["w"], ip["scale"], pc["k_pool"], pc["pool_start"], pc["pool_valid"],
+                          ip["gamma"], ip["beta"], ip["eps"], ip["row_seq"], ip["row_pos"], wl.kp, rows=rows)
+
+
+def check_scores(d, pc, rows=None):
+    ip, wl = d["ip"], d["wl"]
+    got = run_scores(d, pc).cpu().numpy()
+    rows = list(range(wl.Q)) if rows is None else rows
+    ref = oracle_scores(d, pc, rows)
+    A = score_scale(ip["q"], ip["w"], ip["scale"], pc["k_pool"], ip["gamma"], ip["beta"], ip["eps"],
+                    ip["row_seq"], rows)
+    assert_scores_close(got[rows], ref, A)
+    return ref
+
+
+def check_topk(scores_np: np.ndarray, K: int):
+    ref = O.topk_pools(scores_np, K)
+    got = ops().dsa_topk_pools(dev(torch.from_numpy(scores_np)), K).cpu().numpy()
+    np.testing.assert_array_equal(got, ref)
+    return ref
+
+
+def check_expand(ids: np.ndarray, row_seq, pool_start: np.ndarray, kp: int, W: int):
+    ref = O.expand_selection(ids, row_seq, pool_start, kp, W)
+    out = torch.full((ids.shape[0], W), 0x7fffffff, dtype=torch.int32, device="cuda")  # canary
+    got = ops().dsa_expand_selection(dev(torch.from_numpy(ids.astype(np.int32))),
+                                     dev(torch.as_tensor(np.asarray(row_seq, np.int32))),
+                                     dev(torch.from_numpy(pool_start.astype(np.int32))), kp, W,
+                                     token_ids=out).cpu().numpy()
+    assert not (got == 0x7fffffff).any(), "unwritten slots in the token-id destination"
+    np.testing.assert_array_equal(got, ref)
+    return ref
+
+
+def check_mla(q_lat, kv, row_seq, token_ids: np.ndarray, sm_scale, dtype, rows=None):
+    out, lse = ops().dsa_sparse_mla_decode(dev(q_lat), dev(kv), dev(torch.as_tensor(np.asarray(row_seq, np.int32))),
+                                           dev(torch.from_numpy(token_ids.astype(np.int32))), sm_scale)
+    rows = list(range(q_lat.shape[0])) if rows is None else rows
+    ref_o, ref_l = O.sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale, rows=rows)
+    g = out.float().cpu().numpy()[rows]
+    gl = lse.cpu().numpy()[rows]
+    tol_o, tol_l = (2e-2, 2e-3) if dtype == torch.bfloat16 else (1e-4, 1e-5)
+    err = np.abs(g - ref_o)
+    assert err.max() <= tol_o, f"max out err {err.max()}"
+    fin = np.isfinite(ref_l)
+    assert (np.isfinite(gl) == fin).all()
+    assert np.abs(gl[fin] - ref_l[fin]).max(initial=0) <= tol_l * np.maximum(1, np.abs(ref_l[fin])).max(initial=1)
+    return g
+
+
+# ------------------------------------------------------------------ tiny (fp32)
+def test_tiny_compress():
+    check_compress(wl_data("tiny"))
+
+
+def test_tiny_scores_topk_expand_mla():
+    d = wl_data("tiny")
+    wl = d["wl"]
+    pc = scores_inputs(d)
+    ref_scores = check_scores(d, pc)
+    ids = check_topk(ref_scores, wl.K)
+    tok = check_expand(ids, d["ip"]["row_seq"].numpy(), d["comp"]["pool_start"], wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    check_mla(mi["q_lat"], mi["kv"], d["ip"]["row_seq"].numpy(), tok, mi["sm_scale"], wl.torch_dtype)
+
+
+# ------------------------------------------------------------------ decode (bf16, 8192 ctx)
+def test_decode_compress():
+    check_compress(wl_data("decode"))
+
+
+def test_decode_scores_topk_expand():
+    d = wl_data("decode")
+    wl = d["wl"]
+    ref_scores = check_scores(d, scores_inputs(d))
+    ids = check_topk(ref_scores, wl.K)
+    check_expand(ids, d["ip"]["row_seq"].numpy(), d["comp"]["pool_start"], wl.kp, wl.W)
+
+
+def test_decode_mla_on_selected_tokens():
+    d = wl_data("decode")
+    wl = d["wl"]
+    ref_scores = oracle_scores(d, scores_inputs(d))
+    ids = O.topk_pools(ref_scores, wl.K)
+    tok = O.expand_selection(ids, d["ip"]["row_seq"].numpy(), d["comp"]["pool_start"], wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    check_mla(mi["q_lat"], mi["kv"], d["ip"]["row_seq"].numpy(), tok, mi["sm_scale"], wl.torch_dtype)
+
+
+# ------------------------------------------------------------------ batched (32 ragged seqs)
+def test_batched_compress():
+    check_compress(wl_data("batched"))
+
+
+def test_batched_scores_topk_expand_mla():
+    d = wl_data("batched")
+    wl = d["wl"]
+    ref_scores = check_scores(d, scores_inputs(d))
+    ids = check_topk(ref_scores, wl.K)
+    rs = d["ip"]["row_seq"].numpy()
+    tok = check_expand(ids, rs, d["comp"]["pool_start"], wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    check_mla(mi["q_lat"], mi["kv"], rs, tok, mi["sm_scale"], wl.torch_dtype, rows=list(range(0, 32, 3)))
+
+
+# ------------------------------------------------------------------ long (4 x 262144, the bench workload)
+def test_long_compress():
+    check_compress(wl_data("long"))
+
+
+def test_long_scores_topk_expand():
+    d = wl_data("long")
+    wl = d["wl"]
+    ref_scores = check_scores(d, scores_inputs(d))
+    ids = check_topk(ref_scores, wl.K)
+    check_expand(ids, d["ip"]["row_seq"].numpy(), d["comp"]["pool_start"], wl.kp, wl.W)
+
+
+def test_long_mla():
+    d = wl_data("long")
+    wl = d["wl"]
+    rs = d["ip"]["row_seq"].numpy()
+    tok = synth.random_token_ids(wl.Q, wl.W, wl.seq_len, rs.tolist(), seed=wl.seed)
+    mi = synth.mla_inputs(wl)
+    check_mla(mi["q_lat"], mi["kv"], rs, tok.numpy(), mi["sm_scale"], wl.torch_dtype)
+
+
+# ------------------------------------------------------------------ prefill chunk (4096 rows, forced ties)
+def test_prefill_scores_sampled_rows_and_topk():
+    d = wl_data_prefill()
+    wl = d["wl"]
+    pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl))
+    rows = [0, 1, 511, 2048, 3001, 4094, 4095]
+    got = run_scores(d, pc)
+    ref = oracle_scores(d, pc, rows)
+    ip = d["ip"]
+    A = score_scale(ip["q"], ip["w"], ip["scale"], pc["k_pool"], ip["gamma"], ip["beta"], ip["eps"],
+                    ip["row_seq"], rows)
+    g = got.cpu().numpy()
+    assert_scores_close(g[rows], ref, A)
+    # bit-exact top-k on the oracle's rows (ties straddle the cut there)
+    check_topk(ref, wl.K)
+    # the full-size selection on the GPU's own scores: every row valid
+    ids = ops().dsa_topk_pools(got, wl.K).cpu().numpy()
+    sample = list(range(0, 4096, 97)) + [4095]
+    assert_topk_property(g[sample], ids[sample], wl.K)
+
+
+def wl_data_prefill():
+    # the prefill chunk pools a whole 131072-token sequence; the oracle's
+    # compress is only needed for pool_start / pool_valid
+    return wl_data("prefill")
+
+
+def test_prefill_topk_forced_ties_full_size():
+    s = synth.random_scores(4096, 32768, seed=77, tie_levels=300, neg_inf_frac=0.01, signed_zeros=True)
+    got = ops().dsa_topk_pools(dev(s), 512).cpu().numpy()
+    rows = list(range(0, 4096, 257)) + [4095]
+    ref = O.topk_pools(s.numpy()[rows], 512)
+    np.testing.assert_array_equal(got[rows], ref)
+
+
+# ------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("Q,P,K,ties", [(1, 1, 1, 0), (3, 7, 8, 0), (2, 1000, 8, 3), (4, 4097, 512, 50),
+                                        (2, 65537, 512, 0), (4, 65536, 512, 40), (1, 65536, 2048, 0),
+                                        (5, 300000, 64, 1000), (300, 5000, 100, 20)])
+def test_topk_shapes_ties_and_padding(Q, P, K, ties):
+    s = synth.random_scores(Q, P, seed=Q * 1000 + P, tie_levels=ties, neg_inf_frac=0.3, signed_zeros=True)
+    s[0, : P // 2] = -np.inf          # a row with few candidates
+    if Q > 1:
+        s[1, :] = -np.inf             # a row with none
+    check_topk(s.numpy(), K)
+
+
+def test_topk_is_deterministic():
+    s = dev(synth.random_scores(4, 65536, seed=5, tie_levels=100))
+    a = ops().dsa_topk_pools(s, 512)
+    b = ops().dsa_topk_pools(s, 512)
+    assert torch.equal(a, b)
+
+
+def test_compress_edge_cases():
+    # holes, a fully invalid sequence, short sequences, kpool 1 / 3 / 8, fp32 and bf16
+    for kp, dtype in [(1, torch.float32), (3, torch.bfloat16), (8, torch.bfloat16), (4, torch.float32)]:
+        rng = np.random.default_rng(kp)
+        B, T, D = 3, 70, 16
+        k = torch.from_numpy(rng.standard_normal((B, T, D)).astype(np.float32)).to(dtype)
+        gate = torch.from_numpy(rng.standard_normal((B, T, D)).astype(np.float32)).to(dtype)
+        ape = torch.from_numpy((0.1 * rng.standard_normal((kp, D))).astype(np.float32))
+        valid = np.ones((B, T), np.uint8)
+        valid[0, :3] = 0
+        valid[0, 20] = 0          # a hole
+        valid[1, :] = 0           # nothing valid
+        seq_len = np.array([70, 70, 33], np.int32)
+        P_max = T // kp + 1
+        comp = O.kpool_compress(k, gate, valid, ape, seq_len, kp, P_max)
+        out = ops().dsa_kpool_compress(dev(k), dev(gate), dev(torch.from_numpy(valid)), dev(ape),
+                                       dev(torch.from_numpy(seq_len)), kp, P_max)
+        np.testing.assert_array_equal(out["n_pools"].cpu().numpy(), comp["n_pools"])
+        np.testing.assert_array_equal(out["pool_start"].cpu().numpy(), comp["pool_start"])
+        np.testing.assert_array_equal(out["pool_valid"].cpu().numpy().astype(bool), comp["pool_valid"])
+        absk = O.kpool_compress(k.abs(), gate, valid, ape, seq_len, kp, P_max)["k_pool"]
+        assert_compress_close(out["k_pool"], comp["k_pool"], absk, dtype)
+
+
+@pytest.mark.parametrize("H,D,dtype", [(16, 128, torch.bfloat16), (32, 128, torch.bfloat16),
+                                       (8, 64, torch.bfloat16), (5, 32, torch.float32),
+                                       (32, 128, torch.float32)])
+def test_scores_paths_ragged_causal_and_mixed_rows(H, D, dtype):
+    rng = np.random.default_rng(H * D)
+    B, P, kp = 3, 1000, 4
+    k_pool = torch.from_numpy(rng.standard_normal((B, P, D)).astype(np.float32)).to(dtype)
+    pool_start = np.tile((np.arange(P) * kp + 2).astype(np.int32), (B, 1))
+    pool_valid = (rng.random((B, P)) > 0.1).astype(np.uint8)
+    pool_start[2, 700:] = -1
+    pool_valid[2, 700:] = 0
+    Q = 70                                   # several row batches, rows of all sequences mixed
+    row_seq = rng.integers(0, B, Q).astype(np.int32)
+    row_pos = rng.integers(0, P * kp + 10, Q).astype(np.int32)
+    q = torch.from_numpy(rng.standard_normal((Q, H, D)).astype(np.float32)).to(dtype)
+    w = torch.from_numpy((rng.random((Q, H)) / H).astype(np.float32))
+    gamma = torch.from_numpy((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+    beta = torch.from_numpy((0.02 * rng.standard_normal(D)).astype(np.float32))
+    got = ops().dsa_index_scores(dev(q), dev(w), D ** -0.5, dev(k_pool), dev(torch.from_numpy(pool_start)),
+                                 dev(torch.from_numpy(pool_valid)), dev(gamma), dev(beta), 1e-5,
+                                 dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(row_pos)), kp).cpu().numpy()
+    ref = O.index_scores(q, w, D ** -0.5, k_pool, pool_start, pool_valid, gamma, beta, 1e-5, row_seq, row_pos, kp)
+    A = score_scale(q, w, D ** -0.5, k_pool, gamma, beta, 1e-5, row_seq, range(Q))
+    assert_scores_close(got, ref, A)
+
+
+def test_scores_duplicate_pools_are_bit_identical():
+    d = wl_data("prefill")
+    wl = d["wl"]
+    pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl, n_codes=4))
+    got = run_scores(d, pc).cpu().numpy()
+    kp_rows = pc["k_pool"][0].view(torch.int16).numpy()
+    _, code = np.unique(kp_rows, axis=0, return_inverse=True)
+    for r in (0, 4095):
+        s = got[r]
+        for c in range(4):
+            vals = s[(code.ravel() == c) & np.isfinite(s)]
+            assert np.unique(vals).size == 1
+
+
+@pytest.mark.parametrize("Hm,Dl,dtype,W", [(64, 512, torch.bfloat16, 2048), (16, 512, torch.bfloat16, 70),
+                                           (32, 512, torch.bfloat16, 1), (4, 64, torch.bfloat16, 100),
+                                           (4, 64, torch.float32, 300), (128, 512, torch.bfloat16, 300)])
+def test_mla_shapes_holes_and_empty_rows(Hm, Dl, dtype, W):
+    rng = np.random.default_rng(Hm + Dl + W)
+    B, T, Q = 2, 5000, 3
+    q_lat = torch.from_numpy(rng.standard_normal((Q, Hm, Dl)).astype(np.float32)).to(dtype)
+    kv = torch.from_numpy(rng.standard_normal((B, T, Dl)).astype(np.float32)).to(dtype)
+    row_seq = np.array([1, 0, 1], np.int32)
+    tok = synth.random_token_ids(Q, W, [T, T], row_seq.tolist(), seed=W, hole_frac=0.2).numpy()
+    tok[2, :] = -1                       # a row with nothing selected
+    check_mla(q_lat, kv, row_seq, tok, Dl ** -0.5, dtype)
+
+
+def test_mla_permutation_invariant():
+    rng = np.random.default_rng(9)
+    q_lat = torch.from_numpy(rng.standard_normal((1, 64, 512)).astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(rng.standard_normal((1, 4096, 512)).astype(np.float32)).to(torch.bfloat16)
+    tok = synth.random_token_ids(1, 2048, [4096], [0], seed=3).numpy()
+    a = check_mla(q_lat, kv, [0], tok, 512 ** -0.5, torch.bfloat16)
+    b = check_mla(q_lat, kv, [0], tok[:, ::-1].copy(), 512 ** -0.5, torch.bfloat16)
+    assert np.abs(a - b).max() <= 2e-2
+
+
+def test_end_to_end_decode_pipeline_on_gpu():
+    """All stages chained on the GPU (compress -> scores -> top-k -> expand -> MLA)
+    for the decode workload, against the oracle's own pipeline on the same
+    token inputs.  Selection: every pool the oracle ranks clearly inside the cut
+    (beyond the score tolerance) is selected by the GPU, and every GPU pick
+    scores no lower than the oracle's K-th score minus that tolerance.  When
+    the two selections are the same set (the usual case) the attention outputs
+    must agree (attention is invariant to the order of the ids)."""
+    d = wl_data("decode")
+    wl, ip = d["wl"], d["ip"]
+    comp = run_compress(d)
+    scores = ops().dsa_index_scores(dev(ip["q"]), dev(ip["w"]), ip["scale"], comp["k_pool"], comp["pool_start"],
+                                    comp["pool_valid"], dev(ip["gamma"]), dev(ip["beta"]), ip["eps"],
+                                    dev(ip["row_seq"]), dev(ip["row_pos"]), wl.kp)
+    ids = ops().dsa_topk_pools(scores, wl.K)
+    tok = ops().dsa_expand_selection(ids, dev(ip["row_seq"]), comp["pool_start"], wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    out, _ = ops().dsa_sparse_mla_decode(dev(mi["q_lat"]), dev(mi["kv"]), dev(ip["row_seq"]), tok, mi["sm_scale"])
+    torch.cuda.synchronize()
+    # the oracle's pipeline from the same token inputs
+    pc = pool_cache_from_oracle(d["comp"], wl.torch_dtype)
+    ref = oracle_scores(d, pc)
+    ref_ids = O.topk_pools(ref, wl.K)
+    ref_tok = O.expand_selection(ref_ids, ip["row_seq"].numpy(), d["comp"]["pool_start"], wl.kp, wl.W)
+    ref_o, _ = O.sparse_mla_decode(mi["q_lat"], mi["kv"], ip["row_seq"], ref_tok, mi["sm_scale"])
+    s = ref[0]
+    kth = np.sort(s[np.isfinite(s)])[::-1][wl.K - 1]
+    tol = 1e-3 * abs(kth) + 1e-4
+    sel = ids.cpu().numpy()[0]
+    assert (sel >= 0).all() and len(set(sel.tolist())) == wl.K
+    assert (s[sel] >= kth - tol).all()
+    clearly_in = np.flatnonzero(s > kth + tol)
+    assert set(clearly_in.tolist()) <= set(sel.tolist())
+    if set(sel.tolist()) == set(ref_ids[0].tolist()):
+        assert np.abs(out.float().cpu().numpy() - ref_o).max() <= 2e-2
