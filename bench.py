@@ -93,38 +93,47 @@ def main() -> int:
                          dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
-    def scores_stage(r):
-        ops.dsa_index_scores(q, w, ip["scale"], r["k_pool"], r["pool_start"], r["pool_valid"], gamma, beta,
-                             ip["eps"], row_seq, row_pos, wl.kp, scores=r["scores"])
-
-    def rest_stages(r):
-        ops.dsa_topk_pools(r["scores"], K, pool_ids=r["ids"], workspace=tk_ws)
-        ops.dsa_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, W, token_ids=r["tok"])
-        ops.dsa_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], out=r["out"], lse=r["lse"],
-                                  workspace=mla_ws)
-
     stream = torch.cuda.Stream()
+    # every launch argument marshalled once per replica (plain ctypes calls in the loop)
+    with torch.cuda.stream(stream):
+        bound = []
+        for r in reps:
+            bound.append(dict(
+                scores=ops.bind_index_scores(q, w, ip["scale"], r["k_pool"], r["pool_start"], r["pool_valid"],
+                                             gamma, beta, ip["eps"], row_seq, row_pos, wl.kp, r["scores"]),
+                rest=[ops.bind_topk_pools(r["scores"], K, r["ids"], tk_ws),
+                      ops.bind_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, r["tok"]),
+                      ops.bind_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], r["out"],
+                                                 r["lse"], mla_ws)]))
+
+    def scores_stage(i):
+        bound[i]["scores"]()
+
+    def rest_stages(i):
+        for c in bound[i]["rest"]:
+            c()
+
     torch.cuda.synchronize()
     if args.mode == "graph":
         g_scores, g_rest = [], []
         with torch.cuda.stream(stream):
-            for r in reps:  # one eager pass on the capture stream first
-                scores_stage(r)
-                rest_stages(r)
+            for i in range(REPLICAS):  # one eager pass on the capture stream first
+                scores_stage(i)
+                rest_stages(i)
         stream.synchronize()
-        for r in reps:
+        for i in range(REPLICAS):
             ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
             with torch.cuda.graph(ga, stream=stream):
-                scores_stage(r)
+                scores_stage(i)
             with torch.cuda.graph(gb, stream=stream):
-                rest_stages(r)
+                rest_stages(i)
             g_scores.append(ga)
             g_rest.append(gb)
         run_scores = lambda i: g_scores[i].replay()
         run_rest = lambda i: g_rest[i].replay()
     else:
-        run_scores = lambda i: scores_stage(reps[i])
-        run_rest = lambda i: rest_stages(reps[i])
+        run_scores = scores_stage
+        run_rest = rest_stages
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -152,18 +161,13 @@ def main() -> int:
     stage_t = {n: [] for n in stage_names}
     with torch.cuda.stream(stream):
         for i in range(min(64, args.steps)):
-            r = reps[i % REPLICAS]
+            b = bound[i % REPLICAS]
+            calls = [b["scores"]] + b["rest"]
             e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             e[0].record(stream)
-            scores_stage(r)
-            e[1].record(stream)
-            ops.dsa_topk_pools(r["scores"], K, pool_ids=r["ids"], workspace=tk_ws)
-            e[2].record(stream)
-            ops.dsa_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, W, token_ids=r["tok"])
-            e[3].record(stream)
-            ops.dsa_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], out=r["out"],
-                                      lse=r["lse"], workspace=mla_ws)
-            e[4].record(stream)
+            for k, c in enumerate(calls):
+                c()
+                e[k + 1].record(stream)
             stream.synchronize()
             for k, n in enumerate(stage_names):
                 stage_t[n].append(e[k].elapsed_time(e[k + 1]) * 1e3)

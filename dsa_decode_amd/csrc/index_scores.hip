@@ -4,24 +4,30 @@
 // REPLICATED, not sharded": score = sum over heads of w[h]*relu(scale*dot)).
 //
 // MFMA path (bf16, D = 128, H in {16, 32}).  The LayerNorm is folded into the
-// contraction: with x the pooled key, mu / r its mean / inverse std and
-// g[h,c] = q[h,c]*gamma[c],
-//     <q_h, LN(x)> = r * (sum_c g[h,c] x_c - mu * sum_c g[h,c]) + sum_c q[h,c] beta[c].
-// sum_c g[h,c] x_c runs on the matrix cores with heads as M and pools as N:
-// x is exact bf16, and g is carried as an unevaluated pair g_hi + g_lo of
-// bf16 values (g - g_hi - g_lo is ~2^-17 |g|), both accumulated into the same
-// fp32 accumulator.  The normed key is never rounded.
+// contraction.  With x a pooled key, mu / r its mean / inverse std,
+// g[h,c] = q[h,c]*gamma[c] and g'[h,c] = g[h,c] - mean_c g[h,c],
+//     <q_h, LN(x)> = r * sum_c g'[h,c] x_c + sum_c q[h,c] beta[c]
+// (the centring of g' removes the mean of x exactly).  sum_c g'[h,c] x_c runs
+// on the matrix cores, heads as M and pools as N: x is exact bf16 and g' is an
+// unevaluated pair g'_hi + g'_lo of bf16 values (|g' - g'_hi - g'_lo| ~ 2^-17
+// |g'|), both accumulated into one fp32 accumulator.  The LayerNorm statistics
+// come from the matrix cores too: a ones operand gives sum_c x_c, and the
+// 16x16 Gram block of a tile with itself has sum_c x_c^2 on its diagonal, so
+// the vector ALUs only finish r, apply relu/w and reduce the heads.  The normed
+// key is never rounded.
 //
-// A workgroup is 4 waves; each wave owns kTiles tiles of 16 pools and keeps
-// their keys in registers (one 16-byte load per lane per 32 channels, the
-// lane's pool is lane & 15).  Key loads are issued before the per-row set-up,
-// so they are in flight while the workgroup prepares g.  The same kernel runs
-// decode (one row per workgroup, grid.y = rows) and prefill (a group of rows
-// of one sequence per workgroup; the keys are reused across the rows).
+// Lane l of a wave holds pool (l & 15) of a 16-pool tile and channels
+// 8*(kg + 4i) .. +8, kg = l >> 4, for k-step i (one 16-byte load each); the
+// MFMA output puts heads 4*kg + j (j < 4) of that pool in the lane.
 //
-// Per pool the decode kernel moves 256 B of key + 1 B valid + 4 B start and
-// writes 4 B of score: HBM-bound (the fold keeps the fp32 vector work to the
-// LayerNorm statistics and the head reduction).
+// Decode kernel: one row per grid row, pools split over grid.x; each wave
+// issues all its tiles' key loads at once, so the per-tile work overlaps their
+// arrival.  Prefill kernel: a workgroup
+// keeps its pool tiles in registers and runs a group of rows of one sequence
+// over them (rows staged four at a time in LDS).
+//
+// Per pool the decode kernel reads 256 B of key + 1 B valid + 4 B start and
+// writes 4 B of score: it is HBM-bound.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -32,19 +38,200 @@ constexpr int kIsWaves = kIsThreads / kWave;
 constexpr int kIsD = 128;
 constexpr int kIsLd = kIsD + 8;  // padded LDS row: 16 lanes reading 16 rows hit distinct banks
 
-template <int NH, int RPB>  // H = 16 * NH index heads; RPB rows staged in LDS at once
-struct IsShared {
-  uint16_t ghi[RPB][NH * 16][kIsLd];
-  uint16_t glo[RPB][NH * 16][kIsLd];
-  float G[RPB][NH * 16];   // sum_c (g_hi + g_lo)
-  float QB[RPB][NH * 16];  // sum_c q * beta
-  float W[RPB][NH * 16];
-  int pos[RPB];
-  int seq[RPB];
+// Stage one row's g' = q*gamma - mean(q*gamma) as (hi, lo) bf16 pairs, the
+// bias term QB = sum_c q*beta and the head weights.  8 threads per head, 16
+// channels each: u in [0, 8H) gives head u / 8, channels 16*(u % 8) .. +16.
+// Callers pass u for whole waves (the shuffles stay inside 8-lane groups).
+// Split in a load half and a compute half so that callers can issue other
+// loads in between.
+struct RowIn {
+  u32x4 q[2];
+  f32x4 g[4], b[4];
+  float w;
 };
 
+__device__ __forceinline__ RowIn stage_row_load(const uint16_t* __restrict__ q_row,
+                                                const float* __restrict__ w_row,
+                                                const float* __restrict__ gamma,
+                                                const float* __restrict__ beta, int u) {
+  const int h = u >> 3, c0 = (u & 7) * 16;
+  RowIn in;
+  in.w = w_row[h];
+#pragma unroll
+  for (int z = 0; z < 2; ++z) in.q[z] = *reinterpret_cast<const u32x4*>(q_row + h * kIsD + c0 + 8 * z);
+#pragma unroll
+  for (int z = 0; z < 4; ++z) {
+    in.g[z] = *reinterpret_cast<const f32x4*>(gamma + c0 + 4 * z);
+    in.b[z] = *reinterpret_cast<const f32x4*>(beta + c0 + 4 * z);
+  }
+  return in;
+}
+
+__device__ __forceinline__ void stage_row_store(const RowIn& in, uint16_t (*ghi)[kIsLd], uint16_t (*glo)[kIsLd],
+                                                float* QB, float* Wsh, int u) {
+  const int h = u >> 3, part = u & 7, c0 = part * 16;
+  float g[16];
+  float qbs = 0.f, gs = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t word = in.q[e >> 3][(e & 7) >> 1];
+    const float qv = (e & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+    g[e] = qv * in.g[e >> 2][e & 3];
+    gs += g[e];
+    qbs = fmaf(qv, in.b[e >> 2][e & 3], qbs);
+  }
+  gs += __shfl_xor(gs, 1, kWave);
+  gs += __shfl_xor(gs, 2, kWave);
+  gs += __shfl_xor(gs, 4, kWave);
+  qbs += __shfl_xor(qbs, 1, kWave);
+  qbs += __shfl_xor(qbs, 2, kWave);
+  qbs += __shfl_xor(qbs, 4, kWave);
+  const float mean = gs * (1.0f / kIsD);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float gc = g[half * 8 + 2 * e + z] - mean;
+        const uint16_t hi = f2bf(gc);
+        hw[z] = hi;
+        lw[z] = f2bf(gc - bf2f(hi));
+      }
+      ph[e] = hw[0] | (hw[1] << 16);
+      pl[e] = lw[0] | (lw[1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(&ghi[h][c0 + half * 8]) = ph;
+    *reinterpret_cast<u32x4*>(&glo[h][c0 + half * 8]) = pl;
+  }
+  if (part == 0) {
+    QB[h] = qbs;
+    Wsh[h] = in.w;
+  }
+}
+
+// A tile's contribution: LayerNorm statistics on the matrix cores, the folded
+// head dots, relu, head weights and the sum over the lane's heads and the
+// wave's four lane groups.  Returns the score of pool (lane & 15) (in all lanes).
+template <int NH>
+__device__ __forceinline__ float tile_score(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
+                                            const bf16x8 (&alo)[NH][4], const float (&cQ)[NH][4],
+                                            const float (&cW)[NH][4], float scale, float eps, int ln) {
+  const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  f32x4 acc[NH];
+#pragma unroll
+  for (int mb = 0; mb < NH; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 bx = as_bf16x8(x[i]);
+#pragma unroll
+    for (int mb = 0; mb < NH; ++mb) {
+      acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
+      acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
+    }
+    sacc = mfma16x16x32(ones, bx, sacc);   // every row: sum_c x_c of pool (lane & 15)
+    gacc = mfma16x16x32(bx, bx, gacc);     // Gram block: <x_m, x_n>
+  }
+  // diagonal <x_n, x_n> sits in lane 16*(n >> 2) + n, register n & 3
+  const int jd = ln & 3;
+  const float dg = jd == 0 ? gacc[0] : (jd == 1 ? gacc[1] : (jd == 2 ? gacc[2] : gacc[3]));
+  const float sumsq = __shfl(dg, 16 * (ln >> 2) + ln, kWave);
+  const float mu = sacc[0] * (1.0f / kIsD);
+  const float var = fmaxf(sumsq * (1.0f / kIsD) - mu * mu, 0.f);
+  const float rs = 1.0f / sqrtf(var + eps);
+  float part = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < NH; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, scale * fmaf(rs, acc[mb][j], cQ[mb][j])), part);
+  part += __shfl_xor(part, 16, kWave);
+  part += __shfl_xor(part, 32, kWave);
+  return part;
+}
+
+template <int NH>
+__device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], const uint16_t (*glo)[kIsLd],
+                                              const float* QB, const float* Wsh, int kg, int ln,
+                                              bf16x8 (&ahi)[NH][4], bf16x8 (&alo)[NH][4],
+                                              float (&cQ)[NH][4], float (&cW)[NH][4]) {
+#pragma unroll
+  for (int mb = 0; mb < NH; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ahi[mb][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&ghi[mb * 16 + ln][(kg + 4 * i) * 8]));
+      alo[mb][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&glo[mb * 16 + ln][(kg + 4 * i) * 8]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cQ[mb][j] = QB[mb * 16 + 4 * kg + j];
+      cW[mb][j] = Wsh[mb * 16 + 4 * kg + j];
+    }
+  }
+}
+
+// Decode kernel: a workgroup owns 4*TW consecutive 16-pool tiles of one row
+// (wave w takes tiles w, w+4, ...).  All of a wave's key loads are issued at
+// the start, before the row's operands are staged, so the whole workgroup's
+// keys are in flight at once and the per-tile work overlaps their arrival.
+template <int NH, int TW>
+__global__ __launch_bounds__(kIsThreads) void index_scores_decode(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
+    const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
+    const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int P_max, int kp, float* __restrict__ scores) {
+  constexpr int H = NH * 16;
+  __shared__ uint16_t ghi[H][kIsLd];
+  __shared__ uint16_t glo[H][kIsLd];
+  __shared__ float sQB[H], sW[H];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, ln = lane & 15;
+  const int r = blockIdx.y;
+  const int b = row_seq[r];
+  const int pos = row_pos[r];
+  const bool ok = b >= 0 && b < B;
+  const int t_begin = blockIdx.x * (kIsWaves * TW);
+  float* srow = scores + size_t(r) * P_max;
+
+  // the row's q / gamma / beta / w loads first, then every key tile of this
+  // wave (out-of-range tiles read a valid dummy address and are not stored)
+  RowIn rin;
+  if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
+  u32x4 xb[TW][4];
+  int psb[TW], pvb[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int p = (t_begin + wave + kIsWaves * j) * 16 + ln;
+    const bool in = ok && p < P_max;
+    const size_t pi = in ? size_t(b) * P_max + p : 0;
+    const uint16_t* src = k_pool + pi * kIsD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xb[j][i] = *reinterpret_cast<const u32x4*>(src + (kg + 4 * i) * 8);
+    psb[j] = pool_start[pi];
+    pvb[j] = pool_valid[pi];
+  }
+  if (tid < H * 8) stage_row_store(rin, ghi, glo, sQB, sW, tid);
+  __syncthreads();
+  bf16x8 ahi[NH][4], alo[NH][4];
+  float cQ[NH][4], cW[NH][4];
+  load_operands<NH>(ghi, glo, sQB, sW, kg, ln, ahi, alo, cQ, cW);
+
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const float sc = tile_score<NH>(xb[j], ahi, alo, cQ, cW, scale, eps, ln);
+    const int p = (t_begin + wave + kIsWaves * j) * 16 + ln;
+    if (kg == 0 && p < P_max) {
+      const bool cand = ok && pvb[j] != 0 && psb[j] + kp - 1 <= pos;
+      srow[p] = cand ? sc : -INFINITY;
+    }
+  }
+}
+
 template <int NH, int kTiles, int RPB>
-__global__ __launch_bounds__(kIsThreads) void index_scores_mfma(
+__global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
@@ -52,196 +239,70 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_mfma(
     const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int rows_per_group,
     float* __restrict__ scores) {
   constexpr int H = NH * 16;
-  __shared__ IsShared<NH, RPB> sh;
+  __shared__ uint16_t ghi[RPB][H][kIsLd];
+  __shared__ uint16_t glo[RPB][H][kIsLd];
+  __shared__ float sQB[RPB][H], sW[RPB][H];
+  __shared__ int s_pos[RPB], s_seq[RPB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, ln = lane & 15;
   const int r_begin = blockIdx.y * rows_per_group;
   const int r_end = min(Q, r_begin + rows_per_group);
   const int p_wave = blockIdx.x * (kIsWaves * kTiles * 16) + wave * (kTiles * 16);
 
-  // sequence of the first row decides which keys are loaded; rows of another
-  // sequence in the same group reload (correct, slower; groups are normally
-  // rows of one sequence)
+  // keys of this wave's tiles for the sequence of the group's first row; a row
+  // of another sequence reloads them (correct, slower)
   int b_loaded = row_seq[r_begin];
-
-  // ---- issue the key loads of this wave's tiles ----
   u32x4 xk[kTiles][4];
+  int psk[kTiles], pvk[kTiles];
   auto load_keys = [&](int b) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const int p = p_wave + t * 16 + ln;
-      const bool in = (p < P_max) && b >= 0 && b < B;
-      const uint16_t* src = k_pool + (size_t(in ? b : 0) * P_max + (in ? p : 0)) * kIsD;
+      const bool in = p < P_max && b >= 0 && b < B;
+      const size_t pi = in ? size_t(b) * P_max + p : 0;
+      const uint16_t* src = k_pool + pi * kIsD;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // channel group kg + 4i of this pool: 8 channels, 16 bytes
-        xk[t][i] = in ? *reinterpret_cast<const u32x4*>(src + (kg + 4 * i) * 8) : u32x4{0, 0, 0, 0};
-      }
+      for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + (kg + 4 * i) * 8);
+      psk[t] = pool_start[pi];
+      pvk[t] = pool_valid[pi];
     }
   };
   load_keys(b_loaded);
 
-  float mu[kTiles], rs[kTiles];
-  auto ln_stats = [&]() {
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      float s1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s1 += __uint_as_float(xk[t][i][e] << 16);
-          s1 += __uint_as_float(xk[t][i][e] & 0xffff0000u);
-        }
-      s1 += __shfl_xor(s1, 16, kWave);
-      s1 += __shfl_xor(s1, 32, kWave);
-      const float m = s1 * (1.0f / kIsD);
-      float s2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = __uint_as_float(xk[t][i][e] << 16) - m;
-          const float c = __uint_as_float(xk[t][i][e] & 0xffff0000u) - m;
-          s2 = fmaf(a, a, s2);
-          s2 = fmaf(c, c, s2);
-        }
-      s2 += __shfl_xor(s2, 16, kWave);
-      s2 += __shfl_xor(s2, 32, kWave);
-      mu[t] = m;
-      rs[t] = 1.0f / sqrtf(s2 * (1.0f / kIsD) + eps);
-    }
-  };
-  bool stats_done = false;
-
   for (int rb = r_begin; rb < r_end; rb += RPB) {
     const int nr = min(RPB, r_end - rb);
-    __syncthreads();  // previous batch's LDS reads are finished
-    // ---- stage g = q * gamma as (hi, lo) bf16 pairs, G, QB, w ----
+    __syncthreads();  // the previous batch's LDS reads are finished
     for (int u = tid; u < nr * H * 8; u += kIsThreads) {
-      const int rr = u / (H * 8), h = (u / 8) % H, part = u % 8;
-      const int r = rb + rr;
-      const uint16_t* qs = q + (size_t(r) * H + h) * kIsD + part * 16;
-      float gs = 0.f, qbs = 0.f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float qv[8], gm[8], bt[8];
-        load8(qs + half * 8, qv);
-        load8(gamma + part * 16 + half * 8, gm);
-        load8(beta + part * 16 + half * 8, bt);
-        uint16_t hi8[8], lo8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = qv[e] * gm[e];
-          const uint16_t hi = f2bf(g);
-          const uint16_t lo = f2bf(g - bf2f(hi));
-          hi8[e] = hi;
-          lo8[e] = lo;
-          gs += bf2f(hi) + bf2f(lo);
-          qbs = fmaf(qv[e], bt[e], qbs);
-        }
-        u32x4 ph, pl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ph[e] = uint32_t(hi8[2 * e]) | (uint32_t(hi8[2 * e + 1]) << 16);
-          pl[e] = uint32_t(lo8[2 * e]) | (uint32_t(lo8[2 * e + 1]) << 16);
-        }
-        *reinterpret_cast<u32x4*>(&sh.ghi[rr][h][part * 16 + half * 8]) = ph;
-        *reinterpret_cast<u32x4*>(&sh.glo[rr][h][part * 16 + half * 8]) = pl;
-      }
-      // reduce over the 8 consecutive threads of one (row, head)
-      gs += __shfl_xor(gs, 1, kWave);
-      gs += __shfl_xor(gs, 2, kWave);
-      gs += __shfl_xor(gs, 4, kWave);
-      qbs += __shfl_xor(qbs, 1, kWave);
-      qbs += __shfl_xor(qbs, 2, kWave);
-      qbs += __shfl_xor(qbs, 4, kWave);
-      if (part == 0) {
-        sh.G[rr][h] = gs;
-        sh.QB[rr][h] = qbs;
-        sh.W[rr][h] = w[size_t(r) * H + h];
-      }
+      const int rr = u / (H * 8);
+      const RowIn rin = stage_row_load(q + size_t(rb + rr) * H * kIsD, w + size_t(rb + rr) * H, gamma, beta,
+                                       u - rr * H * 8);
+      stage_row_store(rin, ghi[rr], glo[rr], sQB[rr], sW[rr], u - rr * H * 8);
     }
     if (tid < nr) {
-      sh.pos[tid] = row_pos[rb + tid];
-      sh.seq[tid] = row_seq[rb + tid];
+      s_pos[tid] = row_pos[rb + tid];
+      s_seq[tid] = row_seq[rb + tid];
     }
     __syncthreads();
-
     for (int rr = 0; rr < nr; ++rr) {
       const int r = rb + rr;
-      const int b = sh.seq[rr];
-      const int pos = sh.pos[rr];
+      const int b = s_seq[rr];
+      const int pos = s_pos[rr];
       float* srow = scores + size_t(r) * P_max;
       const bool ok = b >= 0 && b < B;
-      if (ok && b != b_loaded) {  // row of another sequence: reload its keys
+      if (ok && b != b_loaded) {
         b_loaded = b;
         load_keys(b);
-        stats_done = false;
       }
-      if (!ok) {
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-          const int p = p_wave + t * 16 + ln;
-          if (kg == 0 && p < P_max) srow[p] = -INFINITY;
-        }
-        continue;
-      }
-      if (!stats_done) {
-        ln_stats();
-        stats_done = true;
-      }
-      // A operands (g for this row): M-block mb, k-step i
       bf16x8 ahi[NH][4], alo[NH][4];
-      float cG[NH][4], cQ[NH][4], cW[NH][4];
-#pragma unroll
-      for (int mb = 0; mb < NH; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ahi[mb][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.ghi[rr][mb * 16 + ln][(kg + 4 * i) * 8]));
-          alo[mb][i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.glo[rr][mb * 16 + ln][(kg + 4 * i) * 8]));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = mb * 16 + 4 * kg + j;
-          cG[mb][j] = sh.G[rr][h];
-          cQ[mb][j] = sh.QB[rr][h];
-          cW[mb][j] = sh.W[rr][h];
-        }
-      }
+      float cQ[NH][4], cW[NH][4];
+      load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, ahi, alo, cQ, cW);
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
+        const float sc = tile_score<NH>(xk[t], ahi, alo, cQ, cW, scale, eps, ln);
         const int p = p_wave + t * 16 + ln;
-        int ps = -1, pv = 0;
         if (kg == 0 && p < P_max) {
-          ps = pool_start[size_t(b) * P_max + p];
-          pv = pool_valid[size_t(b) * P_max + p];
-        }
-        f32x4 acc[NH];
-#pragma unroll
-        for (int mb = 0; mb < NH; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x8 bx = as_bf16x8(xk[t][i]);
-#pragma unroll
-          for (int mb = 0; mb < NH; ++mb) {
-            acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
-            acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
-          }
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < NH; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float dot = rs[t] * (acc[mb][j] - mu[t] * cG[mb][j]) + cQ[mb][j];
-            part = fmaf(cW[mb][j], fmaxf(0.f, scale * dot), part);
-          }
-        part += __shfl_xor(part, 16, kWave);
-        part += __shfl_xor(part, 32, kWave);
-        if (kg == 0 && p < P_max) {
-          const bool cand = pv != 0 && ps + kp - 1 <= pos;
-          srow[p] = cand ? part : -INFINITY;
+          const bool cand = ok && pvk[t] != 0 && psk[t] + kp - 1 <= pos;
+          srow[p] = cand ? sc : -INFINITY;
         }
       }
     }
@@ -299,24 +360,29 @@ __global__ __launch_bounds__(256) void index_scores_generic(
   *out = s;
 }
 
-// Pools per workgroup and rows per workgroup for the MFMA path.
+// Launch shapes of the MFMA path.
 struct IsPlan {
-  int tiles;           // 16-pool tiles per wave (fixed at 4)
-  int rows_per_group;  // rows per workgroup (1: decode)
+  bool rows;  // false: decode kernel (one row per grid row)
+  int tw;     // decode: tiles per wave (2 or 8)
+  int rows_per_group;
 };
 
 static IsPlan is_plan(int Q, int P_max) {
-  // Decode (few rows): one row per workgroup, 4 tiles per wave (256 pools per
-  // workgroup): ~1000 workgroups at 4 x 65536 pools, all key loads in flight
-  // from the start.  Many rows: groups of rows share the keys held in registers.
-  IsPlan pl{4, 1};
-  if (Q > 64) {
-    const long chunks = (P_max + 255) / 256;
-    int groups = int((2048 + chunks - 1) / chunks);
-    if (groups < 1) groups = 1;
-    const int per = (Q + groups - 1) / groups;
-    pl.rows_per_group = per > 16 ? per : 16;
+  IsPlan pl{false, 8, 1};
+  const long ntile = (P_max + 15) / 16;
+  if (Q <= 64) {
+    // decode: 8 tiles per wave (32 KiB of keys per wave in flight) when that
+    // still gives >= 512 workgroups, else 2
+    pl.tw = long(Q) * ((ntile + 31) / 32) >= 512 ? 8 : 2;
+    return pl;
   }
+  // many rows: groups of rows of one sequence share the keys held in registers
+  pl.rows = true;
+  const long chunks = (P_max + 255) / 256;
+  int groups = int((2048 + chunks - 1) / chunks);
+  if (groups < 1) groups = 1;
+  const int per = (Q + groups - 1) / groups;
+  pl.rows_per_group = per > 16 ? per : 16;
   return pl;
 }
 
@@ -337,25 +403,36 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
   if (kpool > DSA_MAX_KPOOL) return DSA_ERR_UNSUPPORTED;
   if (H > 64 || (D != 32 && D != 64 && D != 128)) return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
-  if (Q > 65535 * 64) return DSA_ERR_UNSUPPORTED;
+  if (Q > 65535 * 16) return DSA_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (dtype == DSA_BF16 && D == 128 && (H == 16 || H == 32)) {
     const IsPlan pl = is_plan(Q, P_max);
-    const int pools_per_wg = kIsWaves * pl.tiles * 16;
-    dim3 grid(ceil_div(P_max, pools_per_wg), ceil_div(Q, pl.rows_per_group));
-    if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
-    auto args = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, scale,
-                         (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,
-                         row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores);
-    };
-    if (pl.rows_per_group == 1) {
-      if (H == 32) args(index_scores_mfma<2, 4, 1>);
-      else args(index_scores_mfma<1, 4, 1>);
-    } else {
-      if (H == 32) args(index_scores_mfma<2, 4, 4>);
-      else args(index_scores_mfma<1, 4, 4>);
+    if (!pl.rows) {
+      const int ntile = (P_max + 15) / 16;
+      dim3 grid(ceil_div(ntile, kIsWaves * pl.tw), Q);
+#define DSA_IS_DEC(NH, TW)                                                                            \
+  hipLaunchKernelGGL((index_scores_decode<NH, TW>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, \
+                     scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,   \
+                     row_seq, row_pos, B, P_max, kpool, scores)
+      if (H == 32) {
+        if (pl.tw == 8) DSA_IS_DEC(2, 8);
+        else DSA_IS_DEC(2, 2);
+      } else {
+        if (pl.tw == 8) DSA_IS_DEC(1, 8);
+        else DSA_IS_DEC(1, 2);
+      }
+#undef DSA_IS_DEC
+      return launch_status();
     }
+    dim3 grid(ceil_div(P_max, kIsWaves * 4 * 16), ceil_div(Q, pl.rows_per_group));
+    if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
+#define DSA_IS_ROWS(NH)                                                                               \
+  hipLaunchKernelGGL((index_scores_rows<NH, 4, 4>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
+                     w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
+                     ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
+    if (H == 32) DSA_IS_ROWS(2);
+    else DSA_IS_ROWS(1);
+#undef DSA_IS_ROWS
     return launch_status();
   }
   if (Q > 65535) return DSA_ERR_UNSUPPORTED;

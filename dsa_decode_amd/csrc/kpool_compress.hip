@@ -51,10 +51,12 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const uint8_t* _
   }
 }
 
-template <typename T>
+// KP (the kpool) is a template argument so that all 2*KP row loads of a
+// thread are issued before the first is used.
+template <typename T, int KP>
 __global__ __launch_bounds__(256) void pool_kernel(
     const T* __restrict__ k, const T* __restrict__ gate, const uint8_t* __restrict__ valid,
-    const float* __restrict__ ape, int T_max, int D, int kp, int P_max,
+    const float* __restrict__ ape, int T_max, int D, int P_max,
     const int32_t* __restrict__ n_pools, const int32_t* __restrict__ first_valid,
     T* __restrict__ k_pool, int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid) {
   const int b = blockIdx.y;
@@ -76,51 +78,71 @@ __global__ __launch_bounds__(256) void pool_kernel(
     }
     return;
   }
-  const int t0 = first_valid[b] + p * kp;
+  const int t0 = first_valid[b] + p * KP;
   const size_t row0 = size_t(b) * T_max + t0;
-  // slot logits gate + ape, per channel; max over the slot axis
-  float lg[DSA_MAX_KPOOL][8];
+  float lg[KP][8], kv[KP][8];
+#pragma unroll
+  for (int s = 0; s < KP; ++s) {
+    load8(gate + (row0 + s) * D + c0, lg[s]);
+    load8(k + (row0 + s) * D + c0, kv[s]);
+  }
+  // slot logits gate + ape and their max over the slot axis, per channel
   float mx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) mx[e] = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
-    if (s < kp) {
-      float g[8], a[8];
-      load8(gate + (row0 + s) * D + c0, g);
-      load8(ape + size_t(s) * D + c0, a);
+  for (int s = 0; s < KP; ++s) {
+    float a[8];
+    load8(ape + size_t(s) * D + c0, a);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lg[s][e] = g[e] + a[e];
-        mx[e] = fmaxf(mx[e], lg[s][e]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      lg[s][e] += a[e];
+      mx[e] = fmaxf(mx[e], lg[s][e]);
     }
   }
   float den[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { den[e] = 0.f; acc[e] = 0.f; }
 #pragma unroll
-  for (int s = 0; s < DSA_MAX_KPOOL; ++s) {
-    if (s < kp) {
-      float kv[8];
-      load8(k + (row0 + s) * D + c0, kv);
+  for (int s = 0; s < KP; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = expf(lg[s][e] - mx[e]);
-        den[e] += w;
-        acc[e] = fmaf(w, kv[e], acc[e]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float w = expf(lg[s][e] - mx[e]);
+      den[e] += w;
+      acc[e] = fmaf(w, kv[s][e], acc[e]);
     }
-  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = acc[e] / den[e];
   store8(dst, acc);
   if (c0 == 0) {
     int all = 1;
-    for (int s = 0; s < kp; ++s) all &= (valid[row0 + s] != 0);
+#pragma unroll
+    for (int s = 0; s < KP; ++s) all &= (valid[row0 + s] != 0);
     pool_start[size_t(b) * P_max + p] = t0;
     pool_valid[size_t(b) * P_max + p] = uint8_t(all);
   }
+}
+
+template <typename T>
+static void launch_pool(int kp, dim3 grid, hipStream_t s, const void* k, const void* gate,
+                        const uint8_t* valid, const float* ape, int T_max, int D, int P_max,
+                        const int32_t* n_pools, const int32_t* first_valid, void* k_pool,
+                        int32_t* pool_start, uint8_t* pool_valid) {
+#define DSA_POOL(KP)                                                                           \
+  hipLaunchKernelGGL((pool_kernel<T, KP>), grid, dim3(256), 0, s, (const T*)k, (const T*)gate, \
+                     valid, ape, T_max, D, P_max, n_pools, first_valid, (T*)k_pool, pool_start, \
+                     pool_valid)
+  switch (kp) {
+    case 1: DSA_POOL(1); break;
+    case 2: DSA_POOL(2); break;
+    case 3: DSA_POOL(3); break;
+    case 4: DSA_POOL(4); break;
+    case 5: DSA_POOL(5); break;
+    case 6: DSA_POOL(6); break;
+    case 7: DSA_POOL(7); break;
+    default: DSA_POOL(8); break;
+  }
+#undef DSA_POOL
 }
 
 }  // namespace dsa
@@ -149,12 +171,10 @@ extern "C" int dsa_kpool_compress(const void* k, const void* gate, const uint8_t
   const long work = long(P_max) * (D / 8);
   dim3 grid(ceil_div(work, 256), B);
   if (dtype == DSA_BF16)
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)k,
-                       (const uint16_t*)gate, valid, ape, T_max, D, kpool, P_max, n_pools,
-                       first_valid, (uint16_t*)k_pool, pool_start, pool_valid);
+    launch_pool<uint16_t>(kpool, grid, s, k, gate, valid, ape, T_max, D, P_max, n_pools, first_valid,
+                          k_pool, pool_start, pool_valid);
   else
-    hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s, (const float*)k,
-                       (const float*)gate, valid, ape, T_max, D, kpool, P_max, n_pools,
-                       first_valid, (float*)k_pool, pool_start, pool_valid);
+    launch_pool<float>(kpool, grid, s, k, gate, valid, ape, T_max, D, P_max, n_pools, first_valid,
+                       k_pool, pool_start, pool_valid);
   return launch_status();
 }

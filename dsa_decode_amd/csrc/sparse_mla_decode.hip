@@ -8,42 +8,46 @@
 // softmax-weighted sum of the same kv_j rows.
 //
 // MFMA path (bf16, Dl = 512, Hm = 16 * waves).  A workgroup handles one row and
-// a contiguous slice ("split") of its id list; each wave owns 16 heads.  Per
-// chunk of 32 ids the workgroup gathers the 32 latent rows (1 KiB each,
-// 16-byte loads) into LDS twice: row-major for the logits (contraction over
-// Dl) and transposed for the weighted sum (contraction over tokens), so that
-// every MFMA operand is one 16-byte LDS read.  Logits run as
-// S^T[token, head] = kv . q^T and the output as O^T[dl, head] = kv^T . P^T,
-// with an online (running max / running sum) softmax in the exp2 domain.
-// Splits write normalised fp32 partial outputs and their log-sum-exp; a
-// combine launch merges them.  The gather is the HBM traffic (1 KiB per
-// selected token); the two contractions are ~256 flop per gathered byte.
+// a contiguous slice ("split") of at most 64 ids of its list; each wave owns
+// 16 heads.  The workgroup gathers the split's latent rows (1 KiB each, 16-byte
+// loads) into LDS once, computes all logits S^T[token, head] = kv . q^T on the
+// matrix cores, takes the softmax of the split in one pass (no running
+// rescale), and accumulates O^T[dl, head] = kv^T . P^T.  The kv^T operand is
+// read from the same row-major LDS copy as eight 16-bit reads per lane; the
+// row swizzle makes both access patterns bank-conflict free.  Splits write
+// normalised fp32 partial outputs and their log-sum-exp; a combine launch
+// merges them.  The gather is the HBM traffic (1 KiB per selected token); the
+// two contractions are ~256 flop per gathered byte.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
 namespace dsa {
 
 constexpr int kMlaDl = 512;
-constexpr int kMlaChunk = 32;
+constexpr int kMlaSplit = 64;  // ids per workgroup
 
 struct MlaShared {
-  uint16_t rows[kMlaChunk][kMlaDl];  // 16-byte pieces swizzled per row
-  uint16_t cols[kMlaDl][kMlaChunk];  // 8-token groups swizzled per dl row
-  int ids[kMlaChunk];
+  uint16_t rows[kMlaSplit][kMlaDl];  // 16-byte pieces swizzled per row
+  int ids[kMlaSplit];
 };
 
-// rows: piece c of token row t sits at piece (c ^ row_swz(t)).  The 16 rows one
-// quarter-wave reads together (t = 8a + 4mb + j) get 16 distinct swizzles.
+// piece c of token row t sits at piece (c ^ row_swz(t)).  The 16 rows of one
+// logits read (t = 8a + 4b + j, a, j < 4) and the 4 row groups of one kv^T
+// read (t = 8kg + e) both land on distinct banks.
 __device__ __forceinline__ int row_swz(int t) { return (t & 3) | ((t >> 1) & 12); }
-// cols: 8-token group g of dl row d sits at group (g ^ col_swz(d)).
-__device__ __forceinline__ int col_swz(int d) { return (d >> 2) & 3; }
+
+// token held by row m of logits block mb: lane group kg of block pair
+// (2ks, 2ks+1) receives tokens 32ks + 8kg .. 32ks + 8kg + 7
+__device__ __forceinline__ int blk_token(int mb, int m) {
+  return 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3);
+}
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_decode_mfma(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_mfma(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Hm, int B,
-    int T_max, int W, int split_len, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int T_max, int W, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ MlaShared sh;
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -52,9 +56,17 @@ __global__ __launch_bounds__(NW * 64) void mla_decode_mfma(
   const int h = wave * 16 + ln;
   const int b = row_seq[r];
   const bool bok = b >= 0 && b < B;
-  const int c_begin = sp * split_len;
-  const int c_end = min(W, c_begin + split_len);
+  const int c_begin = sp * kMlaSplit;
 
+  if (tid < kMlaSplit) {
+    const int c = c_begin + tid;
+    int id = -1;
+    if (c < W) {
+      id = token_ids[size_t(r) * W + c];
+      if (!bok || id < 0 || id >= T_max) id = -1;
+    }
+    sh.ids[tid] = id;
+  }
   // q_lat of head h as the B operand of the logits: Dl piece kg + 4i at k-step i
   bf16x8 qop[16];
   {
@@ -62,100 +74,103 @@ __global__ __launch_bounds__(NW * 64) void mla_decode_mfma(
 #pragma unroll
     for (int i = 0; i < 16; ++i) qop[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + (kg + 4 * i) * 8));
   }
-  f32x4 o[32];
+  __syncthreads();
+  // gather: every load of this thread is issued before any LDS store (masked
+  // ids read a valid row and store zeros)
+  constexpr int kPieces = kMlaSplit * (kMlaDl / 8);
+  constexpr int kPer = (kPieces + NT - 1) / NT;
+  {
+    u32x4 v[kPer];
+    const size_t seq_base = size_t(bok ? b : 0) * T_max;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  for (int cb = c_begin; cb < c_end; cb += kMlaChunk) {
-    if (tid < kMlaChunk) {
-      const int c = cb + tid;
-      int id = -1;
-      if (c < c_end) {
-        id = token_ids[size_t(r) * W + c];
-        if (!bok || id < 0 || id >= T_max) id = -1;
-      }
-      sh.ids[tid] = id;
-    }
-    __syncthreads();
-    // gather the chunk's latent rows into both LDS layouts
-    for (int u = tid; u < kMlaChunk * (kMlaDl / 8); u += NT) {
-      const int t = u >> 6, c = u & 63;
+    for (int k = 0; k < kPer; ++k) {
+      const int u = min(tid + k * NT, kPieces - 1), t = u >> 6, c = u & 63;
       const int id = sh.ids[t];
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (id >= 0) v = *reinterpret_cast<const u32x4*>(kv + (size_t(b) * T_max + id) * kMlaDl + c * 8);
-      *reinterpret_cast<u32x4*>(&sh.rows[t][(c ^ row_swz(t)) * 8]) = v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = c * 8 + e;
-        const uint16_t val = uint16_t((e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu));
-        sh.cols[d][(((t >> 3) ^ col_swz(d)) << 3) + (t & 7)] = val;
-      }
+      v[k] = *reinterpret_cast<const u32x4*>(kv + (seq_base + (id >= 0 ? id : 0)) * kMlaDl + c * 8);
     }
-    __syncthreads();
-    // logits: block mb, A row ln holds token 8*(ln>>2) + 4*mb + (ln&3), so that
-    // lane group kg receives tokens 8*kg .. 8*kg+7
-    f32x4 sacc[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int t = 8 * (ln >> 2) + 4 * mb + (ln & 3);
-      const int sw = row_swz(t);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((kg + 4 * i) ^ sw) * 8]));
-        sacc[mb] = mfma16x16x32(a, qop[i], sacc[mb]);
-      }
+    for (int k = 0; k < kPer; ++k) {
+      const int u = tid + k * NT, t = u >> 6, c = u & 63;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if (u < kPieces) *reinterpret_cast<u32x4*>(&sh.rows[t][(c ^ row_swz(t)) * 8]) = sh.ids[t] >= 0 ? v[k] : z;
     }
-    float x[8];
-    float cmax = -INFINITY;
+  }
+  __syncthreads();
+
+  // logits, 4 blocks of 16 tokens
+  f32x4 sacc[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t = blk_token(mb, ln);
+    const int sw = row_swz(t);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = 4 * mb + j;
-        x[e] = sh.ids[8 * kg + e] >= 0 ? sacc[mb][j] * scale_log2 : -INFINITY;
-        cmax = fmaxf(cmax, x[e]);
-      }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, kWave));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-    uint32_t pk[4];
+    for (int i = 0; i < 16; ++i) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((kg + 4 * i) ^ sw) * 8]));
+      sacc[mb] = mfma16x16x32(a, qop[i], sacc[mb]);
+    }
+  }
+  // lane (kg, ln): head h, tokens 32ks + 8kg + e with e = 4*(mb & 1) + j, ks = mb >> 1
+  float x[16];
+  float m = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 32 * (mb >> 1) + 8 * kg + 4 * (mb & 1) + j;
+      x[4 * mb + j] = sh.ids[t] >= 0 ? sacc[mb][j] * scale_log2 : -INFINITY;
+      m = fmaxf(m, x[4 * mb + j]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  const float m_use = m == -INFINITY ? 0.f : m;
+  float l = 0.f;
+  uint32_t pk[2][4];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = exp2f(x[e] - m_use), p1 = exp2f(x[e + 1] - m_use);
-      psum += p0 + p1;
-      pk[e >> 1] = uint32_t(f2bf(p0)) | (uint32_t(f2bf(p1)) << 16);
+      const float p0 = exp2f(x[8 * ks + e] - m_use), p1 = exp2f(x[8 * ks + e + 1] - m_use);
+      l += p0 + p1;
+      pk[ks][e >> 1] = uint32_t(f2bf(p0)) | (uint32_t(f2bf(p1)) << 16);
     }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const bf16x8 pb = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  const bf16x8 pb0 = as_bf16x8(u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]});
+  const bf16x8 pb1 = as_bf16x8(u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]});
+
+  // O^T[dl, head] += kv^T[dl, tokens] . P^T[tokens, head]
+  f32x4 o[32];
 #pragma unroll
-    for (int blk = 0; blk < 32; ++blk) {
-      const int d = blk * 16 + ln;
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.cols[d][(kg ^ col_swz(d)) << 3]));
-      o[blk] *= alpha;
-      o[blk] = mfma16x16x32(a, pb, o[blk]);
+  for (int blk = 0; blk < 32; ++blk) {
+    const int d = blk * 16 + ln;
+    const int c = d >> 3, off = d & 7;
+    o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int t0 = 32 * ks + 8 * kg + e, t1 = t0 + 1;
+        const uint32_t lo = sh.rows[t0][((c ^ row_swz(t0)) << 3) + off];
+        const uint32_t hi = sh.rows[t1][((c ^ row_swz(t1)) << 3) + off];
+        wv[e >> 1] = lo | (hi << 16);
+      }
+      o[blk] = mfma16x16x32(as_bf16x8(u32x4{wv[0], wv[1], wv[2], wv[3]}), ks ? pb1 : pb0, o[blk]);
     }
-    __syncthreads();
   }
 
-  // o[blk][j] = O[head h][dl = 16*blk + 4*kg + j]
-  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-  const float lse_v = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+  // o[blk][j] = sum_t p_t kv[t][dl = 16*blk + 4*kg + j] for head h
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float lse_v = l > 0.f ? (m_use + log2f(l)) * 0.69314718055994531f : -INFINITY;
   if (nsplit == 1) {
     uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + 4 * kg;
 #pragma unroll
     for (int blk = 0; blk < 32; ++blk) {
-      u32x2 pk;
-      pk[0] = uint32_t(f2bf(o[blk][0] * inv)) | (uint32_t(f2bf(o[blk][1] * inv)) << 16);
-      pk[1] = uint32_t(f2bf(o[blk][2] * inv)) | (uint32_t(f2bf(o[blk][3] * inv)) << 16);
-      *reinterpret_cast<u32x2*>(dst + blk * 16) = pk;
+      u32x2 pkd;
+      pkd[0] = uint32_t(f2bf(o[blk][0] * inv)) | (uint32_t(f2bf(o[blk][1] * inv)) << 16);
+      pkd[1] = uint32_t(f2bf(o[blk][2] * inv)) | (uint32_t(f2bf(o[blk][3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
     }
     if (kg == 0 && lse) lse[size_t(r) * Hm + h] = lse_v;
   } else {
@@ -166,32 +181,51 @@ __global__ __launch_bounds__(NW * 64) void mla_decode_mfma(
   }
 }
 
-// Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.
+// Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  The
+// split weights are formed once in LDS; the partial loads are independent.
+constexpr int kMaxSplit = 256;
 __global__ __launch_bounds__(128) void mla_combine(const float* __restrict__ part_o,
                                                    const float* __restrict__ part_lse, int nsplit,
                                                    int Hm, uint16_t* __restrict__ out,
                                                    float* __restrict__ lse) {
-  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_lse[(size_t(r) * nsplit + s) * Hm + h]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float l = part_lse[(size_t(r) * nsplit + s) * Hm + h];
-      if (l == -INFINITY) continue;
-      const float wgt = expf(l - M);
-      wsum += wgt;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ((size_t(r) * nsplit + s) * Hm + h) * kMlaDl + 4 * tid);
-      acc += wgt * v;
-    }
+  __shared__ float wgt[kMaxSplit];
+  __shared__ float red[2];
+  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float lv = -INFINITY;
+  for (int s = tid; s < nsplit; s += 128) {
+    lv = part_lse[(size_t(r) * nsplit + s) * Hm + h];
+    wgt[s] = lv;
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  float M = -INFINITY;
+  for (int s = tid; s < nsplit; s += 128) M = fmaxf(M, wgt[s]);
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float ws = 0.f;
+  for (int s = tid; s < nsplit; s += 128) {
+    const float e = M == -INFINITY ? 0.f : expf(wgt[s] - M);
+    wgt[s] = e;
+    ws += e;
+  }
+  ws = wave_sum(ws);
+  __syncthreads();
+  if (lane == 0) red[wave] = ws;
+  __syncthreads();
+  ws = red[0] + red[1];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float* src = part_o + (size_t(r) * nsplit * Hm + h) * kMlaDl + 4 * tid;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + size_t(s) * Hm * kMlaDl);
+    acc += wgt[s] * v;
+  }
+  const float inv = ws > 0.f ? 1.0f / ws : 0.f;
   u32x2 pk;
   pk[0] = uint32_t(f2bf(acc[0] * inv)) | (uint32_t(f2bf(acc[1] * inv)) << 16);
   pk[1] = uint32_t(f2bf(acc[2] * inv)) | (uint32_t(f2bf(acc[3] * inv)) << 16);
   *reinterpret_cast<u32x2*>(out + (size_t(r) * Hm + h) * kMlaDl + 4 * tid) = pk;
-  if (tid == 0 && lse) lse[size_t(r) * Hm + h] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+  if (tid == 0 && lse) lse[size_t(r) * Hm + h] = ws > 0.f ? M + logf(ws) : -INFINITY;
 }
 
 // Generic path (fp32 or bf16, any Dl <= 512, any Hm): one workgroup per
@@ -265,22 +299,13 @@ __global__ __launch_bounds__(256) void mla_decode_generic(
 struct MlaPlan {
   bool mfma;
   int nsplit;
-  int split_len;
 };
 
 static MlaPlan mla_plan(int Q, int Hm, int Dl, int W, int dtype) {
-  MlaPlan pl{false, 1, W};
+  MlaPlan pl{false, 1};
   if (!(dtype == DSA_BF16 && Dl == kMlaDl && Hm % 16 == 0 && Hm <= 128)) return pl;
   pl.mfma = true;
-  // aim for ~256 workgroups, each with at least two 32-id chunks
-  const int max_split = (W + 63) / 64;
-  int ns = (256 + Q - 1) / Q;
-  if (ns > max_split) ns = max_split;
-  if (ns < 1) ns = 1;
-  int len = (W + ns - 1) / ns;
-  len = (len + kMlaChunk - 1) / kMlaChunk * kMlaChunk;
-  pl.split_len = len;
-  pl.nsplit = (W + len - 1) / len;
+  pl.nsplit = (W + kMlaSplit - 1) / kMlaSplit;
   return pl;
 }
 
@@ -308,6 +333,7 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
   if (Dl != 64 && Dl != 128 && Dl != 256 && Dl != 512) return DSA_ERR_UNSUPPORTED;
   if (Hm > 128 || Q > 65535) return DSA_ERR_UNSUPPORTED;
+  if (long(W) > long(kMlaSplit) * kMaxSplit) return DSA_ERR_UNSUPPORTED;
   const MlaPlan pl = mla_plan(Q, Hm, Dl, W, dtype);
   const size_t need = dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
@@ -336,8 +362,8 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
   const int nw = Hm / 16;
 #define DSA_MLA(NW)                                                                               \
   hipLaunchKernelGGL(mla_decode_mfma<NW>, grid, dim3(NW * 64), 0, s, (const uint16_t*)q_lat,     \
-                     (const uint16_t*)kv, row_seq, token_ids, Hm, B, T_max, W, pl.split_len,      \
-                     scale_log2, (uint16_t*)out, lse, part_o, part_lse)
+                     (const uint16_t*)kv, row_seq, token_ids, Hm, B, T_max, W, scale_log2,        \
+                     (uint16_t*)out, lse, part_o, part_lse)
   switch (nw) {
     case 1: DSA_MLA(1); break;
     case 2: DSA_MLA(2); break;

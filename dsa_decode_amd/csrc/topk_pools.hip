@@ -22,9 +22,7 @@
 
 namespace dsa {
 
-constexpr int kTkThreads = 1024;
-constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kTkMaxChunk = 32768;  // keys per workgroup (kTkThreads * 32)
+constexpr int kTkMaxChunk = 32768;  // keys per workgroup (1024 threads x 32)
 constexpr int kTkMaxSplit = 16;     // chunks merged by one merge launch
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -37,18 +35,20 @@ __device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
   return (uint64_t(score_key(f)) << 32) | uint64_t(0xffffffffu - idx);
 }
 
+template <int NT>
 struct TkShared {
-  uint32_t hist[kTkWaves][256];
+  static constexpr int NW = NT / kWave;
+  uint32_t hist[NW][256];
   uint64_t sel[DSA_MAX_SELECT_K];
-  uint64_t red[kTkWaves][2];
-  uint32_t cnt[kTkWaves];
+  uint64_t red[NW][2];
+  uint32_t cnt[NW];
   uint64_t bound[2];
   uint32_t bin_info[3];
   uint32_t nsel;
 };
 
-template <int KPT>
-__device__ __forceinline__ uint32_t block_count_valid(const uint64_t (&key)[KPT], TkShared& sh) {
+template <int NT, int KPT>
+__device__ __forceinline__ uint32_t block_count_valid(const uint64_t (&key)[KPT], TkShared<NT>& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t c = 0;
 #pragma unroll
@@ -58,16 +58,17 @@ __device__ __forceinline__ uint32_t block_count_valid(const uint64_t (&key)[KPT]
   if (lane == 0) sh.cnt[wave] = c;
   __syncthreads();
   uint32_t tot = 0;
-  for (int w = 0; w < kTkWaves; ++w) tot += sh.cnt[w];
+  for (int w = 0; w < TkShared<NT>::NW; ++w) tot += sh.cnt[w];
   __syncthreads();
   return tot;
 }
 
 // Returns (prefix, lo): the selected keys are exactly those != 0 with
 // (key >> lo) >= (prefix >> lo).  Requires n_valid > K.
-template <int KPT>
-__device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared& sh, uint64_t& prefix_out,
+template <int NT, int KPT>
+__device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh, uint64_t& prefix_out,
                              int& lo_out) {
+  constexpr int NW = TkShared<NT>::NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // block max / min of the valid keys
   uint64_t mx = 0, mn = ~uint64_t(0);
@@ -86,7 +87,7 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared& sh, ui
   if (lane == 0) { sh.red[wave][0] = mx; sh.red[wave][1] = mn; }
   __syncthreads();
   mx = 0; mn = ~uint64_t(0);
-  for (int w = 0; w < kTkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     mx = sh.red[w][0] > mx ? sh.red[w][0] : mx;
     mn = sh.red[w][1] < mn ? sh.red[w][1] : mn;
   }
@@ -101,7 +102,7 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared& sh, ui
     const int width = hi - lo + 1;
     const uint64_t dmask = (uint64_t(1) << width) - 1;
     // zero the per-wave histograms
-    for (int u = tid; u < kTkWaves * 256; u += kTkThreads) (&sh.hist[0][0])[u] = 0;
+    for (int u = tid; u < NW * 256; u += NT) (&sh.hist[0][0])[u] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -116,7 +117,7 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared& sh, ui
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t s = 0;
-        for (int w = 0; w < kTkWaves; ++w) s += sh.hist[w][4 * lane + i];
+        for (int w = 0; w < NW; ++w) s += sh.hist[w][4 * lane + i];
         c[i] = s;
       }
       const uint32_t lane_tot = c[0] + c[1] + c[2] + c[3];
@@ -152,11 +153,77 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared& sh, ui
   lo_out = lo;
 }
 
-// Sort sh.sel[0..n) descending (n <= kp2 <= DSA_MAX_SELECT_K, entries past n are 0).
-__device__ void bitonic_desc(TkShared& sh, int kp2) {
+// Exclusive prefix sum of one value per thread over the workgroup.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TkShared<NT>& sh, uint32_t& total) {
+  constexpr int NW = TkShared<NT>::NW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh.cnt[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  total = 0;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = sh.cnt[w];
+    base += w < wave ? c : 0u;
+    total += c;
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Sort 512 keys descending, two per thread: thread t < 256 holds elements 2t
+// (a0) and 2t+1 (a1).  Bitonic network; partners inside a wave are exchanged
+// with shuffles, the three cross-wave steps through LDS.  Threads >= 256 only
+// take part in the barriers.
+template <int NT>
+__device__ __forceinline__ void sort512_desc(uint64_t& a0, uint64_t& a1, TkShared<NT>& sh) {
+  const int t = threadIdx.x;
+  const bool act = t < 256;
+#pragma unroll
+  for (int k = 2; k <= 512; k <<= 1) {
+    const bool desc = ((2 * t) & k) == 0;
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 1) {
+        const bool sw = desc ? (a0 < a1) : (a0 > a1);
+        const uint64_t x = sw ? a1 : a0, y = sw ? a0 : a1;
+        a0 = x;
+        a1 = y;
+        continue;
+      }
+      const int tj = j >> 1;  // partner thread distance
+      uint64_t b0, b1;
+      if (tj < 64) {
+        b0 = __shfl_xor(a0, tj, kWave);
+        b1 = __shfl_xor(a1, tj, kWave);
+      } else {
+        if (act) { sh.sel[2 * t] = a0; sh.sel[2 * t + 1] = a1; }
+        __syncthreads();
+        if (act) { b0 = sh.sel[2 * (t ^ tj)]; b1 = sh.sel[2 * (t ^ tj) + 1]; }
+        __syncthreads();
+      }
+      const bool keep_max = ((t & tj) == 0) == desc;
+      if (act) {
+        a0 = keep_max ? (a0 > b0 ? a0 : b0) : (a0 < b0 ? a0 : b0);
+        a1 = keep_max ? (a1 > b1 ? a1 : b1) : (a1 < b1 ? a1 : b1);
+      }
+    }
+  }
+}
+
+// Sort sh.sel[0..kp2) descending in LDS (kp2 a power of two <= DSA_MAX_SELECT_K;
+// used when select_k > 512).
+template <int NT>
+__device__ void bitonic_desc(TkShared<NT>& sh, int kp2) {
   for (int k = 2; k <= kp2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < kp2; i += kTkThreads) {
+      for (int i = threadIdx.x; i < kp2; i += NT) {
         const int ixj = i ^ j;
         if (ixj > i) {
           const uint64_t a = sh.sel[i], b = sh.sel[ixj];
@@ -169,71 +236,90 @@ __device__ void bitonic_desc(TkShared& sh, int kp2) {
   }
 }
 
-// One workgroup: select the K largest keys of its KPT*kTkThreads keys and
+// One workgroup: select the K largest keys of its KPT*NT keys and
 // either write them unsorted to the workspace (partial) or sort and write ids.
-template <int KPT, bool FROM_SCORES, bool FINAL>
-__global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restrict__ scores,
+template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
                                                           const uint64_t* __restrict__ keys_in,
                                                           int P, int chunk, int nsplit_in, int K,
                                                           uint64_t* __restrict__ keys_out,
                                                           int32_t* __restrict__ pool_ids) {
-  __shared__ TkShared sh;
+  __shared__ TkShared<NT> sh;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int c = blockIdx.x;
   uint64_t key[KPT];
+  // all loads are issued before any is used (clamped, in-bounds addresses),
+  // so that they are in flight together
   if (FROM_SCORES) {
     const float* s = scores + size_t(row) * P;
     const int base = c * chunk;
     const int end = min(P, base + chunk);
+    float v[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int p = base + j * kTkThreads + tid;
-      key[j] = 0;
-      if (p < end) {
-        const float v = s[p];
-        if (v != -INFINITY) key[j] = make_key(v, uint32_t(p));
-      }
+      const int p = base + j * NT + tid;
+      v[j] = s[p < end ? p : P - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int p = base + j * NT + tid;
+      key[j] = (p < end && v[j] != -INFINITY) ? make_key(v[j], uint32_t(p)) : 0;
     }
   } else {
     const uint64_t* src = keys_in + size_t(row) * nsplit_in * K;
     const int n = nsplit_in * K;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int i = j * kTkThreads + tid;
-      key[j] = i < n ? src[i] : 0;
+      const int i = j * NT + tid;
+      key[j] = src[i < n ? i : n - 1];
     }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (j * NT + tid >= n) key[j] = 0;
   }
-  if (tid == 0) sh.nsel = 0;
-  const uint32_t nvalid = block_count_valid<KPT>(key, sh);  // has barriers
+  const uint32_t nvalid = block_count_valid<NT, KPT>(key, sh);  // has barriers
   uint64_t prefix = 1;
   int lo = 0;
-  if (nvalid > uint32_t(K)) radix_select<KPT>(key, K, sh, prefix, lo);
+  if (nvalid > uint32_t(K)) radix_select<NT, KPT>(key, K, sh, prefix, lo);
   const uint64_t thr = prefix >> lo;
-  const uint32_t nsel = nvalid < uint32_t(K) ? nvalid : uint32_t(K);
-  int kp2 = 1;
-  while (kp2 < K) kp2 <<= 1;
-  if (FINAL)
-    for (int i = tid; i < kp2; i += kTkThreads) sh.sel[i] = 0;
-  __syncthreads();
-  uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * gridDim.x + c) * K;
+  uint32_t mine = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint64_t k = key[j];
-    if (k != 0 && (k >> lo) >= thr) {
-      const uint32_t at = atomicAdd(&sh.nsel, 1u);
-      if (FINAL) sh.sel[at] = k;
-      else out[at] = k;
-    }
-  }
+  for (int j = 0; j < KPT; ++j) mine += (key[j] != 0 && (key[j] >> lo) >= thr) ? 1u : 0u;
+  uint32_t nsel = 0;
+  uint32_t at = block_excl_scan<NT>(mine, sh, nsel);   // nsel = min(K, nvalid)
   if (!FINAL) {
-    for (int i = int(nsel) + tid; i < K; i += kTkThreads) out[i] = 0;
+    uint64_t* out = keys_out + (size_t(row) * gridDim.x + c) * K;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (key[j] != 0 && (key[j] >> lo) >= thr) out[at++] = key[j];
+    for (int i = int(nsel) + tid; i < K; i += NT) out[i] = 0;
     return;
   }
+  int kp2 = 1;
+  while (kp2 < K) kp2 <<= 1;
+  if (kp2 < 512) kp2 = 512;
+  for (int i = tid; i < kp2; i += NT) sh.sel[i] = 0;
   __syncthreads();
-  bitonic_desc(sh, kp2);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (key[j] != 0 && (key[j] >> lo) >= thr) sh.sel[at++] = key[j];
+  __syncthreads();
   int32_t* dst = pool_ids + size_t(row) * K;
-  for (int i = tid; i < K; i += kTkThreads) {
+  if (kp2 == 512) {
+    uint64_t a0 = 0, a1 = 0;
+    if (tid < 256) { a0 = sh.sel[2 * tid]; a1 = sh.sel[2 * tid + 1]; }
+    __syncthreads();
+    sort512_desc<NT>(a0, a1, sh);
+    if (tid < 256) {
+      const int e0 = 2 * tid, e1 = 2 * tid + 1;
+      if (e0 < K) dst[e0] = (e0 < int(nsel) && a0 != 0) ? int32_t(0xffffffffu - uint32_t(a0)) : -1;
+      if (e1 < K) dst[e1] = (e1 < int(nsel) && a1 != 0) ? int32_t(0xffffffffu - uint32_t(a1)) : -1;
+    }
+    return;
+  }
+  bitonic_desc<NT>(sh, kp2);
+  for (int i = tid; i < K; i += NT) {
     const uint64_t k = sh.sel[i];
     dst[i] = (i < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
   }
@@ -242,8 +328,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_kernel(const float* __restric
 struct TkPlan {
   int nsplit;  // chunks per row (1: single launch)
   int chunk;   // pools per chunk
-  int kpt;     // keys per thread in the first launch
-  int kpt_merge;
+  int nt1, kpt1;  // first launch: threads and keys per thread
+  int nt2, kpt2;  // merge launch
 };
 
 static int pow2_at_least(long v) {
@@ -252,8 +338,15 @@ static int pow2_at_least(long v) {
   return p;
 }
 
+// threads and keys per thread for n keys: 256 threads while that needs at most
+// 32 keys each, else 1024 threads
+static void tk_shape(long n, int& nt, int& kpt) {
+  nt = n <= 256L * 32 ? 256 : 1024;
+  kpt = pow2_at_least((n + nt - 1) / nt);
+}
+
 static TkPlan tk_plan(int Q, int P, int K) {
-  TkPlan pl{1, P, 1, 0};
+  TkPlan pl{1, P, 256, 1, 256, 0};
   int nsplit = 1;
   if (P > kTkMaxChunk) nsplit = int((P + kTkMaxChunk - 1) / kTkMaxChunk);
   if (Q < 256) {
@@ -266,9 +359,26 @@ static TkPlan tk_plan(int Q, int P, int K) {
   }
   pl.nsplit = nsplit;
   pl.chunk = (P + nsplit - 1) / nsplit;
-  pl.kpt = pow2_at_least((pl.chunk + kTkThreads - 1) / kTkThreads);
-  pl.kpt_merge = nsplit > 1 ? pow2_at_least((long(nsplit) * K + kTkThreads - 1) / kTkThreads) : 0;
+  tk_shape(pl.chunk, pl.nt1, pl.kpt1);
+  if (nsplit > 1) tk_shape(long(nsplit) * K, pl.nt2, pl.kpt2);
   return pl;
+}
+
+template <int NT, bool FROM_SCORES, bool FINAL>
+static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, const uint64_t* keys_in,
+                      int P, int chunk, int nsplit_in, int K, uint64_t* keys_out, int32_t* pool_ids) {
+#define DSA_TK(KPT)                                                                                \
+  hipLaunchKernelGGL((topk_kernel<NT, KPT, FROM_SCORES, FINAL>), grid, dim3(NT), 0, s, scores,    \
+                     keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids)
+  switch (kpt) {
+    case 1: DSA_TK(1); break;
+    case 2: DSA_TK(2); break;
+    case 4: DSA_TK(4); break;
+    case 8: DSA_TK(8); break;
+    case 16: DSA_TK(16); break;
+    default: DSA_TK(32); break;
+  }
+#undef DSA_TK
 }
 
 }  // namespace dsa
@@ -289,44 +399,23 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
   if (long(P) > long(kTkMaxChunk) * kTkMaxSplit) return DSA_ERR_UNSUPPORTED;
   if (Q > 65535) return DSA_ERR_UNSUPPORTED;
   const TkPlan pl = tk_plan(Q, P, K);
-  if (pl.nsplit > kTkMaxSplit || pl.kpt > 32 || pl.kpt_merge > 32) return DSA_ERR_UNSUPPORTED;
+  if (pl.nsplit > kTkMaxSplit || pl.kpt1 > 32 || pl.kpt2 > 32) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa_topk_workspace_bytes(Q, P, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   uint64_t* ws = static_cast<uint64_t*>(workspace);
   dim3 g1(pl.nsplit, Q);
-#define DSA_TK1(KPT)                                                                              \
-  do {                                                                                            \
-    if (pl.nsplit == 1)                                                                           \
-      hipLaunchKernelGGL((topk_kernel<KPT, true, true>), g1, dim3(kTkThreads), 0, s, scores,      \
-                         nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);                          \
-    else                                                                                          \
-      hipLaunchKernelGGL((topk_kernel<KPT, true, false>), g1, dim3(kTkThreads), 0, s, scores,     \
-                         nullptr, P, pl.chunk, 0, K, ws, nullptr);                                \
-  } while (0)
-  switch (pl.kpt) {
-    case 1: DSA_TK1(1); break;
-    case 2: DSA_TK1(2); break;
-    case 4: DSA_TK1(4); break;
-    case 8: DSA_TK1(8); break;
-    case 16: DSA_TK1(16); break;
-    default: DSA_TK1(32); break;
+  if (pl.nsplit == 1) {
+    if (pl.nt1 == 256) launch_tk<256, true, true>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
+    else launch_tk<1024, true, true>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
+    return launch_status();
   }
-#undef DSA_TK1
+  if (pl.nt1 == 256) launch_tk<256, true, false>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
+  else launch_tk<1024, true, false>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
   int st = launch_status();
-  if (st || pl.nsplit == 1) return st;
+  if (st) return st;
   dim3 g2(1, Q);
-#define DSA_TK2(KPT)                                                                               \
-  hipLaunchKernelGGL((topk_kernel<KPT, false, true>), g2, dim3(kTkThreads), 0, s, nullptr, ws, P, \
-                     0, pl.nsplit, K, nullptr, pool_ids)
-  switch (pl.kpt_merge) {
-    case 1: DSA_TK2(1); break;
-    case 2: DSA_TK2(2); break;
-    case 4: DSA_TK2(4); break;
-    case 8: DSA_TK2(8); break;
-    case 16: DSA_TK2(16); break;
-    default: DSA_TK2(32); break;
-  }
-#undef DSA_TK2
+  if (pl.nt2 == 256) launch_tk<256, false, true>(pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
+  else launch_tk<1024, false, true>(pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
   return launch_status();
 }

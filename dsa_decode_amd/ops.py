@@ -144,3 +144,59 @@ def dsa_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, out=No
         ws_ptr, ws_bytes, _stream())
     check("dsa_sparse_mla_decode", st)
     return out, lse
+
+
+# ----------------------------------------------------------------------------
+# Pre-bound calls: the same entry points with their argument tuple marshalled
+# once, for loops that launch the same stage many times (benchmarks, serving
+# steps).  Calling the result launches on the stream captured at bind time.
+class BoundCall:
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name: str, args: tuple):
+        self.name = name
+        self.fn = getattr(_lib.load(), name)
+        self.args = args
+
+    def __call__(self) -> None:
+        st = self.fn(*self.args)
+        if st:
+            check(self.name, st)
+
+
+def bind_index_scores(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,
+                      row_pos, kpool, scores) -> BoundCall:
+    Q, H, D = q.shape
+    B, P_max, _ = k_pool.shape
+    return BoundCall("dsa_index_scores", (
+        _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
+        _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
+        _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps),
+        _dev(row_seq, "row_seq", torch.int32), _dev(row_pos, "row_pos", torch.int32), Q, H, D, B, P_max,
+        kpool, _act_code(k_pool), _dev(scores, "scores", torch.float32), _stream()))
+
+
+def bind_topk_pools(scores, K, pool_ids, workspace) -> BoundCall:
+    Q, P = scores.shape
+    return BoundCall("dsa_topk_pools", (
+        _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
+
+
+def bind_expand_selection(pool_ids, row_seq, pool_start, kpool, token_ids) -> BoundCall:
+    Q, K = pool_ids.shape
+    B, P_max = pool_start.shape
+    return BoundCall("dsa_expand_selection", (
+        _dev(pool_ids, "pool_ids", torch.int32), Q, K, _dev(row_seq, "row_seq", torch.int32),
+        _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool, _dev(token_ids, "token_ids", torch.int32),
+        token_ids.shape[1], _stream()))
+
+
+def bind_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale, out, lse, workspace) -> BoundCall:
+    Q, Hm, Dl = q_lat.shape
+    B, T_max, _ = kv.shape
+    return BoundCall("dsa_sparse_mla_decode", (
+        _dev(q_lat, "q_lat", kv.dtype), _dev(kv, "kv"), _dev(row_seq, "row_seq", torch.int32),
+        _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, T_max, token_ids.shape[1], float(sm_scale),
+        _act_code(kv), _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
