@@ -16,12 +16,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // bf16 is carried as its raw 16 bits (uint16_t) in memory.
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+
+// two fp32 -> packed bf16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Activation element access for fp32 and bf16 tensors.
@@ -53,7 +56,7 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = uint32_t(f2bf(v[2 * i])) | (uint32_t(f2bf(v[2 * i + 1])) << 16);
+  for (int i = 0; i < 4; ++i) r[i] = pack2bf(v[2 * i], v[2 * i + 1]);
   *reinterpret_cast<u32x4*>(p) = r;
 }
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {

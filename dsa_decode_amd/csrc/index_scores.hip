@@ -28,6 +28,8 @@
 //
 // Per pool the decode kernel reads 256 B of key + 1 B valid + 4 B start and
 // writes 4 B of score: it is HBM-bound.
+#include <climits>
+
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -230,6 +232,99 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_decode(
   }
 }
 
+// Streaming decode kernel: a workgroup owns kRingTiles consecutive 16-pool
+// tiles of one row; each wave runs through its tiles (w, w+4, ...) with a
+// 4-deep register ring (three tiles' key loads in flight while one is
+// computed).  Key rows are read with non-temporal loads (each byte is used
+// once).  The candidate test of the workgroup's pools is prepared in LDS up
+// front from coalesced loads of pool_start / pool_valid (one int per pool:
+// its first token if valid, else INT_MAX), and the workgroup's scores are
+// gathered in LDS and written with coalesced stores at the end.
+#ifndef DSA_IS_RING_TILES
+#define DSA_IS_RING_TILES 32
+#endif
+constexpr int kRing = 4;
+constexpr int kRingTiles = DSA_IS_RING_TILES;  // 16-pool tiles per workgroup
+constexpr int kRingPools = kRingTiles * 16;
+
+__device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int NH>
+__global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(3))) void index_scores_ring(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
+    const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
+    const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_pos, int B, int P_max, int kp, float* __restrict__ scores) {
+  constexpr int H = NH * 16;
+  __shared__ uint16_t ghi[H][kIsLd];
+  __shared__ uint16_t glo[H][kIsLd];
+  __shared__ float sQB[H], sW[H];
+  __shared__ int sStart[kRingPools];   // first token of a valid pool, INT_MAX otherwise
+  __shared__ float sOut[kRingPools];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, ln = lane & 15;
+  const int r = blockIdx.y;
+  const int b = row_seq[r];
+  const int pos = row_pos[r];
+  const bool ok = b >= 0 && b < B;
+  const int p0 = blockIdx.x * kRingPools;       // first pool of the workgroup
+  constexpr int nt = kRingTiles / kIsWaves;     // tiles per wave
+  u32x4 xb[kRing][4];
+  auto issue = [&](int slot, int j) {
+    const int p = p0 + (wave + kIsWaves * j) * 16 + ln;
+    const bool in = ok && j < nt && p < P_max;
+    const uint16_t* src = k_pool + (in ? size_t(b) * P_max + p : 0) * kIsD;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xb[slot][i] = ld_stream(src + (kg + 4 * i) * 8);
+  };
+  // operand / metadata loads first, then the first ring of key tiles
+  RowIn rin;
+  if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
+  int st[kRingPools / kIsThreads];
+  uint8_t vl[kRingPools / kIsThreads];
+#pragma unroll
+  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
+    const int p = p0 + u * kIsThreads + tid;
+    const size_t pi = (ok && p < P_max) ? size_t(b) * P_max + p : 0;
+    st[u] = pool_start[pi];
+    vl[u] = pool_valid[pi];
+  }
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) issue(s, s);
+  if (tid < H * 8) stage_row_store(rin, ghi, glo, sQB, sW, tid);
+#pragma unroll
+  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
+    const int p = p0 + u * kIsThreads + tid;
+    sStart[u * kIsThreads + tid] = (ok && p < P_max && vl[u] != 0) ? st[u] : INT_MAX;
+  }
+  __syncthreads();
+  bf16x8 ahi[NH][4], alo[NH][4];
+  float cQ[NH][4], cW[NH][4];
+  load_operands<NH>(ghi, glo, sQB, sW, kg, ln, ahi, alo, cQ, cW);
+  const int last_ok = pos - (kp - 1);            // candidate iff its start <= last_ok
+#pragma unroll
+  for (int j0 = 0; j0 < nt; j0 += kRing) {
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int j = j0 + s;
+      const float sc = tile_score<NH>(xb[s], ahi, alo, cQ, cW, scale, eps, ln);
+      const int lp = (wave + kIsWaves * j) * 16 + ln;   // pool within the workgroup
+      if (kg == 0) sOut[lp] = sStart[lp] <= last_ok ? sc : -INFINITY;
+      issue(s, j + kRing);
+    }
+  }
+  __syncthreads();
+  float* srow = scores + size_t(r) * P_max;
+#pragma unroll
+  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
+    const int p = p0 + u * kIsThreads + tid;
+    if (p < P_max) srow[p] = sOut[u * kIsThreads + tid];
+  }
+}
+
 template <int NH, int kTiles, int RPB>
 __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
@@ -361,9 +456,17 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 }
 
 // Launch shapes of the MFMA path.
+// Decode launch shape (tuned on MI355X at 4 x 65536 pools)
+#ifndef DSA_IS_DECODE
+#define DSA_IS_DECODE 1  // 1: streaming ring kernel; 0: all loads up front, DSA_IS_TW tiles per wave
+#endif
+#ifndef DSA_IS_TW
+#define DSA_IS_TW 8
+#endif
+
 struct IsPlan {
   bool rows;  // false: decode kernel (one row per grid row)
-  int tw;     // decode: tiles per wave (2 or 8)
+  int tw;     // decode: tiles per wave
   int rows_per_group;
 };
 
@@ -373,7 +476,7 @@ static IsPlan is_plan(int Q, int P_max) {
   if (Q <= 64) {
     // decode: 8 tiles per wave (32 KiB of keys per wave in flight) when that
     // still gives >= 512 workgroups, else 2
-    pl.tw = long(Q) * ((ntile + 31) / 32) >= 512 ? 8 : 2;
+    pl.tw = long(Q) * ((ntile + 4 * DSA_IS_TW - 1) / (4 * DSA_IS_TW)) >= 512 ? DSA_IS_TW : 2;
     return pl;
   }
   // many rows: groups of rows of one sequence share the keys held in registers
@@ -409,16 +512,24 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
     const IsPlan pl = is_plan(Q, P_max);
     if (!pl.rows) {
       const int ntile = (P_max + 15) / 16;
+      if (DSA_IS_DECODE == 1) {
+        dim3 grid(ceil_div(P_max, kRingPools), Q);
+        auto kr = H == 32 ? index_scores_ring<2> : index_scores_ring<1>;
+        hipLaunchKernelGGL(kr, grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, scale,
+                           (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,
+                           row_seq, row_pos, B, P_max, kpool, scores);
+        return launch_status();
+      }
       dim3 grid(ceil_div(ntile, kIsWaves * pl.tw), Q);
 #define DSA_IS_DEC(NH, TW)                                                                            \
   hipLaunchKernelGGL((index_scores_decode<NH, TW>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, \
                      scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,   \
                      row_seq, row_pos, B, P_max, kpool, scores)
       if (H == 32) {
-        if (pl.tw == 8) DSA_IS_DEC(2, 8);
+        if (pl.tw == DSA_IS_TW) DSA_IS_DEC(2, DSA_IS_TW);
         else DSA_IS_DEC(2, 2);
       } else {
-        if (pl.tw == 8) DSA_IS_DEC(1, 8);
+        if (pl.tw == DSA_IS_TW) DSA_IS_DEC(1, DSA_IS_TW);
         else DSA_IS_DEC(1, 2);
       }
 #undef DSA_IS_DEC

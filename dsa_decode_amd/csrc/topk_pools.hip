@@ -11,8 +11,8 @@
 //
 // Selection is a radix select inside one workgroup over keys held in
 // registers: the bits common to the row's largest and smallest key are
-// skipped, then 8-bit digits are histogrammed (one LDS histogram per wave)
-// until the bin holding the K-th key is exactly consumed.  Long rows are split
+// skipped, then 11-bit digits are histogrammed in LDS until the bin holding the
+// K-th key is exactly consumed (about three passes for distinct scores).  Long rows are split
 // into chunks whose K largest keys go to a workspace; a merge launch selects
 // the K largest of the chunk winners (the K largest of a union are among the
 // K largest of each part, so this is exact).  The final K keys are sorted with
@@ -35,10 +35,13 @@ __device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
   return (uint64_t(score_key(f)) << 32) | uint64_t(0xffffffffu - idx);
 }
 
+constexpr int kDig = 11;              // radix digit width
+constexpr int kBins = 1 << kDig;      // 2048 bins, 32 per lane of the scanning wave
+
 template <int NT>
 struct TkShared {
   static constexpr int NW = NT / kWave;
-  uint32_t hist[NW][256];
+  uint32_t hist[kBins];
   uint64_t sel[DSA_MAX_SELECT_K];
   uint64_t red[NW][2];
   uint32_t cnt[NW];
@@ -47,80 +50,85 @@ struct TkShared {
   uint32_t nsel;
 };
 
+// Number of valid keys and their max / min over the workgroup (one barrier;
+// the LDS slots are not rewritten before the caller's next barrier).
 template <int NT, int KPT>
-__device__ __forceinline__ uint32_t block_count_valid(const uint64_t (&key)[KPT], TkShared<NT>& sh) {
+__device__ __forceinline__ uint32_t block_stats(const uint64_t (&key)[KPT], TkShared<NT>& sh, uint64_t& mx,
+                                                uint64_t& mn) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) c += key[j] != 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
-  if (lane == 0) sh.cnt[wave] = c;
-  __syncthreads();
-  uint32_t tot = 0;
-  for (int w = 0; w < TkShared<NT>::NW; ++w) tot += sh.cnt[w];
-  __syncthreads();
-  return tot;
-}
-
-// Returns (prefix, lo): the selected keys are exactly those != 0 with
-// (key >> lo) >= (prefix >> lo).  Requires n_valid > K.
-template <int NT, int KPT>
-__device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh, uint64_t& prefix_out,
-                             int& lo_out) {
-  constexpr int NW = TkShared<NT>::NW;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // block max / min of the valid keys
-  uint64_t mx = 0, mn = ~uint64_t(0);
+  mx = 0;
+  mn = ~uint64_t(0);
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (key[j] != 0) {
+      ++c;
       mx = key[j] > mx ? key[j] : mx;
       mn = key[j] < mn ? key[j] : mn;
     }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
+    c += __shfl_xor(c, o, kWave);
     const uint64_t a = __shfl_xor(mx, o, kWave), b = __shfl_xor(mn, o, kWave);
     mx = a > mx ? a : mx;
     mn = b < mn ? b : mn;
   }
-  if (lane == 0) { sh.red[wave][0] = mx; sh.red[wave][1] = mn; }
+  if (lane == 0) {
+    sh.cnt[wave] = c;
+    sh.red[wave][0] = mx;
+    sh.red[wave][1] = mn;
+  }
   __syncthreads();
-  mx = 0; mn = ~uint64_t(0);
-  for (int w = 0; w < NW; ++w) {
+  uint32_t tot = 0;
+  mx = 0;
+  mn = ~uint64_t(0);
+  for (int w = 0; w < TkShared<NT>::NW; ++w) {
+    tot += sh.cnt[w];
     mx = sh.red[w][0] > mx ? sh.red[w][0] : mx;
     mn = sh.red[w][1] < mn ? sh.red[w][1] : mn;
   }
+  return tot;
+}
+
+// Returns (prefix, lo): the selected keys are exactly those != 0 with
+// (key >> lo) >= (prefix >> lo).  Requires n_valid > K; mx / mn are the largest
+// and smallest valid keys.
+template <int NT, int KPT>
+__device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh, uint64_t mx, uint64_t mn,
+                             uint64_t& prefix_out, int& lo_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // n_valid > K >= 1 and keys are distinct, so mx != mn
   const int top = 63 - __clzll(mx ^ mn);      // highest differing bit
   uint64_t prefix = (top == 63) ? 0 : (mx >> (top + 1)) << (top + 1);
   uint32_t need = uint32_t(K);
   int hi = top;
   int lo = 0;
+  for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
+  __syncthreads();
   while (true) {
-    lo = hi >= 7 ? hi - 7 : 0;
+    lo = hi >= kDig - 1 ? hi - (kDig - 1) : 0;
     const int width = hi - lo + 1;
     const uint64_t dmask = (uint64_t(1) << width) - 1;
-    // zero the per-wave histograms
-    for (int u = tid; u < NW * 256; u += NT) (&sh.hist[0][0])[u] = 0;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint64_t k = key[j];
       const bool match = k != 0 && (hi == 63 || (k >> (hi + 1)) == (prefix >> (hi + 1)));
-      if (match) atomicAdd(&sh.hist[wave][uint32_t((k >> lo) & dmask)], 1u);
+      if (match) atomicAdd(&sh.hist[uint32_t((k >> lo) & dmask)], 1u);
     }
     __syncthreads();
     if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; suffix sums over bins (high to low)
-      uint32_t c[4];
+      // lane owns bins 32*lane .. 32*lane+31 (read, then cleared for the next
+      // pass); suffix sums over bins (high to low)
+      u32x4* hv = reinterpret_cast<u32x4*>(&sh.hist[32 * lane]);
+      u32x4 cv[8];
+      uint32_t lane_tot = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t s = 0;
-        for (int w = 0; w < NW; ++w) s += sh.hist[w][4 * lane + i];
-        c[i] = s;
+      for (int i = 0; i < 8; ++i) {
+        cv[i] = hv[i];
+        lane_tot += (cv[i][0] + cv[i][1]) + (cv[i][2] + cv[i][3]);
       }
-      const uint32_t lane_tot = c[0] + c[1] + c[2] + c[3];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hv[i] = u32x4{0u, 0u, 0u, 0u};
       uint32_t incl = lane_tot;  // sum over lanes >= lane
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -130,9 +138,13 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh
       uint32_t above = incl - lane_tot;  // keys in bins of higher lanes
       int found = -1;
       uint32_t f_above = 0, f_cnt = 0;
-      for (int i = 3; i >= 0; --i) {
-        if (found < 0 && above + c[i] >= need) { found = 4 * lane + i; f_above = above; f_cnt = c[i]; }
-        above += c[i];
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          if (found < 0 && above + cv[i][e] >= need) { found = 32 * lane + 4 * i + e; f_above = above; f_cnt = cv[i][e]; }
+          above += cv[i][e];
+        }
       }
       // exactly one lane holds the bin where the running count first reaches need
       if (found >= 0 && f_above < need) {
@@ -142,8 +154,8 @@ __device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh
       }
     }
     __syncthreads();
+    // bin_info is rewritten only after the next pass's barrier
     const uint32_t d = sh.bin_info[0], above = sh.bin_info[1], cnt = sh.bin_info[2];
-    __syncthreads();
     prefix |= uint64_t(d) << lo;
     need -= above;
     if (cnt == need || lo == 0) break;
@@ -177,43 +189,82 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TkShared<NT>& sh
   return base + incl - v;
 }
 
+// value of lane (lane ^ TJ) for TJ < 32: DPP for 1, 2, 4, 8 (quad permutes,
+// row shifts and the 8-lane row rotate), ds_swizzle (xor mode) for 16
+template <int TJ>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (TJ == 1) {
+    return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (TJ == 2) {
+    return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (TJ == 4) {
+    const uint32_t up = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);  // row_shl:4 (lane + 4)
+    const uint32_t dn = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);  // row_shr:4 (lane - 4)
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (TJ == 8) {
+    return __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else {
+    static_assert(TJ == 16, "in-wave xor distance");
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                     // xor 16 within 32 lanes
+  }
+}
+
+template <int TJ>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  if constexpr (TJ < 32) {
+    const uint32_t lo = xor_lane<TJ>(uint32_t(v)), hi = xor_lane<TJ>(uint32_t(v >> 32));
+    return (uint64_t(hi) << 32) | lo;
+  } else {
+    return __shfl_xor(v, TJ, kWave);
+  }
+}
+
+// one compare-exchange step of the bitonic network: element pair distance j =
+// 2*TJ (thread distance TJ), sort direction from k
+template <int NT, int TJ>
+__device__ __forceinline__ void bitonic_step(uint64_t& a0, uint64_t& a1, int k, TkShared<NT>& sh) {
+  const int t = threadIdx.x;
+  const bool act = t < 256;
+  const bool desc = ((2 * t) & k) == 0;
+  uint64_t b0 = 0, b1 = 0;
+  if constexpr (TJ < 64) {
+    b0 = xor_lane64<TJ>(a0);
+    b1 = xor_lane64<TJ>(a1);
+  } else {
+    if (act) { sh.sel[2 * t] = a0; sh.sel[2 * t + 1] = a1; }
+    __syncthreads();
+    if (act) { b0 = sh.sel[2 * (t ^ TJ)]; b1 = sh.sel[2 * (t ^ TJ) + 1]; }
+    __syncthreads();
+  }
+  const bool keep_max = ((t & TJ) == 0) == desc;
+  a0 = keep_max ? (a0 > b0 ? a0 : b0) : (a0 < b0 ? a0 : b0);
+  a1 = keep_max ? (a1 > b1 ? a1 : b1) : (a1 < b1 ? a1 : b1);
+}
+
 // Sort 512 keys descending, two per thread: thread t < 256 holds elements 2t
-// (a0) and 2t+1 (a1).  Bitonic network; partners inside a wave are exchanged
-// with shuffles, the three cross-wave steps through LDS.  Threads >= 256 only
-// take part in the barriers.
+// (a0) and 2t+1 (a1).  Bitonic network: the j = 1 exchanges stay in a thread,
+// in-wave partners are exchanged with DPP / swizzle / shuffles, and the three
+// cross-wave steps go through LDS.  Threads >= 256 only take part in barriers
+// (their results are discarded).
 template <int NT>
 __device__ __forceinline__ void sort512_desc(uint64_t& a0, uint64_t& a1, TkShared<NT>& sh) {
   const int t = threadIdx.x;
-  const bool act = t < 256;
 #pragma unroll
   for (int k = 2; k <= 512; k <<= 1) {
     const bool desc = ((2 * t) & k) == 0;
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j == 1) {
-        const bool sw = desc ? (a0 < a1) : (a0 > a1);
-        const uint64_t x = sw ? a1 : a0, y = sw ? a0 : a1;
-        a0 = x;
-        a1 = y;
-        continue;
-      }
-      const int tj = j >> 1;  // partner thread distance
-      uint64_t b0, b1;
-      if (tj < 64) {
-        b0 = __shfl_xor(a0, tj, kWave);
-        b1 = __shfl_xor(a1, tj, kWave);
-      } else {
-        if (act) { sh.sel[2 * t] = a0; sh.sel[2 * t + 1] = a1; }
-        __syncthreads();
-        if (act) { b0 = sh.sel[2 * (t ^ tj)]; b1 = sh.sel[2 * (t ^ tj) + 1]; }
-        __syncthreads();
-      }
-      const bool keep_max = ((t & tj) == 0) == desc;
-      if (act) {
-        a0 = keep_max ? (a0 > b0 ? a0 : b0) : (a0 < b0 ? a0 : b0);
-        a1 = keep_max ? (a1 > b1 ? a1 : b1) : (a1 < b1 ? a1 : b1);
-      }
-    }
+    if (k >= 512) bitonic_step<NT, 128>(a0, a1, k, sh);
+    if (k >= 256) bitonic_step<NT, 64>(a0, a1, k, sh);
+    if (k >= 128) bitonic_step<NT, 32>(a0, a1, k, sh);
+    if (k >= 64) bitonic_step<NT, 16>(a0, a1, k, sh);
+    if (k >= 32) bitonic_step<NT, 8>(a0, a1, k, sh);
+    if (k >= 16) bitonic_step<NT, 4>(a0, a1, k, sh);
+    if (k >= 8) bitonic_step<NT, 2>(a0, a1, k, sh);
+    if (k >= 4) bitonic_step<NT, 1>(a0, a1, k, sh);
+    // j = 1: the thread's own pair
+    const bool sw = desc ? (a0 < a1) : (a0 > a1);
+    const uint64_t x = sw ? a1 : a0, y = sw ? a0 : a1;
+    a0 = x;
+    a1 = y;
   }
 }
 
@@ -278,21 +329,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     for (int j = 0; j < KPT; ++j)
       if (j * NT + tid >= n) key[j] = 0;
   }
-  const uint32_t nvalid = block_count_valid<NT, KPT>(key, sh);  // has barriers
+  uint64_t kmax, kmin;
+  const uint32_t nvalid = block_stats<NT, KPT>(key, sh, kmax, kmin);  // one barrier
   uint64_t prefix = 1;
   int lo = 0;
-  if (nvalid > uint32_t(K)) radix_select<NT, KPT>(key, K, sh, prefix, lo);
+  if (nvalid > uint32_t(K)) radix_select<NT, KPT>(key, K, sh, kmax, kmin, prefix, lo);
   const uint64_t thr = prefix >> lo;
-  uint32_t mine = 0;
+  uint32_t selmask = 0;  // bit j: key[j] is selected (KPT <= 32)
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) mine += (key[j] != 0 && (key[j] >> lo) >= thr) ? 1u : 0u;
+  for (int j = 0; j < KPT; ++j) selmask |= (key[j] != 0 && (key[j] >> lo) >= thr) ? (1u << j) : 0u;
   uint32_t nsel = 0;
-  uint32_t at = block_excl_scan<NT>(mine, sh, nsel);   // nsel = min(K, nvalid)
+  uint32_t at = block_excl_scan<NT>(uint32_t(__builtin_popcount(selmask)), sh, nsel);  // nsel = min(K, nvalid)
   if (!FINAL) {
     uint64_t* out = keys_out + (size_t(row) * gridDim.x + c) * K;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (key[j] != 0 && (key[j] >> lo) >= thr) out[at++] = key[j];
+      if ((selmask >> j) & 1u) out[at++] = key[j];
     for (int i = int(nsel) + tid; i < K; i += NT) out[i] = 0;
     return;
   }
@@ -303,7 +355,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    if (key[j] != 0 && (key[j] >> lo) >= thr) sh.sel[at++] = key[j];
+    if ((selmask >> j) & 1u) sh.sel[at++] = key[j];
   __syncthreads();
   int32_t* dst = pool_ids + size_t(row) * K;
   if (kp2 == 512) {
