@@ -10,10 +10,11 @@ cache comes from an untimed dsa_kpool_compress over synthetic tokens.
 Inputs are resident in HBM before the timed region.  Eight replicas of the
 pool cache and of the latent cache (about 8.5 GiB) rotate from step to step, so
 the 256 MB last-level cache cannot serve a step from the previous one.  Each
-step is replayed from HIP graphs captured per replica (one graph holding the
-score kernel, one the rest); HIP events on the same stream bracket the score
-graph of every timed step, which gives that kernel's per-launch time for the
-roofline line.
+step launches the four stages from argument tuples bound once per replica
+(``--mode graph`` replays HIP graphs captured per replica instead); HIP events
+on the launch stream bracket the score kernel of every timed step, which gives
+that kernel's per-launch time for the roofline line.  The roofline's traffic
+figure comes from the committed counter summary of the same kernel source.
 
 Prints ONE JSON line.
 """
@@ -39,10 +40,42 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="eager")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 64 MiB device copy first (a known-size kernel for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_scores_traffic.txt")
+SCORE_SOURCES = [os.path.join(ROOT, "dsa_decode_amd", "csrc", f) for f in ("index_scores.hip", "dsa_common.hpp")]
+
+
+def score_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per score-kernel launch from the committed counter summary, or
+    None when it is missing or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != score_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def score_bytes_per_pool() -> int:
@@ -64,6 +97,12 @@ def main() -> int:
     _lib.load()
     torch.cuda.set_device(0)
     dev = lambda t: t.contiguous().cuda()
+    if args.copy_probe:
+        a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     wl = synth.workload("long")
     Q, P, K, W = wl.Q, wl.P_max, wl.K, wl.W
@@ -201,9 +240,9 @@ def main() -> int:
                    "replicas": REPLICAS},
         "tokens_per_s": round(steps_per_s * Q, 1),
         "stages_us": stages_us,
-        "roofline": {"bound": "hbm", "kernel": "index_scores_mfma", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "index_scores_ring", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "launch_us": round(score_us_mean, 3),
+                     "traffic": measured_traffic(), "launch_us": round(score_us_mean, 3),
                      "algorithmic_bytes": bytes_per_launch},
         "cpu_baseline": cpu,
     }
