@@ -67,6 +67,14 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
+// Buffer resource over [p, p + bytes) (bytes < 2^31).  A load whose per-lane
+// offset is at or past `bytes` returns 0 (the hardware range check), so loads
+// need no clamped addresses and no per-lane 64-bit pointers.  Offsets go in
+// the per-lane operand: the range check does not cover the scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 r) { return __builtin_bit_cast(bf16x8, r); }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row

@@ -3,20 +3,26 @@
 // indexer is REPLICATED, not sharded": higher score first, then the smaller
 // pool index).
 //
-// Every candidate becomes one 64-bit key: the high word maps the fp32 score to
-// an unsigned integer with the same order (-0 folded onto +0), the low word is
-// 0xffffffff - pool index.  Larger key = earlier in the output, and all keys of
-// a row are distinct, so "the K largest keys" is exactly the wanted set and
-// "keys descending" exactly the wanted order.  Key 0 means "no candidate".
+// Order.  Every candidate is the pair (hi, lo): hi maps the fp32 score to a
+// nonzero u32 with the same order (-0 folded onto +0; 0 marks a non-candidate),
+// lo = 0xffffffff - pool index.  The 64-bit key (hi << 32 | lo) is larger
+// exactly when the pool comes earlier in the output, and all keys of a row are
+// distinct, so "the K largest keys" is the wanted set and "keys descending"
+// the wanted order.
 //
 // Selection is a radix select inside one workgroup over keys held in
-// registers: the bits common to the row's largest and smallest key are
-// skipped, then 11-bit digits are histogrammed in LDS until the bin holding the
-// K-th key is exactly consumed (about three passes for distinct scores).  Long rows are split
-// into chunks whose K largest keys go to a workspace; a merge launch selects
-// the K largest of the chunk winners (the K largest of a union are among the
-// K largest of each part, so this is exact).  The final K keys are sorted with
-// a bitonic network in LDS and written as pool ids, -1 padded.
+// registers, latency first (a decode row has only a few workgroups in flight):
+//  * the bits common to the largest and smallest hi are skipped, then 11-bit
+//    digits of hi are histogrammed in LDS until the bin holding the K-th key is
+//    exactly consumed (two passes for distinct scores);
+//  * the histogram is scanned by one wave with DPP prefix sums and ballots;
+//  * only when the K-th score is tied do keys go further: by position (a
+//    ballot rank) when they come straight from the scores, by the lo digits
+//    when they come from chunk winners.
+// Long rows are split into chunks whose K largest keys go to a workspace; a
+// merge launch selects the K largest of the chunk winners (the K largest of a
+// union are among the K largest of each part, so this is exact).  The final K
+// keys are sorted with a bitonic network and written as pool ids, -1 padded.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -25,168 +31,199 @@ namespace dsa {
 constexpr int kTkMaxChunk = 32768;  // keys per workgroup (1024 threads x 32)
 constexpr int kTkMaxSplit = 16;     // chunks merged by one merge launch
 
+// Order-preserving map of a score to a nonzero u32; 0 for a non-candidate
+// (-inf, and NaN, which the interface excludes).
+// Written with selects only, so that a loop of them stays branch-free.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) == 0u) u = 0u;  // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = (u << 1) == 0u ? 0u : u;  // -0 -> +0
+  const uint32_t k = int32_t(u) < 0 ? ~u : (u | 0x80000000u);
+  return f > -INFINITY ? k : 0u;
 }
 
-__device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
-  return (uint64_t(score_key(f)) << 32) | uint64_t(0xffffffffu - idx);
+// The score a key stands for (inverse of score_key for candidates).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float(int32_t(k) < 0 ? (k & 0x7fffffffu) : ~k);
 }
 
 constexpr int kDig = 11;              // radix digit width
 constexpr int kBins = 1 << kDig;      // 2048 bins, 32 per lane of the scanning wave
+constexpr int kRankCap = 64;          // largest bin that is ordered by pairwise ranks
+
+// ---------------------------------------------------------------- wave helpers
+// v from lane (lane - n) of the same row of 16 lanes, 0 for the first n lanes
+template <int N>
+__device__ __forceinline__ uint32_t row_shr(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x110 + N, 0xF, 0xF, true));
+}
+
+// inclusive prefix sum over the wave: DPP shifts within rows of 16, then the
+// row broadcasts (lane 15 of a row into the next row, lane 31 into rows 2, 3)
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// maximum over the wave (wave-uniform result)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, row_shr<1>(v));
+  v = max(v, row_shr<2>(v));
+  v = max(v, row_shr<4>(v));
+  v = max(v, row_shr<8>(v));
+  return max(max(uint32_t(__builtin_amdgcn_readlane(v, 15)), uint32_t(__builtin_amdgcn_readlane(v, 31))),
+             max(uint32_t(__builtin_amdgcn_readlane(v, 47)), uint32_t(__builtin_amdgcn_readlane(v, 63))));
+}
+
+// number of set bits of m below this lane
+__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
 
 template <int NT>
 struct TkShared {
   static constexpr int NW = NT / kWave;
-  uint32_t hist[kBins];
-  uint64_t sel[DSA_MAX_SELECT_K];
-  uint64_t red[NW][2];
-  uint32_t cnt[NW];
-  uint64_t bound[2];
-  uint32_t bin_info[3];
-  uint32_t nsel;
+  alignas(16) uint32_t hist[kBins];
+  alignas(16) uint32_t sfx[kBins];  // first pass: keys in higher bins, per bin
+  uint64_t sel[DSA_MAX_SELECT_K + kRankCap];
+  uint32_t red[NW][4];
+  uint32_t tie[32 * NW];  // per (key slot, wave): tied keys, then their exclusive prefix
+  uint32_t info[4];
+  uint32_t slot;
 };
 
-// Number of valid keys and their max / min over the workgroup (one barrier;
+// Valid keys (hi != 0): their number, largest and smallest hi (one barrier;
 // the LDS slots are not rewritten before the caller's next barrier).
 template <int NT, int KPT>
-__device__ __forceinline__ uint32_t block_stats(const uint64_t (&key)[KPT], TkShared<NT>& sh, uint64_t& mx,
-                                                uint64_t& mn) {
+__device__ __forceinline__ void block_stats(const uint32_t (&hi)[KPT], TkShared<NT>& sh, uint32_t& n,
+                                            uint32_t& mx, uint32_t& mn) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t c = 0;
-  mx = 0;
-  mn = ~uint64_t(0);
+  uint32_t c = 0, a = 0, b = 0;  // count, max hi, max ~hi (= ~min hi)
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (key[j] != 0) {
-      ++c;
-      mx = key[j] > mx ? key[j] : mx;
-      mn = key[j] < mn ? key[j] : mn;
-    }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    c += __shfl_xor(c, o, kWave);
-    const uint64_t a = __shfl_xor(mx, o, kWave), b = __shfl_xor(mn, o, kWave);
-    mx = a > mx ? a : mx;
-    mn = b < mn ? b : mn;
+  for (int j = 0; j < KPT; ++j) {
+    const bool v = hi[j] != 0;
+    c += v ? 1u : 0u;
+    a = max(a, hi[j]);
+    b = max(b, v ? ~hi[j] : 0u);
   }
+  c = __builtin_amdgcn_readlane(wave_incl_sum(c), 63);
+  a = wave_max_u32(a);
+  b = wave_max_u32(b);
   if (lane == 0) {
-    sh.cnt[wave] = c;
-    sh.red[wave][0] = mx;
-    sh.red[wave][1] = mn;
+    sh.red[wave][0] = c;
+    sh.red[wave][1] = a;
+    sh.red[wave][2] = b;
   }
   __syncthreads();
-  uint32_t tot = 0;
+  n = 0;
   mx = 0;
-  mn = ~uint64_t(0);
+  b = 0;
+#pragma unroll
   for (int w = 0; w < TkShared<NT>::NW; ++w) {
-    tot += sh.cnt[w];
-    mx = sh.red[w][0] > mx ? sh.red[w][0] : mx;
-    mn = sh.red[w][1] < mn ? sh.red[w][1] : mn;
+    n += sh.red[w][0];
+    mx = max(mx, sh.red[w][1]);
+    b = max(b, sh.red[w][2]);
   }
-  return tot;
+  mn = ~b;
 }
 
-// Returns (prefix, lo): the selected keys are exactly those != 0 with
-// (key >> lo) >= (prefix >> lo).  Requires n_valid > K; mx / mn are the largest
-// and smallest valid keys.
+// Wave 0: scans the histogram from the highest bin down and finds the bin where
+// the running count reaches need (need >= 1, and the histogram holds at least
+// need keys).  Writes (bin, keys in higher bins, keys in the bin) to sh.info
+// and clears the histogram for the next pass.
+// With SFX it also writes, for every bin, the number of keys in higher bins
+// to sh.sfx, and the largest count of a bin at or above the found one to
+// sh.info[3].
+template <int NT, bool SFX = false>
+__device__ __forceinline__ void scan_find(TkShared<NT>& sh, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  u32x4* hv = reinterpret_cast<u32x4*>(&sh.hist[32 * lane]);  // bins 32*lane .. 32*lane+31
+  u32x4 cv[8];
+  uint32_t tot = 0, lmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    cv[i] = hv[i];
+    tot += (cv[i][0] + cv[i][1]) + (cv[i][2] + cv[i][3]);
+    if (SFX) lmax = max(lmax, max(max(cv[i][0], cv[i][1]), max(cv[i][2], cv[i][3])));
+  }
+  const uint32_t incl = wave_incl_sum(tot);
+  const uint32_t above = __builtin_amdgcn_readlane(incl, 63) - incl;  // keys in higher lanes' bins
+  // lanes 0..L satisfy this (the count from the top is non-increasing in lane)
+  const uint64_t b = __ballot(above + tot >= need);
+  const int L = 63 - __builtin_clzll(b);
+  const uint32_t aboveL = __builtin_amdgcn_readlane(above, L);
+  // lane L's 32 bins, highest first, over lanes 0..31
+  const uint32_t x = lane < 32 ? sh.hist[32 * L + 31 - lane] : 0u;
+  const uint32_t xin = wave_incl_sum(x);
+  const uint64_t b2 = __ballot(aboveL + xin >= need);
+  const int i = __builtin_ctzll(b2);
+  const uint32_t xi = __builtin_amdgcn_readlane(x, i);
+  const uint32_t xin_i = __builtin_amdgcn_readlane(xin, i);
+  uint32_t maxc = 0;
+  if (SFX) {
+    u32x4* sv = reinterpret_cast<u32x4*>(&sh.sfx[32 * lane]);
+    uint32_t run = above;
+#pragma unroll
+    for (int k = 7; k >= 0; --k) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        o[e] = run;
+        run += cv[k][e];
+      }
+      sv[k] = o;
+    }
+    // lanes above L hold only bins above the found one; lanes 0..i hold lane
+    // L's bins down to the found one
+    maxc = wave_max_u32(max(lane > L ? lmax : 0u, lane <= i ? x : 0u));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) hv[k] = u32x4{0u, 0u, 0u, 0u};
+  if (lane == 0) {
+    sh.info[0] = uint32_t(32 * L + 31 - i);
+    sh.info[1] = aboveL + xin_i - xi;
+    sh.info[2] = xi;
+    sh.info[3] = maxc;
+  }
+}
+
+struct RadixResult {
+  uint32_t prefix;  // decided bits (bits >= lo)
+  int lo;           // lowest decided bit
+  uint32_t cnt;     // keys whose bits >= lo equal prefix's
+  uint32_t need;    // of those, how many are selected
+};
+
+// Radix select over the 32-bit values v[j] with bit j of vmask set.  Bits above
+// h are already decided (equal to prefix's for every key in vmask).  The
+// histogram is zero on entry and on return.  On return the selected keys are
+// those with (v >> lo) > (prefix >> lo), plus `need` of the cnt keys with
+// (v >> lo) == (prefix >> lo) (all of them when cnt == need).
 template <int NT, int KPT>
-__device__ void radix_select(const uint64_t (&key)[KPT], int K, TkShared<NT>& sh, uint64_t mx, uint64_t mn,
-                             uint64_t& prefix_out, int& lo_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // n_valid > K >= 1 and keys are distinct, so mx != mn
-  const int top = 63 - __clzll(mx ^ mn);      // highest differing bit
-  uint64_t prefix = (top == 63) ? 0 : (mx >> (top + 1)) << (top + 1);
-  uint32_t need = uint32_t(K);
-  int hi = top;
-  int lo = 0;
-  for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
-  __syncthreads();
+__device__ RadixResult radix_on(const uint32_t (&v)[KPT], uint32_t vmask, int h, uint32_t prefix,
+                                uint32_t need, TkShared<NT>& sh) {
   while (true) {
-    lo = hi >= kDig - 1 ? hi - (kDig - 1) : 0;
-    const int width = hi - lo + 1;
-    const uint64_t dmask = (uint64_t(1) << width) - 1;
+    const int lo = h >= kDig - 1 ? h - (kDig - 1) : 0;
+    const uint32_t hmask = h >= 31 ? 0u : (0xffffffffu << (h + 1));
+    const uint32_t want = prefix & hmask;
+    const uint32_t dmask = (2u << (h - lo)) - 1u;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint64_t k = key[j];
-      const bool match = k != 0 && (hi == 63 || (k >> (hi + 1)) == (prefix >> (hi + 1)));
-      if (match) atomicAdd(&sh.hist[uint32_t((k >> lo) & dmask)], 1u);
-    }
+    for (int j = 0; j < KPT; ++j)
+      if (((vmask >> j) & 1u) && (v[j] & hmask) == want) atomicAdd(&sh.hist[(v[j] >> lo) & dmask], 1u);
     __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 32*lane .. 32*lane+31 (read, then cleared for the next
-      // pass); suffix sums over bins (high to low)
-      u32x4* hv = reinterpret_cast<u32x4*>(&sh.hist[32 * lane]);
-      u32x4 cv[8];
-      uint32_t lane_tot = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        cv[i] = hv[i];
-        lane_tot += (cv[i][0] + cv[i][1]) + (cv[i][2] + cv[i][3]);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hv[i] = u32x4{0u, 0u, 0u, 0u};
-      uint32_t incl = lane_tot;  // sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(incl, o, kWave);
-        if (lane + o < 64) incl += v;
-      }
-      uint32_t above = incl - lane_tot;  // keys in bins of higher lanes
-      int found = -1;
-      uint32_t f_above = 0, f_cnt = 0;
-#pragma unroll
-      for (int i = 7; i >= 0; --i) {
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          if (found < 0 && above + cv[i][e] >= need) { found = 32 * lane + 4 * i + e; f_above = above; f_cnt = cv[i][e]; }
-          above += cv[i][e];
-        }
-      }
-      // exactly one lane holds the bin where the running count first reaches need
-      if (found >= 0 && f_above < need) {
-        sh.bin_info[0] = uint32_t(found);
-        sh.bin_info[1] = f_above;
-        sh.bin_info[2] = f_cnt;
-      }
-    }
+    if ((threadIdx.x >> 6) == 0) scan_find<NT>(sh, need);
     __syncthreads();
-    // bin_info is rewritten only after the next pass's barrier
-    const uint32_t d = sh.bin_info[0], above = sh.bin_info[1], cnt = sh.bin_info[2];
-    prefix |= uint64_t(d) << lo;
+    // sh.info is rewritten only after the next pass's first barrier
+    const uint32_t d = sh.info[0], above = sh.info[1], cnt = sh.info[2];
+    prefix = want | (d << lo);
     need -= above;
-    if (cnt == need || lo == 0) break;
-    hi = lo - 1;
+    if (cnt == need || lo == 0) return {prefix, lo, cnt, need};
+    h = lo - 1;
   }
-  prefix_out = prefix;
-  lo_out = lo;
-}
-
-// Exclusive prefix sum of one value per thread over the workgroup.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TkShared<NT>& sh, uint32_t& total) {
-  constexpr int NW = TkShared<NT>::NW;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) sh.cnt[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-  total = 0;
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t c = sh.cnt[w];
-    base += w < wave ? c : 0u;
-    total += c;
-  }
-  __syncthreads();
-  return base + incl - v;
 }
 
 // value of lane (lane ^ TJ) for TJ < 32: DPP for 1, 2, 4, 8 (quad permutes,
@@ -287,93 +324,238 @@ __device__ void bitonic_desc(TkShared<NT>& sh, int kp2) {
   }
 }
 
-// One workgroup: select the K largest keys of its KPT*NT keys and
-// either write them unsorted to the workspace (partial) or sort and write ids.
+// Tied keys (bit j of eqm) at the K-th score, taken in position order: key
+// slot j of thread t is position base + j*NT + t.  Returns the mask of the
+// first `need` of them (two barriers).
+template <int NT, int KPT>
+__device__ uint32_t tie_by_position(uint32_t eqm, uint32_t need, TkShared<NT>& sh) {
+  constexpr int NW = TkShared<NT>::NW;
+  constexpr int NE = KPT * NW;                       // (slot, wave) counters
+  constexpr int PER = (NE + kWave - 1) / kWave;      // counters per lane of wave 0
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t m = __ballot((eqm >> j) & 1u);
+    if (lane == 0) sh.tie[j * NW + wave] = uint32_t(__builtin_popcountll(m));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t c[PER], s = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = lane * PER + e;
+      c[e] = i < NE ? sh.tie[i] : 0u;
+      s += c[e];
+    }
+    uint32_t run = wave_incl_sum(s) - s;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = lane * PER + e;
+      if (i < NE) sh.tie[i] = run;
+      run += c[e];
+    }
+  }
+  __syncthreads();
+  uint32_t take = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t m = __ballot((eqm >> j) & 1u);  // recomputed: cheaper than holding KPT ranks
+    if (((eqm >> j) & 1u) && sh.tie[j * NW + wave] + lane_rank(m) < need) take |= 1u << j;
+  }
+  return take;
+}
+
+// One workgroup: select the K largest keys of its KPT*NT keys and either write
+// them unsorted to the workspace (partial) or sort them and write pool ids.
 template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
-                                                          const uint64_t* __restrict__ keys_in,
-                                                          int P, int chunk, int nsplit_in, int K,
-                                                          uint64_t* __restrict__ keys_out,
-                                                          int32_t* __restrict__ pool_ids) {
+                                                  const uint64_t* __restrict__ keys_in,
+                                                  int P, int chunk, int nsplit_in, int K,
+                                                  uint64_t* __restrict__ keys_out,
+                                                  int32_t* __restrict__ pool_ids) {
+  static_assert(KPT <= 32, "selection masks are 32-bit");
   __shared__ TkShared<NT> sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.y;
   const int c = blockIdx.x;
-  uint64_t key[KPT];
-  // all loads are issued before any is used (clamped, in-bounds addresses),
-  // so that they are in flight together
-  if (FROM_SCORES) {
-    const float* s = scores + size_t(row) * P;
-    const int base = c * chunk;
+  uint32_t hi[KPT];
+  uint32_t lo[FROM_SCORES ? 1 : KPT];
+  const int base = c * chunk;
+  // all loads are issued before any is used, so that they are in flight
+  // together; buffer loads past the chunk's end return 0
+  if constexpr (FROM_SCORES) {
     const int end = min(P, base + chunk);
+    const auto rs = make_rsrc(scores + size_t(row) * P + base, uint32_t(max(end - base, 0)) * 4u);
     float v[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int p = base + j * NT + tid;
-      v[j] = s[p < end ? p : P - 1];
-    }
+    for (int j = 0; j < KPT; ++j)
+      v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j * NT + tid) * 4, 0, 0));
+    // The range test is an AND with a mask the compiler cannot see through:
+    // as a select it becomes a branch per key, with the load sunk into it.
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int p = base + j * NT + tid;
-      key[j] = (p < end && v[j] != -INFINITY) ? make_key(v[j], uint32_t(p)) : 0;
+      uint32_t in = base + j * NT + tid < end ? 0xffffffffu : 0u;
+      asm volatile("" : "+v"(in));
+      hi[j] = score_key(v[j]) & in;
     }
   } else {
-    const uint64_t* src = keys_in + size_t(row) * nsplit_in * K;
     const int n = nsplit_in * K;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = j * NT + tid;
-      key[j] = src[i < n ? i : n - 1];
-    }
+    const auto rs = make_rsrc(keys_in + size_t(row) * n, uint32_t(n) * 8u);
+    u32x2 k[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (j * NT + tid >= n) key[j] = 0;
-  }
-  uint64_t kmax, kmin;
-  const uint32_t nvalid = block_stats<NT, KPT>(key, sh, kmax, kmin);  // one barrier
-  uint64_t prefix = 1;
-  int lo = 0;
-  if (nvalid > uint32_t(K)) radix_select<NT, KPT>(key, K, sh, kmax, kmin, prefix, lo);
-  const uint64_t thr = prefix >> lo;
-  uint32_t selmask = 0;  // bit j: key[j] is selected (KPT <= 32)
+      k[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (j * NT + tid) * 8, 0, 0));
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) selmask |= (key[j] != 0 && (key[j] >> lo) >= thr) ? (1u << j) : 0u;
-  uint32_t nsel = 0;
-  uint32_t at = block_excl_scan<NT>(uint32_t(__builtin_popcount(selmask)), sh, nsel);  // nsel = min(K, nvalid)
-  if (!FINAL) {
+    for (int j = 0; j < KPT; ++j) {
+      hi[j] = k[j][1];  // 0 for padding keys and past the end
+      lo[j] = k[j][0];
+    }
+  }
+  if (tid == 0) sh.slot = 0;
+  for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
+  uint32_t nvalid, kmax, kmin;
+  block_stats<NT, KPT>(hi, sh, nvalid, kmax, kmin);  // its barrier also publishes the cleared LDS
+  const uint32_t nsel = min(nvalid, uint32_t(K));
+
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) vmask |= hi[j] != 0 ? (1u << j) : 0u;
+  // the 64-bit key of slot j
+  auto key_of = [&](int j) -> uint64_t {
+    const uint32_t l = FROM_SCORES ? 0xffffffffu - uint32_t(base + j * NT + tid) : lo[FROM_SCORES ? 0 : j];
+    return (uint64_t(hi[j]) << 32) | l;
+  };
+  uint32_t selmask = vmask;
+  if (nvalid > uint32_t(K)) {
+    RadixResult st;
+    if (kmax == kmin) {
+      st = {kmax, 0, nvalid, uint32_t(K)};  // every candidate has the same score
+    } else {
+      // First pass: 2048 bins of equal width in score between the smallest
+      // and the largest candidate (fp32 subtraction and scaling are monotone,
+      // so bins keep the key order, ties included).  It also leaves, per bin,
+      // the number of keys in higher bins.
+      const float fmn = key_float(kmin);
+      const float scale = float(kBins) / (key_float(kmax) - fmn);  // 0 if the range overflows
+      auto bin_of = [&](uint32_t k) -> uint32_t {
+        return min(uint32_t((key_float(k) - fmn) * scale), uint32_t(kBins - 1));
+      };
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if ((vmask >> j) & 1u) atomicAdd(&sh.hist[bin_of(hi[j])], 1u);
+      __syncthreads();
+      if ((tid >> 6) == 0) scan_find<NT, true>(sh, uint32_t(K));
+      __syncthreads();
+      const uint32_t t = sh.info[0], above = sh.info[1], cnt = sh.info[2], maxc = sh.info[3];
+      if (maxc <= uint32_t(kRankCap)) {
+        // Every bin from the K-th key's bin up holds at most kRankCap keys:
+        // output position = keys in higher bins + rank inside the own bin.
+        // Keys are gathered per bin in LDS (the cleared histogram counts the
+        // slots), then ranked against their bin mates.
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t d = bin_of(hi[j]);
+          if (((vmask >> j) & 1u) && d >= t) sh.sel[sh.sfx[d] + atomicAdd(&sh.hist[d], 1u)] = key_of(j);
+        }
+        __syncthreads();
+        // slots [0, above + cnt) now hold the keys of those bins, bin by bin;
+        // one thread per slot ranks its key (bin mates read four at a time)
+        uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * gridDim.x + c) * K;
+        int32_t* dst = FINAL ? pool_ids + size_t(row) * K : nullptr;
+        for (uint32_t sl = tid; sl < above + cnt; sl += NT) {
+          const uint64_t me = sh.sel[sl];
+          const uint32_t d = bin_of(uint32_t(me >> 32));
+          const uint32_t r0 = sh.sfx[d], n = sh.hist[d];
+          uint32_t pos = r0;
+          for (uint32_t i = 0; i < n; i += 4) {
+            const uint64_t a0 = sh.sel[r0 + i];
+            const uint64_t a1 = sh.sel[r0 + min(i + 1, n - 1)];
+            const uint64_t a2 = sh.sel[r0 + min(i + 2, n - 1)];
+            const uint64_t a3 = sh.sel[r0 + min(i + 3, n - 1)];
+            pos += (a0 > me ? 1u : 0u) + (i + 1 < n && a1 > me ? 1u : 0u) + (i + 2 < n && a2 > me ? 1u : 0u) +
+                   (i + 3 < n && a3 > me ? 1u : 0u);
+          }
+          if (pos < uint32_t(K)) {
+            if constexpr (FINAL) dst[pos] = int32_t(0xffffffffu - uint32_t(me));
+            else out[pos] = me;
+          }
+        }
+        return;
+      }
+      // a bin at or above the K-th key's is large (ties, or scores spread
+      // over many orders of magnitude): radix select on the key bits below
+      // those common to every candidate (the histogram is clear again)
+      const int top = 31 - __builtin_clz(kmax ^ kmin);
+      const uint32_t pre = top >= 31 ? 0u : (kmax & (0xffffffffu << (top + 1)));
+      st = radix_on<NT, KPT>(hi, vmask, top, pre, uint32_t(K), sh);
+    }
+    const uint32_t thr = st.prefix >> st.lo;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      gt |= ((vmask >> j) & 1u) && (hi[j] >> st.lo) > thr ? (1u << j) : 0u;
+      eq |= ((vmask >> j) & 1u) && (hi[j] >> st.lo) == thr ? (1u << j) : 0u;
+    }
+    if (st.cnt == st.need) {
+      selmask = gt | eq;
+    } else if constexpr (FROM_SCORES) {
+      // the K-th score is tied: smaller positions first
+      selmask = gt | tie_by_position<NT, KPT>(eq, st.need, sh);
+    } else {
+      // the K-th score is tied: radix select on lo among the tied keys.  lo =
+      // ~index with index < P, so the bits above P-1's top bit are all ones.
+      const int h2 = P > 1 ? 31 - __builtin_clz(uint32_t(P - 1)) : 0;
+      const uint32_t pre2 = h2 >= 31 ? 0u : (0xffffffffu << (h2 + 1));
+      const RadixResult s2 = radix_on<NT, KPT>(lo, eq, h2, pre2, st.need, sh);
+      const uint32_t thr2 = s2.prefix >> s2.lo;
+      uint32_t take = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) take |= ((eq >> j) & 1u) && (lo[j] >> s2.lo) >= thr2 ? (1u << j) : 0u;
+      selmask = gt | take;
+    }
+  }
+
+  // output slots: a DPP scan of the per-thread counts and one LDS atomic per wave
+  const uint32_t mine = uint32_t(__builtin_popcount(selmask));
+  const uint32_t incl = wave_incl_sum(mine);
+  uint32_t wbase = 0;
+  if (lane == 63) wbase = atomicAdd(&sh.slot, incl);
+  uint32_t at = __builtin_amdgcn_readlane(wbase, 63) + incl - mine;
+
+  if constexpr (!FINAL) {
     uint64_t* out = keys_out + (size_t(row) * gridDim.x + c) * K;
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if ((selmask >> j) & 1u) out[at++] = key[j];
+      if ((selmask >> j) & 1u) out[at++] = key_of(j);
     for (int i = int(nsel) + tid; i < K; i += NT) out[i] = 0;
     return;
-  }
-  int kp2 = 1;
-  while (kp2 < K) kp2 <<= 1;
-  if (kp2 < 512) kp2 = 512;
-  for (int i = tid; i < kp2; i += NT) sh.sel[i] = 0;
-  __syncthreads();
+  } else {
+    int kp2 = 1;
+    while (kp2 < K) kp2 <<= 1;
+    if (kp2 < 512) kp2 = 512;
+    for (int i = int(nsel) + tid; i < kp2; i += NT) sh.sel[i] = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if ((selmask >> j) & 1u) sh.sel[at++] = key[j];
-  __syncthreads();
-  int32_t* dst = pool_ids + size_t(row) * K;
-  if (kp2 == 512) {
-    uint64_t a0 = 0, a1 = 0;
-    if (tid < 256) { a0 = sh.sel[2 * tid]; a1 = sh.sel[2 * tid + 1]; }
+    for (int j = 0; j < KPT; ++j)
+      if ((selmask >> j) & 1u) sh.sel[at++] = key_of(j);
     __syncthreads();
-    sort512_desc<NT>(a0, a1, sh);
-    if (tid < 256) {
-      const int e0 = 2 * tid, e1 = 2 * tid + 1;
-      if (e0 < K) dst[e0] = (e0 < int(nsel) && a0 != 0) ? int32_t(0xffffffffu - uint32_t(a0)) : -1;
-      if (e1 < K) dst[e1] = (e1 < int(nsel) && a1 != 0) ? int32_t(0xffffffffu - uint32_t(a1)) : -1;
+    int32_t* dst = pool_ids + size_t(row) * K;
+    if (kp2 == 512) {
+      uint64_t a0 = 0, a1 = 0;
+      if (tid < 256) { a0 = sh.sel[2 * tid]; a1 = sh.sel[2 * tid + 1]; }
+      __syncthreads();
+      sort512_desc<NT>(a0, a1, sh);
+      if (tid < 256) {
+        const int e0 = 2 * tid, e1 = 2 * tid + 1;
+        if (e0 < K) dst[e0] = (e0 < int(nsel) && a0 != 0) ? int32_t(0xffffffffu - uint32_t(a0)) : -1;
+        if (e1 < K) dst[e1] = (e1 < int(nsel) && a1 != 0) ? int32_t(0xffffffffu - uint32_t(a1)) : -1;
+      }
+      return;
     }
-    return;
-  }
-  bitonic_desc<NT>(sh, kp2);
-  for (int i = tid; i < K; i += NT) {
-    const uint64_t k = sh.sel[i];
-    dst[i] = (i < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
+    bitonic_desc<NT>(sh, kp2);
+    for (int i = tid; i < K; i += NT) {
+      const uint64_t k = sh.sel[i];
+      dst[i] = (i < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
+    }
   }
 }
 
@@ -390,10 +572,10 @@ static int pow2_at_least(long v) {
   return p;
 }
 
-// threads and keys per thread for n keys: 256 threads while that needs at most
-// 32 keys each, else 1024 threads
+// threads and keys per thread for n keys: 256 threads for up to 2K keys, 512
+// up to 4K, else 1024 (more waves shorten each pass's instruction stream)
 static void tk_shape(long n, int& nt, int& kpt) {
-  nt = n <= 256L * 32 ? 256 : 1024;
+  nt = n <= 2048 ? 256 : (n <= 4096 ? 512 : 1024);
   kpt = pow2_at_least((n + nt - 1) / nt);
 }
 
@@ -433,6 +615,18 @@ static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, co
 #undef DSA_TK
 }
 
+template <bool FROM_SCORES, bool FINAL>
+static void launch_tk_nt(int nt, int kpt, dim3 grid, hipStream_t s, const float* scores,
+                         const uint64_t* keys_in, int P, int chunk, int nsplit_in, int K,
+                         uint64_t* keys_out, int32_t* pool_ids) {
+  if (nt == 256)
+    launch_tk<256, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+  else if (nt == 512)
+    launch_tk<512, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+  else
+    launch_tk<1024, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+}
+
 }  // namespace dsa
 
 using namespace dsa;
@@ -458,16 +652,13 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
   uint64_t* ws = static_cast<uint64_t*>(workspace);
   dim3 g1(pl.nsplit, Q);
   if (pl.nsplit == 1) {
-    if (pl.nt1 == 256) launch_tk<256, true, true>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
-    else launch_tk<1024, true, true>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
+    launch_tk_nt<true, true>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
     return launch_status();
   }
-  if (pl.nt1 == 256) launch_tk<256, true, false>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
-  else launch_tk<1024, true, false>(pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
+  launch_tk_nt<true, false>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
   int st = launch_status();
   if (st) return st;
   dim3 g2(1, Q);
-  if (pl.nt2 == 256) launch_tk<256, false, true>(pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
-  else launch_tk<1024, false, true>(pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
+  launch_tk_nt<false, true>(pl.nt2, pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
   return launch_status();
 }
