@@ -13,7 +13,9 @@ the 256 MB last-level cache cannot serve a step from the previous one.  Each
 step launches the four stages from argument tuples bound once per replica
 (``--mode graph`` replays HIP graphs captured per replica instead); HIP events
 on the launch stream bracket the score kernel of every timed step, which gives
-that kernel's per-launch time for the roofline line.  The roofline's traffic
+that kernel's per-launch time for the roofline line.  They are timing-only
+events (no system-scope fence at record), so that measuring does not add cache
+flushes to the step.  The roofline's traffic
 figure comes from the committed counter summary of the same kernel source.
 
 Prints ONE JSON line.
@@ -33,6 +35,55 @@ sys.path.insert(0, ROOT)
 METRIC = "DSA decode steps/s (indexer+top-k+sparse MLA) @262K ctx; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 REPLICAS = 8
+
+
+class TimingEvents:
+    """HIP events for timing only, created through the HIP runtime that torch
+    uses, with hipEventDisableSystemFence: recording them performs no
+    system-scope cache writeback and invalidation (HIP's documented flag for
+    events that only measure time), so they neither pad the measured launch
+    nor slow the work that follows."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, n: int):
+        import ctypes
+        self._c = ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            st = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS)
+            if st != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+            self.ev.append(e)
+
+    def record(self, i: int, stream_handle: int) -> None:
+        self.hip.hipEventRecord(self.ev[i], stream_handle)
+
+    def elapsed_us(self, i: int, j: int) -> float:
+        ms = self._c.c_float()
+        st = self.hip.hipEventElapsedTime(self._c.byref(ms), self.ev[i], self.ev[j])
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value * 1e3
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def _parse():
@@ -180,19 +231,23 @@ def main() -> int:
             run_rest(i % REPLICAS)
         stream.synchronize()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        tev = TimingEvents(2 * args.steps)
+        sh = stream.cuda_stream
         t0 = time.perf_counter()
         for i in range(args.steps):
             j = i % REPLICAS
-            ev[i][0].record(stream)
+            tev.record(2 * i, sh)
             run_scores(j)
-            ev[i][1].record(stream)
+            tev.record(2 * i + 1, sh)
             run_rest(j)
+        t_issued = time.perf_counter()
         stream.synchronize()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    score_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    host_issue_us = (t_issued - t0) * 1e6 / args.steps  # host time to enqueue one step
+    score_us = [tev.elapsed_us(2 * i, 2 * i + 1) for i in range(args.steps)]
+    tev.close()
     score_us_mean = float(np.mean(score_us))
 
     # per-stage breakdown (separate instrumented pass, eager launches, events around each stage)
@@ -202,14 +257,15 @@ def main() -> int:
         for i in range(min(64, args.steps)):
             b = bound[i % REPLICAS]
             calls = [b["scores"]] + b["rest"]
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-            e[0].record(stream)
+            e = TimingEvents(5)
+            e.record(0, stream.cuda_stream)
             for k, c in enumerate(calls):
                 c()
-                e[k + 1].record(stream)
+                e.record(k + 1, stream.cuda_stream)
             stream.synchronize()
             for k, n in enumerate(stage_names):
-                stage_t[n].append(e[k].elapsed_time(e[k + 1]) * 1e3)
+                stage_t[n].append(e.elapsed_us(k, k + 1))
+            e.close()
     stages_us = {n: round(float(np.median(v)), 2) for n, v in stage_t.items()}
 
     bytes_per_launch = score_bytes_per_pool() * Q * P + q.numel() * 2 + w.numel() * 4 + 2 * 128 * 4
@@ -240,6 +296,7 @@ def main() -> int:
                    "replicas": REPLICAS},
         "tokens_per_s": round(steps_per_s * Q, 1),
         "stages_us": stages_us,
+        "host_issue_us_per_step": round(host_issue_us, 2),
         "roofline": {"bound": "hbm", "kernel": "index_scores_ring", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "launch_us": round(score_us_mean, 3),

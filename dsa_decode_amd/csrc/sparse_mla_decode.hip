@@ -9,21 +9,23 @@
 //
 // MFMA path (bf16, Dl = 512, Hm a multiple of 16).  A workgroup handles one
 // row, one group of 16 heads and a contiguous slice ("split") of 64 ids of the
-// row's list.  Its 4 waves each own a quarter of the latent width (128 of the
-// 512 channels):
-//   - the split's 64 latent rows are gathered into LDS (16-byte loads);
-//   - each wave forms partial logits S^T[token, head] = kv . q^T over its
-//     quarter on the matrix cores; the four partials are summed through LDS;
-//   - every wave takes the (same) softmax over the 64 ids and accumulates its
-//     quarter of O^T[dl, head] = kv^T . P^T on the matrix cores.
-// The row-major LDS copy serves both contractions: 16-byte reads for the
-// logits and eight 16-bit reads per lane for kv^T; the row swizzle makes both
-// bank-conflict free.  80 KiB of LDS and <= 256 registers per lane keep two
-// workgroups per CU.  The head groups of one (row, split) read the same latent
-// rows; their workgroup ids are spaced by a multiple of 8 so that they share an
-// XCD and its L2.  Splits write normalised partial outputs, rounded to bf16 (in
-// the lanes' order: 512 B per store instruction), and their fp32 log-sum-exp;
-// a combine launch merges them in fp32.  The gather is the HBM traffic (1 KiB per selected token).
+// row's list, with 4 waves:
+//   - wave w gathers the latent rows of ids 16w .. 16w+15 straight into LDS
+//     (one 1 KiB row per load instruction, 16 bytes per lane; the row swizzle
+//     is applied through the source addresses);
+//   - it forms the logits of those 16 tokens for the 16 heads over the full
+//     latent width on the matrix cores (kv rows x q^T), so no partial logits
+//     cross waves: only the per-head max and sum do, through LDS;
+//   - the probabilities P (bf16) are shared through LDS, and wave w
+//     accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over all 64
+//     tokens, reading kv^T with the transposing LDS reads.
+// The swizzle makes both LDS read patterns bank-conflict free.  68 KiB of LDS
+// keeps two workgroups per CU.  The head groups of one (row, split) read the
+// same latent rows; their workgroup ids are spaced by a multiple of 8 so that
+// they share an XCD and its L2.  Splits write normalised partial outputs,
+// rounded to bf16 (in the lanes' order: 512 B per store instruction), and
+// their fp32 log-sum-exp; a combine launch merges them in fp32.  The gather is
+// the HBM traffic (1 KiB per selected token).
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -34,22 +36,24 @@ constexpr int kMlaSplit = 64;   // ids per workgroup
 constexpr int kMlaThreads = 256;
 
 struct MlaShared {
-  uint16_t rows[kMlaSplit][kMlaDl];  // 16-byte pieces swizzled per row (64 KiB)
-  union {
-    int ids[kMlaSplit];              // during the gather
-    f32x4 lg[4][4][64];              // partial logits [wave][block][lane] (16 KiB)
-  } u;
+  uint16_t rows[kMlaSplit][kMlaDl];  // latent rows, 16-byte pieces swizzled per row (64 KiB)
+  uint16_t p[16][kMlaSplit];         // probabilities P[head][token], bf16
+  float red[2][16][16];              // per head: [max | sum][head][wave * 4 + lane group]
 };
 
-// piece c of token row t sits at piece (c ^ row_swz(t)).  The 16 rows of one
-// logits read (t = 8a + 4b + j, a, j < 4) and the 4 row groups of one kv^T
-// read (t = 8kg + e) both land on distinct banks.
-__device__ __forceinline__ int row_swz(int t) { return (t & 3) | ((t >> 1) & 12); }
+// Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Makes the
+// logits reads (16 consecutive rows x 4 pieces) and the transposing reads
+// (rows 8g + e, g, e < 4, x 2 adjacent pieces) bank-conflict free.
+__device__ __forceinline__ int mla_swz(int t) { return (t & 11) | ((((t >> 2) ^ (t >> 4)) & 1) << 2); }
 
-// token held by row m of logits block mb: lane group kg of block pair
-// (2ks, 2ks+1) receives tokens 32ks + 8kg .. 32ks + 8kg + 7
-__device__ __forceinline__ int blk_token(int mb, int m) {
-  return 32 * (mb >> 1) + 8 * (m >> 2) + 4 * (mb & 1) + (m & 3);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read: within each group of 16 lanes, lane i receives element
+// (i & 3) of the 4 16-bit elements read by lanes 4e + (i >> 2), e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // offset (in elements) of partial-output element (head group hg, lane, dl) of a
@@ -64,7 +68,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     int T_max, int W, int nsplit, int ns8, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ MlaShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, dq = tid >> 6;  // wave = latent quarter
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
   const int HG = Hm >> 4;
   const int hg = blockIdx.x / ns8, sp = blockIdx.x % ns8;
@@ -74,121 +79,116 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int b = row_seq[r];
   const bool bok = b >= 0 && b < B;
   const size_t seq_base = size_t(bok ? b : 0) * T_max;
-  const int c_begin = sp * kMlaSplit;
 
-  if (tid < kMlaSplit) {
-    const int c = c_begin + tid;
-    int id = -1;
+  // ids of this wave's 16 tokens (lanes 0..15), -1 when absent or out of range
+  int myid = -1;
+  if (lane < 16) {
+    const int c = sp * kMlaSplit + 16 * w + lane;
     if (c < W) {
-      id = token_ids[size_t(r) * W + c];
-      if (!bok || id < 0 || id >= T_max) id = -1;
+      const int id = token_ids[size_t(r) * W + c];
+      myid = (bok && id >= 0 && id < T_max) ? id : -1;
     }
-    sh.u.ids[tid] = id;
   }
-  // q_lat of head h, latent quarter dq, as the B operand of the logits
-  bf16x8 qop[4];
+  // q_lat of head h as the B operand of the logits: k-step k covers latent
+  // channels 32k .. 32k+31, lane group kg holds channels 32k + 8kg .. +7
+  bf16x8 qop[16];
   {
-    const uint16_t* qs = q_lat + (size_t(r) * Hm + h) * kMlaDl + dq * 128;
+    const uint16_t* qs = q_lat + (size_t(r) * Hm + h) * kMlaDl + 8 * kg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qop[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + (kg + 4 * i) * 8));
+    for (int k = 0; k < 16; ++k) qop[k] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + 32 * k));
   }
-  __syncthreads();
-  // validity of this lane's 16 logits (tokens 32ks + 8kg + e), read before the
-  // id array is reused for the logits exchange
+  // gather: one row per instruction, lane i fills piece position i with piece
+  // i ^ swz of the token's row; absent ids give a zero row
   uint32_t vmask = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) vmask |= (sh.u.ids[32 * (e >> 3) + 8 * kg + (e & 7)] >= 0 ? 1u : 0u) << e;
-  {
-    // gather: piece k of this thread is row (tid >> 6) + 4k, 16-byte piece tid & 63
-    u32x4 gv[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int id = sh.u.ids[(tid >> 6) + 4 * k];
-      gv[k] = *reinterpret_cast<const u32x4*>(kv + (seq_base + (id >= 0 ? id : 0)) * kMlaDl + (tid & 63) * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int t = (tid >> 6) + 4 * k, c = tid & 63;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(&sh.rows[t][(c ^ row_swz(t)) * 8]) = sh.u.ids[t] >= 0 ? gv[k] : z;
+  for (int i = 0; i < 16; ++i) {
+    const int id = __builtin_amdgcn_readlane(myid, i);
+    const int t = 16 * w + i;
+    if (id >= 0) {
+      vmask |= 1u << i;
+      const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[t][0]), 16, 0, 0);
+    } else {
+      *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows are in LDS
 
-  // partial logits over this wave's latent quarter
+  // logits of tokens 16w + 4kg + j (j < 4) for head ln, full latent width;
+  // two accumulators shorten the MFMA dependency chain
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  {
+    const int t = 16 * w + ln, sw = mla_swz(t);
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int t = blk_token(mb, ln);
-    const int sw = row_swz(t);
-    bf16x8 a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((dq * 16 + kg + 4 * i) ^ sw) * 8]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = mfma16x16x32(a[i], qop[i], acc);
-    sh.u.lg[dq][mb][lane] = acc;
+    for (int k = 0; k < 16; k += 2) {
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + kg) ^ sw) * 8]));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + 4 + kg) ^ sw) * 8]));
+      acc0 = mfma16x16x32(a0, qop[k], acc0);
+      acc1 = mfma16x16x32(a1, qop[k + 1], acc1);
+    }
   }
-  __syncthreads();
-  // lane (kg, ln): head h, logits of tokens 32ks + 8kg + e at x[8ks + e]
-  float x[16];
+  float x[4];
   float m = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const f32x4 s0 = sh.u.lg[0][mb][lane], s1 = sh.u.lg[1][mb][lane];
-    const f32x4 s2 = sh.u.lg[2][mb][lane], s3 = sh.u.lg[3][mb][lane];
+  for (int j = 0; j < 4; ++j) {
+    x[j] = (vmask >> (4 * kg + j)) & 1u ? (acc0[j] + acc1[j]) * scale_log2 : -INFINITY;
+    m = fmaxf(m, x[j]);
+  }
+  sh.red[0][ln][4 * w + kg] = m;
+  __syncthreads();  // maxima published; every wave's rows are in LDS
+  {
+    const f32x4* rm = reinterpret_cast<const f32x4*>(&sh.red[0][ln][0]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 8 * (mb >> 1) + 4 * (mb & 1) + j;
-      const float v = ((s0[j] + s1[j]) + (s2[j] + s3[j])) * scale_log2;
-      x[e] = (vmask >> e) & 1u ? v : -INFINITY;
-      m = fmaxf(m, x[e]);
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = rm[i];
+      m = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
     }
   }
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
   const float m_use = m == -INFINITY ? 0.f : m;
-  float l = 0.f;
-  uint32_t pk[2][4];
+  float p[4], l = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[8 * ks + e] - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(x[8 * ks + e + 1] - m_use);
-      l += p0 + p1;
-      pk[ks][e >> 1] = pack2bf(p0, p1);
-    }
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  const bf16x8 pb0 = as_bf16x8(u32x4{pk[0][0], pk[0][1], pk[0][2], pk[0][3]});
-  const bf16x8 pb1 = as_bf16x8(u32x4{pk[1][0], pk[1][1], pk[1][2], pk[1][3]});
+  for (int j = 0; j < 4; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
+    l += p[j];
+  }
+  sh.red[1][ln][4 * w + kg] = l;
+  *reinterpret_cast<u32x2*>(&sh.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+  __syncthreads();  // P and the sums published
 
-  // O^T[dl, head] = kv^T[dl, tokens] . P^T[tokens, head] over this quarter
+  // O^T[dl, head] over latent quarter w: A = kv^T (16 dl x 32 tokens) from two
+  // transposing reads, B = P^T (32 tokens x 16 heads)
+  const bf16x8 pb0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[ln][8 * kg]));
+  const bf16x8 pb1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[ln][32 + 8 * kg]));
   f32x4 o[8];
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
-    const int d = dq * 128 + blk * 16 + ln;
-    const int c = d >> 3, off = d & 7;
-    uint32_t wv[2][4];
+    const int col = 128 * w + 16 * blk + 4 * (ln & 3);
+    const int pc = col >> 3, off = col & 7;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
+      const u32x2 lo = lds_read_tr16(&sh.rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
+      const u32x2 hi = lds_read_tr16(&sh.rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
+      a = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), ks ? pb1 : pb0, a);
+    }
+    o[blk] = a;
+  }
+  {
+    const f32x4* rs = reinterpret_cast<const f32x4*>(&sh.red[1][ln][0]);
+    l = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int t0 = 32 * ks + 8 * kg + e, t1 = t0 + 1;
-        const uint32_t lo = sh.rows[t0][((c ^ row_swz(t0)) << 3) + off];
-        const uint32_t hi = sh.rows[t1][((c ^ row_swz(t1)) << 3) + off];
-        wv[ks][e >> 1] = lo | (hi << 16);
-      }
-    o[blk] = mfma16x16x32(as_bf16x8(u32x4{wv[0][0], wv[0][1], wv[0][2], wv[0][3]}), pb0, f32x4{0.f, 0.f, 0.f, 0.f});
-    o[blk] = mfma16x16x32(as_bf16x8(u32x4{wv[1][0], wv[1][1], wv[1][2], wv[1][3]}), pb1, o[blk]);
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = rs[i];
+      l += (v[0] + v[1]) + (v[2] + v[3]);
+    }
   }
 
-  // o[blk][j] = sum_t p_t kv[t][dl = 128 dq + 16 blk + 4 kg + j] for head h
+  // o[blk][j] = sum_t p_t kv[t][dl = 128 w + 16 blk + 4 kg + j] for head h
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   const float lse_v = l > 0.f ? (m_use + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
   if (nsplit == 1) {
-    uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + dq * 128 + 4 * kg;
+    uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       u32x2 pkd;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       pkd[1] = pack2bf(o[blk][2] * inv, o[blk][3] * inv);
       *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
     }
-    if (dq == 0 && kg == 0 && lse) lse[size_t(r) * Hm + h] = lse_v;
+    if (w == 0 && kg == 0 && lse) lse[size_t(r) * Hm + h] = lse_v;
   } else {
     const size_t rs = size_t(r) * nsplit + sp;
 #pragma unroll
@@ -204,63 +204,62 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       u32x2 pkd;
       pkd[0] = pack2bf(o[blk][0] * inv, o[blk][1] * inv);
       pkd[1] = pack2bf(o[blk][2] * inv, o[blk][3] * inv);
-      *reinterpret_cast<u32x2*>(part_o + part_off(rs, HG, hg, dq, blk, lane)) = pkd;
+      __builtin_nontemporal_store(pkd, reinterpret_cast<u32x2*>(part_o + part_off(rs, HG, hg, w, blk, lane)));
     }
-    if (dq == 0 && kg == 0) part_lse[rs * Hm + h] = lse_v;
+    if (w == 0 && kg == 0) part_lse[rs * Hm + h] = lse_v;
   }
 }
 
 // Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  One
-// workgroup per (row, head group, latent quarter); thread = (blk, lane) of
-// the partial layout, so every split's read is one contiguous 8 KiB block.
+// wave per (row, head group, latent quarter, 16-channel block): lane (kg, ln)
+// owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken 32 at
+// a time; within a batch every lane issues all its loads (the split weights
+// of its head and its slice of every split's partial: one contiguous 512-byte
+// block per split and wave) before using any, and batches are merged with a
+// running maximum.
 constexpr int kMaxSplit = 256;
-__global__ __launch_bounds__(512) void mla_combine(const uint16_t* __restrict__ part_o,
-                                                   const float* __restrict__ part_lse, int nsplit,
-                                                   int Hm, uint16_t* __restrict__ out,
-                                                   float* __restrict__ lse) {
-  __shared__ float wgt[kMaxSplit][16];
-  __shared__ float sM[16], sWs[16];
+constexpr int kCombineBatch = 32;
+__global__ __launch_bounds__(64) void mla_combine(const uint16_t* __restrict__ part_o,
+                                                  const float* __restrict__ part_lse, int nsplit,
+                                                  int Hm, uint16_t* __restrict__ out,
+                                                  float* __restrict__ lse) {
   const int HG = Hm >> 4;
-  const int hg = blockIdx.x >> 2, dq = blockIdx.x & 3, r = blockIdx.y;
-  const int tid = threadIdx.x, blk = tid >> 6, lane = tid & 63, kg = lane >> 4, ln = lane & 15;
-  // split weights per head of the group: thread (s, head) loads one lse; the
-  // max and the sum over splits run as LDS reductions per head
-  for (int u = tid; u < nsplit * 16; u += 512)
-    wgt[u >> 4][u & 15] = part_lse[(size_t(r) * nsplit + (u >> 4)) * Hm + hg * 16 + (u & 15)];
-  __syncthreads();
-  if (tid < 16) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wgt[s][tid]);
-    sM[tid] = M;
-  }
-  __syncthreads();
-  for (int u = tid; u < nsplit * 16; u += 512) {
-    const float M = sM[u & 15], l = wgt[u >> 4][u & 15];
-    wgt[u >> 4][u & 15] = (M == -INFINITY || l == -INFINITY) ? 0.f : __expf(l - M);
-  }
-  __syncthreads();
-  if (tid < 16) {
-    float ws = 0.f;
-    for (int s = 0; s < nsplit; ++s) ws += wgt[s][tid];
-    sWs[tid] = ws;
-  }
-  __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
-    const u32x2 pv = *reinterpret_cast<const u32x2*>(part_o + part_off(size_t(r) * nsplit + s, HG, hg, dq, blk, lane));
-    const f32x4 v = {__uint_as_float(pv[0] << 16), __uint_as_float(pv[0] & 0xffff0000u),
-                     __uint_as_float(pv[1] << 16), __uint_as_float(pv[1] & 0xffff0000u)};
-    acc += wgt[s][ln] * v;
-  }
-  const float ws = sWs[ln];
-  const float inv = ws > 0.f ? 1.0f / ws : 0.f;
+  const int blk = blockIdx.x & 7, dq = (blockIdx.x >> 3) & 3, hg = blockIdx.x >> 5, r = blockIdx.y;
+  const int lane = threadIdx.x, kg = lane >> 4, ln = lane & 15;
   const int h = hg * 16 + ln;
+  float M = -INFINITY, ws = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+    float ls[kCombineBatch];
+    u32x2 pv[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int sc = min(s0 + i, nsplit - 1);
+      ls[i] = part_lse[(size_t(r) * nsplit + sc) * Hm + h];
+      pv[i] = *reinterpret_cast<const u32x2*>(part_o + part_off(size_t(r) * nsplit + sc, HG, hg, dq, blk, lane));
+    }
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) Mn = s0 + i < nsplit ? fmaxf(Mn, ls[i]) : Mn;
+    const float keep = M == -INFINITY ? 0.f : __expf(M - Mn);  // rescale of the earlier batches
+    ws *= keep;
+    acc *= keep;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const float wgt = (s0 + i < nsplit && ls[i] != -INFINITY) ? __expf(ls[i] - Mn) : 0.f;
+      ws += wgt;
+      const f32x4 v = {__uint_as_float(pv[i][0] << 16), __uint_as_float(pv[i][0] & 0xffff0000u),
+                       __uint_as_float(pv[i][1] << 16), __uint_as_float(pv[i][1] & 0xffff0000u)};
+      acc += wgt * v;
+    }
+    M = Mn;
+  }
+  const float inv = ws > 0.f ? 1.0f / ws : 0.f;
   u32x2 pk;
   pk[0] = pack2bf(acc[0] * inv, acc[1] * inv);
   pk[1] = pack2bf(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<u32x2*>(out + (size_t(r) * Hm + h) * kMlaDl + dq * 128 + blk * 16 + 4 * kg) = pk;
-  if (dq == 0 && blk == 0 && kg == 0 && lse) lse[size_t(r) * Hm + h] = ws > 0.f ? sM[ln] + logf(ws) : -INFINITY;
+  if (dq == 0 && blk == 0 && kg == 0 && lse) lse[size_t(r) * Hm + h] = ws > 0.f ? M + logf(ws) : -INFINITY;
 }
 
 // Generic path (fp32 or bf16, any Dl <= 512, any Hm): one workgroup per
@@ -401,7 +400,7 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
                      scale_log2, (uint16_t*)out, lse, part_o, part_lse);
   int st = launch_status();
   if (st || pl.nsplit == 1) return st;
-  hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 4, Q), dim3(512), 0, s, part_o, part_lse, pl.nsplit,
+  hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, pl.nsplit,
                      Hm, (uint16_t*)out, lse);
   return launch_status();
 }
