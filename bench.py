@@ -320,7 +320,9 @@ def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    pc = dict(k_pool=comp["k_pool"].cpu(), pool_start=comp["pool_start"].cpu(), pool_valid=comp["pool_valid"].cpu())
+    from dsa_decode_amd.layout import untile_pool_cache
+    pc = dict(k_pool=untile_pool_cache(comp["k_pool"].cpu(), wl.P_max), pool_start=comp["pool_start"].cpu(),
+              pool_valid=comp["pool_valid"].cpu())
     rows_done = 0
     t0 = time.perf_counter()
     while True:

@@ -75,6 +75,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
 }
 
+// Pool-cache layout.  The pooled keys [B, P_max, D] are stored tile-interleaved:
+// pools are grouped in tiles of 16 (P_tiles = ceil(P_max / 16) per sequence),
+// and a tile stores its 16-byte pieces piece-major, so piece c of the tile's
+// 16 pools forms 256 contiguous bytes.  For bf16 keys with D = 128 a 16-pool
+// tile is 4 KiB and one wave-wide 16-byte load per lane covers pieces 4i ..
+// 4i+3 of all 16 pools (1 KiB contiguous), exactly the matrix-core operand
+// layout.  E = elements per piece.
+template <typename T>
+struct KpLayout {
+  static constexpr int E = 16 / int(sizeof(T));
+  static __host__ __device__ __forceinline__ size_t index(size_t b, int p, int ch, int P_tiles, int D) {
+    return (((b * P_tiles + (p >> 4)) * size_t(D / E) + ch / E) * 16 + (p & 15)) * E + ch % E;
+  }
+};
+__host__ __device__ __forceinline__ int pool_tiles(int P_max) { return (P_max + 15) >> 4; }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 r) { return __builtin_bit_cast(bf16x8, r); }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).  Lane l supplies row

@@ -17,12 +17,13 @@
 // key is never rounded.
 //
 // Lane l of a wave holds pool (l & 15) of a 16-pool tile and channels
-// 8*(kg + 4i) .. +8, kg = l >> 4, for k-step i (one 16-byte load each); the
-// MFMA output puts heads 4*kg + j (j < 4) of that pool in the lane.
+// 8*(kg + 4i) .. +8, kg = l >> 4, for k-step i (one 16-byte load each; in the
+// tile-interleaved pool cache the 64 lanes' loads of one k-step are 1 KiB of
+// contiguous memory); the MFMA output puts heads 4*kg + j (j < 4) of that pool
+// in the lane.
 //
-// Decode kernel: one row per grid row, pools split over grid.x; each wave
-// issues all its tiles' key loads at once, so the per-tile work overlaps their
-// arrival.  Prefill kernel: a workgroup
+// Decode kernel: one row per grid row, pools split over grid.x, each wave
+// streaming its tiles through a register ring.  Prefill kernel: a workgroup
 // keeps its pool tiles in registers and runs a group of rows of one sequence
 // over them (rows staged four at a time in LDS).
 //
@@ -174,154 +175,110 @@ __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], cons
   }
 }
 
-// Decode kernel: a workgroup owns 4*TW consecutive 16-pool tiles of one row
-// (wave w takes tiles w, w+4, ...).  All of a wave's key loads are issued at
-// the start, before the row's operands are staged, so the whole workgroup's
-// keys are in flight at once and the per-tile work overlaps their arrival.
-template <int NH, int TW>
-__global__ __launch_bounds__(kIsThreads) void index_scores_decode(
-    const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
-    const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
-    const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_pos, int B, int P_max, int kp, float* __restrict__ scores) {
-  constexpr int H = NH * 16;
-  __shared__ uint16_t ghi[H][kIsLd];
-  __shared__ uint16_t glo[H][kIsLd];
-  __shared__ float sQB[H], sW[H];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kg = lane >> 4, ln = lane & 15;
-  const int r = blockIdx.y;
-  const int b = row_seq[r];
-  const int pos = row_pos[r];
-  const bool ok = b >= 0 && b < B;
-  const int t_begin = blockIdx.x * (kIsWaves * TW);
-  float* srow = scores + size_t(r) * P_max;
-
-  // the row's q / gamma / beta / w loads first, then every key tile of this
-  // wave (out-of-range tiles read a valid dummy address and are not stored)
-  RowIn rin;
-  if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
-  u32x4 xb[TW][4];
-  int psb[TW], pvb[TW];
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    const int p = (t_begin + wave + kIsWaves * j) * 16 + ln;
-    const bool in = ok && p < P_max;
-    const size_t pi = in ? size_t(b) * P_max + p : 0;
-    const uint16_t* src = k_pool + pi * kIsD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xb[j][i] = *reinterpret_cast<const u32x4*>(src + (kg + 4 * i) * 8);
-    psb[j] = pool_start[pi];
-    pvb[j] = pool_valid[pi];
-  }
-  if (tid < H * 8) stage_row_store(rin, ghi, glo, sQB, sW, tid);
-  __syncthreads();
-  bf16x8 ahi[NH][4], alo[NH][4];
-  float cQ[NH][4], cW[NH][4];
-  load_operands<NH>(ghi, glo, sQB, sW, kg, ln, ahi, alo, cQ, cW);
-
-#pragma unroll
-  for (int j = 0; j < TW; ++j) {
-    const float sc = tile_score<NH>(xb[j], ahi, alo, cQ, cW, scale, eps, ln);
-    const int p = (t_begin + wave + kIsWaves * j) * 16 + ln;
-    if (kg == 0 && p < P_max) {
-      const bool cand = ok && pvb[j] != 0 && psb[j] + kp - 1 <= pos;
-      srow[p] = cand ? sc : -INFINITY;
-    }
-  }
-}
-
-// Streaming decode kernel: a workgroup owns kRingTiles consecutive 16-pool
-// tiles of one row; each wave runs through its tiles (w, w+4, ...) with a
-// 4-deep register ring (three tiles' key loads in flight while one is
-// computed).  Key rows are read with non-temporal loads (each byte is used
-// once).  The candidate test of the workgroup's pools is prepared in LDS up
-// front from coalesced loads of pool_start / pool_valid (one int per pool:
-// its first token if valid, else INT_MAX), and the workgroup's scores are
-// gathered in LDS and written with coalesced stores at the end.
-#ifndef DSA_IS_RING_TILES
-#define DSA_IS_RING_TILES 32
-#endif
-constexpr int kRing = 4;
-constexpr int kRingTiles = DSA_IS_RING_TILES;  // 16-pool tiles per workgroup
-constexpr int kRingPools = kRingTiles * 16;
+// Decode kernel.  A workgroup owns 4*NT consecutive 16-pool tiles of one row
+// (wave w takes tiles w, w+4, ...); each wave runs through its tiles with a
+// kStreamRing-deep register ring (the next tiles' key loads in flight while one
+// is computed).  In the tile-interleaved pool cache each of a tile's 4 key
+// loads per lane covers 1 KiB of contiguous memory and lands directly in the
+// matrix-core operand layout; keys are read non-temporally (each byte is used
+// once).  The row's folded LayerNorm operands are staged once in LDS (8
+// threads per head) while the first ring of keys is in flight.  The candidate
+// test of the workgroup's pools is prepared in LDS from coalesced loads of
+// pool_start / pool_valid (first token if valid, else INT_MAX), and the scores
+// are gathered in LDS and written with coalesced stores.
+constexpr int kStreamRing = 4;           // tiles in flight per wave
+constexpr int kTileElems = 16 * kIsD;    // 4 KiB of bf16 keys
 
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <int NH>
-__global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(3))) void index_scores_ring(
+template <int NH, int NT>
+__global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2))) void index_scores_stream(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
     const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int B, int P_max, int kp, float* __restrict__ scores) {
   constexpr int H = NH * 16;
+  constexpr int kPools = kIsWaves * NT * 16;  // pools per workgroup
+  constexpr int R = NT < kStreamRing ? NT : kStreamRing;
+  constexpr int MP = (kPools + kIsThreads - 1) / kIsThreads;  // metadata entries per thread
   __shared__ uint16_t ghi[H][kIsLd];
   __shared__ uint16_t glo[H][kIsLd];
   __shared__ float sQB[H], sW[H];
-  __shared__ int sStart[kRingPools];   // first token of a valid pool, INT_MAX otherwise
-  __shared__ float sOut[kRingPools];
+  __shared__ int sStart[kPools];  // first token of a valid pool, INT_MAX otherwise
+  __shared__ float sOut[kPools];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, ln = lane & 15;
   const int r = blockIdx.y;
   const int b = row_seq[r];
   const int pos = row_pos[r];
   const bool ok = b >= 0 && b < B;
-  const int p0 = blockIdx.x * kRingPools;       // first pool of the workgroup
-  constexpr int nt = kRingTiles / kIsWaves;     // tiles per wave
-  u32x4 xb[kRing][4];
-  auto issue = [&](int slot, int j) {
-    const int p = p0 + (wave + kIsWaves * j) * 16 + ln;
-    const bool in = ok && j < nt && p < P_max;
-    const uint16_t* src = k_pool + (in ? size_t(b) * P_max + p : 0) * kIsD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xb[slot][i] = ld_stream(src + (kg + 4 * i) * 8);
-  };
-  // operand / metadata loads first, then the first ring of key tiles
+  const int P_tiles = pool_tiles(P_max);
+  const int t0 = blockIdx.x * (kIsWaves * NT);  // first tile of the workgroup
+  const int p0 = t0 * 16;
+  const size_t seq0 = size_t(ok ? b : 0) * P_max;
+  const uint16_t* kseq = k_pool + size_t(ok ? b : 0) * P_tiles * kTileElems;
+
+  // operand and metadata loads first, then the first ring of key tiles
   RowIn rin;
   if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
-  int st[kRingPools / kIsThreads];
-  uint8_t vl[kRingPools / kIsThreads];
+  int st[MP];
+  uint8_t vl[MP];
 #pragma unroll
-  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
-    const int p = p0 + u * kIsThreads + tid;
-    const size_t pi = (ok && p < P_max) ? size_t(b) * P_max + p : 0;
+  for (int u = 0; u < MP; ++u) {
+    const int lp = u * kIsThreads + tid;
+    const int p = p0 + lp;
+    const size_t pi = (ok && p < P_max && lp < kPools) ? seq0 + p : 0;
     st[u] = pool_start[pi];
     vl[u] = pool_valid[pi];
   }
+  u32x4 xb[R][4];
+  auto issue = [&](int slot, int j) {
+    const int t = t0 + wave + kIsWaves * j;
+    const bool in = j < NT && t < P_tiles;
+    const uint16_t* src = kseq + size_t(in ? t : 0) * kTileElems + 8 * lane;
 #pragma unroll
-  for (int s = 0; s < kRing; ++s) issue(s, s);
+    for (int i = 0; i < 4; ++i) xb[slot][i] = ld_stream(src + 512 * i);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < R; ++s) issue(s, s);
+  // keep the key stream's first loads ahead of the operand arithmetic (the
+  // scheduler would otherwise sink them below it to save registers, and the
+  // whole grid would wait for its operands before any key is requested)
+  __builtin_amdgcn_sched_barrier(0);
   if (tid < H * 8) stage_row_store(rin, ghi, glo, sQB, sW, tid);
 #pragma unroll
-  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
-    const int p = p0 + u * kIsThreads + tid;
-    sStart[u * kIsThreads + tid] = (ok && p < P_max && vl[u] != 0) ? st[u] : INT_MAX;
+  for (int u = 0; u < MP; ++u) {
+    const int lp = u * kIsThreads + tid;
+    const int p = p0 + lp;
+    if (lp < kPools) sStart[lp] = (ok && p < P_max && vl[u] != 0) ? st[u] : INT_MAX;
   }
   __syncthreads();
   bf16x8 ahi[NH][4], alo[NH][4];
   float cQ[NH][4], cW[NH][4];
   load_operands<NH>(ghi, glo, sQB, sW, kg, ln, ahi, alo, cQ, cW);
-  const int last_ok = pos - (kp - 1);            // candidate iff its start <= last_ok
+  const int last_ok = pos - (kp - 1);  // candidate iff its start <= last_ok
 #pragma unroll
-  for (int j0 = 0; j0 < nt; j0 += kRing) {
+  for (int j0 = 0; j0 < NT; j0 += R) {
 #pragma unroll
-    for (int s = 0; s < kRing; ++s) {
+    for (int s = 0; s < R; ++s) {
       const int j = j0 + s;
       const float sc = tile_score<NH>(xb[s], ahi, alo, cQ, cW, scale, eps, ln);
-      const int lp = (wave + kIsWaves * j) * 16 + ln;   // pool within the workgroup
+      const int lp = (wave + kIsWaves * j) * 16 + ln;  // pool within the workgroup
       if (kg == 0) sOut[lp] = sStart[lp] <= last_ok ? sc : -INFINITY;
-      issue(s, j + kRing);
+      issue(s, j + R);
     }
   }
   __syncthreads();
   float* srow = scores + size_t(r) * P_max;
 #pragma unroll
-  for (int u = 0; u < kRingPools / kIsThreads; ++u) {
-    const int p = p0 + u * kIsThreads + tid;
-    if (p < P_max) srow[p] = sOut[u * kIsThreads + tid];
+  for (int u = 0; u < MP; ++u) {
+    const int lp = u * kIsThreads + tid;
+    const int p = p0 + lp;
+    if (lp < kPools && p < P_max) srow[p] = sOut[lp];
   }
 }
 
@@ -349,15 +306,18 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   int b_loaded = row_seq[r_begin];
   u32x4 xk[kTiles][4];
   int psk[kTiles], pvk[kTiles];
+  const int P_tiles = pool_tiles(P_max);
   auto load_keys = [&](int b) {
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const int p = p_wave + t * 16 + ln;
       const bool in = p < P_max && b >= 0 && b < B;
       const size_t pi = in ? size_t(b) * P_max + p : 0;
-      const uint16_t* src = k_pool + pi * kIsD;
+      const int tile = (p_wave >> 4) + t;
+      const size_t ti = (b >= 0 && b < B && tile < P_tiles) ? size_t(b) * P_tiles + tile : 0;
+      const uint16_t* src = k_pool + ti * (16 * kIsD) + 8 * lane;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + (kg + 4 * i) * 8);
+      for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + 512 * i);
       psk[t] = pool_start[pi];
       pvk[t] = pool_valid[pi];
     }
@@ -404,6 +364,20 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   }
 }
 
+// channels c .. c+7 of pool p from the pool cache (one 16-byte piece for
+// bf16, two for fp32)
+__device__ __forceinline__ void load_kp8(const uint16_t* k_pool, int b, int p, int c, int P_tiles, int D,
+                                         float (&v)[8]) {
+  load8(k_pool + KpLayout<uint16_t>::index(b, p, c, P_tiles, D), v);
+}
+__device__ __forceinline__ void load_kp8(const float* k_pool, int b, int p, int c, int P_tiles, int D,
+                                         float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(k_pool + KpLayout<float>::index(b, p, c, P_tiles, D));
+  const f32x4 z = *reinterpret_cast<const f32x4*>(k_pool + KpLayout<float>::index(b, p, c + 4, P_tiles, D));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = z[i]; }
+}
+
 // Generic path: any H <= 64, D in {32, 64, 128}, fp32 or bf16 activations.
 // One thread per pool; the normed key is formed explicitly in fp32 registers.
 template <typename T, int D>
@@ -427,11 +401,12 @@ __global__ __launch_bounds__(256) void index_scores_generic(
   if (b < 0 || b >= B) { *out = -INFINITY; return; }
   const size_t pi = size_t(b) * P_max + p;
   if (!(pool_valid[pi] != 0 && pool_start[pi] + kp - 1 <= pos)) { *out = -INFINITY; return; }
+  const int P_tiles = pool_tiles(P_max);
   float x[D];
 #pragma unroll
   for (int c = 0; c < D; c += 8) {
     float v[8];
-    load8(k_pool + pi * D + c, v);
+    load_kp8(k_pool, b, p, c, P_tiles, D, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[c + e] = v[e];
   }
@@ -457,13 +432,6 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 
 // Launch shapes of the MFMA path.
 // Decode launch shape (tuned on MI355X at 4 x 65536 pools)
-#ifndef DSA_IS_DECODE
-#define DSA_IS_DECODE 1  // 1: streaming ring kernel; 0: all loads up front, DSA_IS_TW tiles per wave
-#endif
-#ifndef DSA_IS_TW
-#define DSA_IS_TW 8
-#endif
-
 struct IsPlan {
   bool rows;  // false: decode kernel (one row per grid row)
   int tw;     // decode: tiles per wave
@@ -474,9 +442,12 @@ static IsPlan is_plan(int Q, int P_max) {
   IsPlan pl{false, 8, 1};
   const long ntile = (P_max + 15) / 16;
   if (Q <= 64) {
-    // decode: 8 tiles per wave (32 KiB of keys per wave in flight) when that
-    // still gives >= 512 workgroups, else 2
-    pl.tw = long(Q) * ((ntile + 4 * DSA_IS_TW - 1) / (4 * DSA_IS_TW)) >= 512 ? DSA_IS_TW : 2;
+    // decode: 16 tiles per wave (1024 pools per workgroup) while that gives
+    // >= 256 workgroups (one per CU: fewer key bytes in flight stream better
+    // than more), else 4 tiles, else 1
+    if (long(Q) * ((ntile + 63) / 64) >= 256) pl.tw = 16;
+    else if (long(Q) * ((ntile + 15) / 16) >= 128) pl.tw = 4;
+    else pl.tw = 1;
     return pl;
   }
   // many rows: groups of rows of one sequence share the keys held in registers
@@ -511,28 +482,21 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
   if (dtype == DSA_BF16 && D == 128 && (H == 16 || H == 32)) {
     const IsPlan pl = is_plan(Q, P_max);
     if (!pl.rows) {
-      const int ntile = (P_max + 15) / 16;
-      if (DSA_IS_DECODE == 1) {
-        dim3 grid(ceil_div(P_max, kRingPools), Q);
-        auto kr = H == 32 ? index_scores_ring<2> : index_scores_ring<1>;
-        hipLaunchKernelGGL(kr, grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, scale,
-                           (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,
-                           row_seq, row_pos, B, P_max, kpool, scores);
-        return launch_status();
-      }
-      dim3 grid(ceil_div(ntile, kIsWaves * pl.tw), Q);
-#define DSA_IS_DEC(NH, TW)                                                                            \
-  hipLaunchKernelGGL((index_scores_decode<NH, TW>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, \
+      dim3 grid(ceil_div(P_max, kIsWaves * pl.tw * 16), Q);
+#define DSA_IS_STREAM(NH, NT)                                                                       \
+  hipLaunchKernelGGL((index_scores_stream<NH, NT>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, \
                      scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,   \
                      row_seq, row_pos, B, P_max, kpool, scores)
       if (H == 32) {
-        if (pl.tw == DSA_IS_TW) DSA_IS_DEC(2, DSA_IS_TW);
-        else DSA_IS_DEC(2, 2);
+        if (pl.tw == 16) DSA_IS_STREAM(2, 16);
+        else if (pl.tw == 4) DSA_IS_STREAM(2, 4);
+        else DSA_IS_STREAM(2, 1);
       } else {
-        if (pl.tw == DSA_IS_TW) DSA_IS_DEC(1, DSA_IS_TW);
-        else DSA_IS_DEC(1, 2);
+        if (pl.tw == 16) DSA_IS_STREAM(1, 16);
+        else if (pl.tw == 4) DSA_IS_STREAM(1, 4);
+        else DSA_IS_STREAM(1, 1);
       }
-#undef DSA_IS_DEC
+#undef DSA_IS_STREAM
       return launch_status();
     }
     dim3 grid(ceil_div(P_max, kIsWaves * 4 * 16), ceil_div(Q, pl.rows_per_group));

@@ -8,7 +8,8 @@
 // thread per (pool, 8-channel group).  The pool kernel is HBM-bound: it reads
 // kpool token rows of k and gate (2 * kpool * 2 B per channel for bf16) and
 // writes one pooled row; the kpool <= 8 slot logits of each channel live in
-// registers.
+// registers.  The pooled keys go to the tile-interleaved pool-cache layout
+// (KpLayout); the padding pools of the last tile are written as zeros.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -51,6 +52,18 @@ __global__ __launch_bounds__(kAnchorThreads) void anchor_kernel(const uint8_t* _
   }
 }
 
+// 8 channels c0 .. c0+7 of pool p into the pool cache: one 16-byte piece for
+// bf16, two for fp32
+__device__ __forceinline__ void store_kp(uint16_t* k_pool, int b, int p, int c0, int P_tiles, int D,
+                                         const float (&v)[8]) {
+  store8(k_pool + KpLayout<uint16_t>::index(b, p, c0, P_tiles, D), v);
+}
+__device__ __forceinline__ void store_kp(float* k_pool, int b, int p, int c0, int P_tiles, int D,
+                                         const float (&v)[8]) {
+  *reinterpret_cast<f32x4*>(k_pool + KpLayout<float>::index(b, p, c0, P_tiles, D)) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(k_pool + KpLayout<float>::index(b, p, c0 + 4, P_tiles, D)) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // KP (the kpool) is a template argument so that all 2*KP row loads of a
 // thread are issued before the first is used.
 template <typename T, int KP>
@@ -61,18 +74,18 @@ __global__ __launch_bounds__(256) void pool_kernel(
     T* __restrict__ k_pool, int32_t* __restrict__ pool_start, uint8_t* __restrict__ pool_valid) {
   const int b = blockIdx.y;
   const int groups = D >> 3;
+  const int P_tiles = pool_tiles(P_max);
   const long gid = long(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gid >= long(P_max) * groups) return;
+  if (gid >= long(P_tiles) * 16 * groups) return;
   const int p = int(gid / groups);
   const int c0 = int(gid % groups) * 8;
   const int n = n_pools[b];
-  T* dst = k_pool + (size_t(b) * P_max + p) * D + c0;
   float acc[8];
   if (p >= n) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    store8(dst, acc);
-    if (c0 == 0) {
+    store_kp(k_pool, b, p, c0, P_tiles, D, acc);
+    if (c0 == 0 && p < P_max) {
       pool_start[size_t(b) * P_max + p] = -1;
       pool_valid[size_t(b) * P_max + p] = 0;
     }
@@ -113,7 +126,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
     }
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = acc[e] / den[e];
-  store8(dst, acc);
+  store_kp(k_pool, b, p, c0, P_tiles, D, acc);
   if (c0 == 0) {
     int all = 1;
 #pragma unroll
@@ -168,7 +181,7 @@ extern "C" int dsa_kpool_compress(const void* k, const void* gate, const uint8_t
                      kpool, n_pools, first_valid);
   int st = launch_status();
   if (st) return st;
-  const long work = long(P_max) * (D / 8);
+  const long work = long(pool_tiles(P_max)) * 16 * (D / 8);
   dim3 grid(ceil_div(work, 256), B);
   if (dtype == DSA_BF16)
     launch_pool<uint16_t>(kpool, grid, s, k, gate, valid, ape, T_max, D, P_max, n_pools, first_valid,

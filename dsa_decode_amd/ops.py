@@ -11,6 +11,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
+from .layout import pool_cache_pools
 from ._lib import DSA_BF16, DSA_F32, DsaError, check  # noqa: F401
 
 _ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
@@ -41,11 +42,12 @@ def _act_code(t: torch.Tensor) -> int:
 
 
 def dsa_kpool_compress(k, gate, valid, ape, seq_len, kpool: int, P_max: int, out=None):
-    """-> dict(k_pool [B,P_max,D], pool_start, pool_valid [B,P_max], n_pools, first_valid [B])."""
+    """-> dict(k_pool [B, pool_cache_pools(P_max), D] tile-interleaved, pool_start,
+    pool_valid [B,P_max], n_pools, first_valid [B])."""
     B, T_max, D = k.shape
     if out is None:
         dev = k.device
-        out = dict(k_pool=torch.empty((B, P_max, D), dtype=k.dtype, device=dev),
+        out = dict(k_pool=torch.empty((B, pool_cache_pools(P_max), D), dtype=k.dtype, device=dev),
                    pool_start=torch.empty((B, P_max), dtype=torch.int32, device=dev),
                    pool_valid=torch.empty((B, P_max), dtype=torch.uint8, device=dev),
                    n_pools=torch.empty((B,), dtype=torch.int32, device=dev),
@@ -63,11 +65,11 @@ def dsa_kpool_compress(k, gate, valid, ape, seq_len, kpool: int, P_max: int, out
 
 def dsa_index_scores(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamma, ln_beta,
                      ln_eps: float, row_seq, row_pos, kpool: int, scores=None):
-    """-> scores [Q, P_max] fp32 (-inf = not a candidate)."""
+    """-> scores [Q, P_max] fp32 (-inf = not a candidate); k_pool is the
+    tile-interleaved pool cache [B, pool_cache_pools(P_max), D]."""
     Q, H, D = q.shape
-    B, P_max, D2 = k_pool.shape
-    if D2 != D:
-        raise ValueError("q and k_pool disagree on D")
+    B, P_max = pool_start.shape
+    _check_pool_cache(k_pool, B, P_max, D)
     if scores is None:
         scores = torch.empty((Q, P_max), dtype=torch.float32, device=q.device)
     st = _lib.load().dsa_index_scores(
@@ -79,6 +81,12 @@ def dsa_index_scores(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamm
         _dev(scores, "scores", torch.float32), _stream())
     check("dsa_index_scores", st)
     return scores
+
+
+def _check_pool_cache(k_pool, B: int, P_max: int, D: int) -> None:
+    if tuple(k_pool.shape) != (B, pool_cache_pools(P_max), D):
+        raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected the pool cache "
+                         f"{(B, pool_cache_pools(P_max), D)}")
 
 
 def dsa_topk_workspace_bytes(Q: int, P: int, K: int) -> int:
@@ -167,7 +175,8 @@ class BoundCall:
 def bind_index_scores(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,
                       row_pos, kpool, scores) -> BoundCall:
     Q, H, D = q.shape
-    B, P_max, _ = k_pool.shape
+    B, P_max = pool_start.shape
+    _check_pool_cache(k_pool, B, P_max, D)
     return BoundCall("dsa_index_scores", (
         _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
         _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),

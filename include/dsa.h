@@ -54,6 +54,21 @@ extern "C" {
 #define DSA_F32   0
 #define DSA_BF16  1
 
+/*
+ * The pool cache.  dsa_kpool_compress writes the pooled keys k_pool[b,p,c]
+ * (b < B, p < P_max, c < D) tile-interleaved, and dsa_index_scores reads them
+ * in that layout: pools are grouped in tiles of 16 (P_tiles = ceil(P_max/16)
+ * tiles per sequence) and a tile stores the 16-byte pieces of its 16 pools
+ * piece-major.  With E = 16 / sizeof(act) elements per piece (8 for bf16, 4 for
+ * fp32), k_pool[b,p,c] sits at element
+ *     (((b*P_tiles + p/16) * (D/E) + c/E) * 16 + p%16) * E + c%E
+ * of a buffer of B * P_tiles * 16 * D elements (DSA_POOL_CACHE_POOLS(P_max)
+ * pools per sequence; the padding pools of the last tile are zeros).  For
+ * bf16 keys with D = 128 each wave-wide 16-byte load of the score kernel then
+ * reads 1 KiB of contiguous memory straight into the matrix-core operand layout.
+ */
+#define DSA_POOL_CACHE_POOLS(P_max) ((((P_max) + 15) / 16) * 16)
+
 /* Most pool slots (kpool) accepted.  The "Module glm5next_dsa" page, section
  * "Constants" (KERNEL_MAX_KPOOL), states that the reference compression kernel
  * holds at most 8 slots and silently truncates more; here a larger kpool is
@@ -84,13 +99,15 @@ int dsa_abi_version(void);
  *     a_s = softmax_s(gate[b,t_s,c] + ape[s,c]),  k_pool[b,p,c] = sum_s a_s k[b,t_s,c].
  * pool_valid[b,p] = 1 iff all kpool slot tokens are valid (a hole invalidates
  * its pool).  Rows p >= n_pools[b] are written as k_pool = 0,
- * pool_start = -1, pool_valid = 0: the whole output is written.  A sequence
- * with no valid token gets n_pools = 0 and first_valid = seq_len[b].
+ * pool_start = -1, pool_valid = 0: the whole output is written (k_pool
+ * including the padding pools of the pool-cache layout).  A sequence with no
+ * valid token gets n_pools = 0 and first_valid = seq_len[b].
  *
  *   k, gate      [B, T_max, D] act        valid [B, T_max] uint8 (nonzero = valid)
  *   ape          [kpool, D] fp32          seq_len [B] int32, each in [0, T_max]
- *   k_pool       [B, P_max, D] act (out)  pool_start [B, P_max] int32 (out)
- *   pool_valid   [B, P_max] uint8 (out)   n_pools, first_valid [B] int32 (out)
+ *   k_pool       pool cache (out): B * DSA_POOL_CACHE_POOLS(P_max) * D act
+ *   pool_start   [B, P_max] int32 (out)   pool_valid [B, P_max] uint8 (out)
+ *   n_pools, first_valid [B] int32 (out)
  * Requires 1 <= kpool <= DSA_MAX_KPOOL, D % 8 == 0 and D <= 1024,
  * P_max >= T_max / kpool.  Computes in fp32; bf16 outputs are rounded to
  * nearest even once.
@@ -107,7 +124,8 @@ int dsa_kpool_compress(const void* k, const void* gate, const uint8_t* valid, co
  * mean-subtracting, with bias); "Module tp", "Why the indexer is REPLICATED,
  * not sharded" (the score is a plain sum over heads of w[h]*relu(scale*dot)).
  *
- * For row q of sequence b = row_seq[q] and pool p:
+ * For row q of sequence b = row_seq[q] and pool p (k_pool in the pool-cache
+ * layout described above):
  *   kn = LayerNorm(k_pool[b,p,:]; gamma, beta, eps)   (biased variance)
  *   scores[q,p] = sum_h w[q,h] * max(0, scale * <q[q,h,:], kn>)
  * when p is a candidate -- pool_valid[b,p] != 0 and
@@ -116,7 +134,8 @@ int dsa_kpool_compress(const void* k, const void* gate, const uint8_t* valid, co
  * written.
  *
  *   q [Q, H, D] act     w [Q, H] fp32     gamma, beta [D] fp32
- *   k_pool [B, P_max, D] act              pool_start [B, P_max] int32
+ *   k_pool: pool cache, B * DSA_POOL_CACHE_POOLS(P_max) * D act
+ *   pool_start [B, P_max] int32
  *   pool_valid [B, P_max] uint8           row_seq, row_pos [Q] int32
  *   scores [Q, P_max] fp32 (out)
  * Requires D in {32, 64, 128} and 1 <= H <= 64.

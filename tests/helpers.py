@@ -9,6 +9,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from dsa_decode_amd.layout import tile_pool_cache, untile_pool_cache  # noqa: F401
+
 from oracle import dsa_oracle as O
 
 

@@ -19,7 +19,8 @@ import torch
 from dsa_decode_amd import synth
 from oracle import dsa_oracle as O
 from tests.helpers import (act_from_f64, assert_compress_close, assert_scores_close,
-                           assert_topk_property, dev, pool_cache_from_oracle, score_scale)
+                           assert_topk_property, dev, pool_cache_from_oracle, score_scale,
+                           tile_pool_cache, untile_pool_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +67,9 @@ def check_compress(d):
     np.testing.assert_array_equal(out["pool_start"].cpu().numpy(), comp["pool_start"])
     np.testing.assert_array_equal(out["pool_valid"].cpu().numpy().astype(bool), comp["pool_valid"])
     absk = _absk_pool(d)
-    assert_compress_close(out["k_pool"], comp["k_pool"], absk, wl.torch_dtype)
+    got = out["k_pool"].cpu()
+    assert_compress_close(untile_pool_cache(got, wl.P_max), comp["k_pool"], absk, wl.torch_dtype)
+    assert tuple(got.shape) == (wl.B, 16 * ((wl.P_max + 15) // 16), wl.D)
 
 
 def scores_inputs(d, k_pool_override=None):
@@ -79,7 +82,7 @@ def scores_inputs(d, k_pool_override=None):
 
 def run_scores(d, pc):
     ip, wl = d["ip"], d["wl"]
-    return ops().dsa_index_scores(dev(ip["q"]), dev(ip["w"]), ip["scale"], dev(pc["k_pool"]),
+    return ops().dsa_index_scores(dev(ip["q"]), dev(ip["w"]), ip["scale"], dev(tile_pool_cache(pc["k_pool"])),
                                   dev(pc["pool_start"]), dev(pc["pool_valid"]), dev(ip["gamma"]),
                                   dev(ip["beta"]), ip["eps"], dev(ip["row_seq"]), dev(ip["row_pos"]),
                                   wl.kp)
@@ -289,7 +292,11 @@ def test_compress_edge_cases():
         np.testing.assert_array_equal(out["pool_start"].cpu().numpy(), comp["pool_start"])
         np.testing.assert_array_equal(out["pool_valid"].cpu().numpy().astype(bool), comp["pool_valid"])
         absk = O.kpool_compress(k.abs(), gate, valid, ape, seq_len, kp, P_max)["k_pool"]
-        assert_compress_close(out["k_pool"], comp["k_pool"], absk, dtype)
+        got = out["k_pool"].cpu()
+        assert_compress_close(untile_pool_cache(got, P_max), comp["k_pool"], absk, dtype)
+        # the layout's padding pools (past P_max, up to a whole 16-pool tile) are written as zeros
+        full = untile_pool_cache(got, got.shape[1])
+        assert (full[:, P_max:] == 0).all()
 
 
 @pytest.mark.parametrize("H,D,dtype", [(16, 128, torch.bfloat16), (32, 128, torch.bfloat16),
@@ -310,7 +317,8 @@ def test_scores_paths_ragged_causal_and_mixed_rows(H, D, dtype):
     w = torch.from_numpy((rng.random((Q, H)) / H).astype(np.float32))
     gamma = torch.from_numpy((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
     beta = torch.from_numpy((0.02 * rng.standard_normal(D)).astype(np.float32))
-    got = ops().dsa_index_scores(dev(q), dev(w), D ** -0.5, dev(k_pool), dev(torch.from_numpy(pool_start)),
+    got = ops().dsa_index_scores(dev(q), dev(w), D ** -0.5, dev(tile_pool_cache(k_pool)),
+                                 dev(torch.from_numpy(pool_start)),
                                  dev(torch.from_numpy(pool_valid)), dev(gamma), dev(beta), 1e-5,
                                  dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(row_pos)), kp).cpu().numpy()
     ref = O.index_scores(q, w, D ** -0.5, k_pool, pool_start, pool_valid, gamma, beta, 1e-5, row_seq, row_pos, kp)
