@@ -178,7 +178,7 @@ def main() -> int:
     q, w, gamma, beta = dev(ip["q"]), dev(ip["w"]), dev(ip["gamma"]), dev(ip["beta"])
     row_seq, row_pos = dev(ip["row_seq"]), dev(ip["row_pos"])
     q_lat = dev(mi["q_lat"])
-    tk_ws = torch.empty(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    tk_ws = torch.zeros(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
     mla_ws = torch.empty(max(1, ops.dsa_sparse_mla_workspace_bytes(Q, wl.Hm, wl.Dl, W, ops.DSA_BF16)),
                          dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()

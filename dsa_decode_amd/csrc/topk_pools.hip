@@ -94,6 +94,8 @@ struct TkShared {
   uint32_t tie[32 * NW];  // per (key slot, wave): tied keys, then their exclusive prefix
   uint32_t info[4];
   uint32_t slot;
+  uint32_t ticket;
+  uint32_t flag;
 };
 
 // Valid keys (hi != 0): their number, largest and smallest hi (one barrier;
@@ -204,7 +206,7 @@ struct RadixResult {
 // those with (v >> lo) > (prefix >> lo), plus `need` of the cnt keys with
 // (v >> lo) == (prefix >> lo) (all of them when cnt == need).
 template <int NT, int KPT>
-__device__ RadixResult radix_on(const uint32_t (&v)[KPT], uint32_t vmask, int h, uint32_t prefix,
+__device__ __forceinline__ RadixResult radix_on(const uint32_t (&v)[KPT], uint32_t vmask, int h, uint32_t prefix,
                                 uint32_t need, TkShared<NT>& sh) {
   while (true) {
     const int lo = h >= kDig - 1 ? h - (kDig - 1) : 0;
@@ -308,7 +310,7 @@ __device__ __forceinline__ void sort512_desc(uint64_t& a0, uint64_t& a1, TkShare
 // Sort sh.sel[0..kp2) descending in LDS (kp2 a power of two <= DSA_MAX_SELECT_K;
 // used when select_k > 512).
 template <int NT>
-__device__ void bitonic_desc(TkShared<NT>& sh, int kp2) {
+__device__ __forceinline__ void bitonic_desc(TkShared<NT>& sh, int kp2) {
   for (int k = 2; k <= kp2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < kp2; i += NT) {
@@ -328,7 +330,7 @@ __device__ void bitonic_desc(TkShared<NT>& sh, int kp2) {
 // slot j of thread t is position base + j*NT + t.  Returns the mask of the
 // first `need` of them (two barriers).
 template <int NT, int KPT>
-__device__ uint32_t tie_by_position(uint32_t eqm, uint32_t need, TkShared<NT>& sh) {
+__device__ __forceinline__ uint32_t tie_by_position(uint32_t eqm, uint32_t need, TkShared<NT>& sh) {
   constexpr int NW = TkShared<NT>::NW;
   constexpr int NE = KPT * NW;                       // (slot, wave) counters
   constexpr int PER = (NE + kWave - 1) / kWave;      // counters per lane of wave 0
@@ -367,17 +369,23 @@ __device__ uint32_t tie_by_position(uint32_t eqm, uint32_t need, TkShared<NT>& s
 
 // One workgroup: select the K largest keys of its KPT*NT keys and either write
 // them unsorted to the workspace (partial) or sort them and write pool ids.
+// A chunk winner for the merge: an agent-scope store (written through to the
+// device's coherence point, so the merging workgroup can read it without
+// whole-cache writeback and invalidation).
+__device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup's selection: chunk c of row `row` (FROM_SCORES: pools c*chunk
+// .. of the scores; otherwise the nsplit_in chunk winner lists of the row) ->
+// its K largest keys, written to chunk slot c of keys_out (partial) or sorted
+// to pool_ids (FINAL).  nchunk: chunk slots per row of keys_out.
 template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
-__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
-                                                  const uint64_t* __restrict__ keys_in,
-                                                  int P, int chunk, int nsplit_in, int K,
-                                                  uint64_t* __restrict__ keys_out,
-                                                  int32_t* __restrict__ pool_ids) {
+__device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int nchunk, const float* __restrict__ scores,
+                           const uint64_t* __restrict__ keys_in, int P, int chunk, int nsplit_in, int K,
+                           uint64_t* __restrict__ keys_out, int32_t* __restrict__ pool_ids) {
   static_assert(KPT <= 32, "selection masks are 32-bit");
-  __shared__ TkShared<NT> sh;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int row = blockIdx.y;
-  const int c = blockIdx.x;
   uint32_t hi[KPT];
   uint32_t lo[FROM_SCORES ? 1 : KPT];
   const int base = c * chunk;
@@ -399,16 +407,21 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       hi[j] = score_key(v[j]) & in;
     }
   } else {
+    // chunk winners published by other workgroups of this launch: agent-scope
+    // loads (coherent with their agent-scope stores, no cache maintenance)
     const int n = nsplit_in * K;
-    const auto rs = make_rsrc(keys_in + size_t(row) * n, uint32_t(n) * 8u);
-    u32x2 k[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      k[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (j * NT + tid) * 8, 0, 0));
+    const uint64_t* src = keys_in + size_t(row) * n;
+    uint64_t k[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      hi[j] = k[j][1];  // 0 for padding keys and past the end
-      lo[j] = k[j][0];
+      const int i = j * NT + tid;
+      k[j] = __hip_atomic_load(src + (i < n ? i : n - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool in = j * NT + tid < n;
+      hi[j] = in ? uint32_t(k[j] >> 32) : 0u;  // 0 for padding keys and past the end
+      lo[j] = uint32_t(k[j]);
     }
   }
   if (tid == 0) sh.slot = 0;
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         __syncthreads();
         // slots [0, above + cnt) now hold the keys of those bins, bin by bin;
         // one thread per slot ranks its key (bin mates read four at a time)
-        uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * gridDim.x + c) * K;
+        uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * nchunk + c) * K;
         int32_t* dst = FINAL ? pool_ids + size_t(row) * K : nullptr;
         for (uint32_t sl = tid; sl < above + cnt; sl += NT) {
           const uint64_t me = sh.sel[sl];
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
           }
           if (pos < uint32_t(K)) {
             if constexpr (FINAL) dst[pos] = int32_t(0xffffffffu - uint32_t(me));
-            else out[pos] = me;
+            else publish(out + pos, me);
           }
         }
         return;
@@ -522,41 +535,155 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   if (lane == 63) wbase = atomicAdd(&sh.slot, incl);
   uint32_t at = __builtin_amdgcn_readlane(wbase, 63) + incl - mine;
 
-  if constexpr (!FINAL) {
-    uint64_t* out = keys_out + (size_t(row) * gridDim.x + c) * K;
+  // sort the selected keys (0-padded) in LDS; chunk winners (partial) are
+  // written sorted too, as the merge reads only the head of each list first
+  int kp2 = 1;
+  while (kp2 < K) kp2 <<= 1;
+  if (kp2 < 512) kp2 = 512;
+  for (int i = int(nsel) + tid; i < kp2; i += NT) sh.sel[i] = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if ((selmask >> j) & 1u) out[at++] = key_of(j);
-    for (int i = int(nsel) + tid; i < K; i += NT) out[i] = 0;
-    return;
-  } else {
-    int kp2 = 1;
-    while (kp2 < K) kp2 <<= 1;
-    if (kp2 < 512) kp2 = 512;
-    for (int i = int(nsel) + tid; i < kp2; i += NT) sh.sel[i] = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      if ((selmask >> j) & 1u) sh.sel[at++] = key_of(j);
+  for (int j = 0; j < KPT; ++j)
+    if ((selmask >> j) & 1u) sh.sel[at++] = key_of(j);
+  __syncthreads();
+  uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * nchunk + c) * K;
+  int32_t* dst = FINAL ? pool_ids + size_t(row) * K : nullptr;
+  auto emit = [&](int e, uint64_t k) {
+    if constexpr (FINAL) dst[e] = (e < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
+    else publish(out + e, e < int(nsel) ? k : 0);
+  };
+  if (kp2 == 512) {
+    uint64_t a0 = 0, a1 = 0;
+    if (tid < 256) { a0 = sh.sel[2 * tid]; a1 = sh.sel[2 * tid + 1]; }
     __syncthreads();
-    int32_t* dst = pool_ids + size_t(row) * K;
-    if (kp2 == 512) {
-      uint64_t a0 = 0, a1 = 0;
-      if (tid < 256) { a0 = sh.sel[2 * tid]; a1 = sh.sel[2 * tid + 1]; }
-      __syncthreads();
-      sort512_desc<NT>(a0, a1, sh);
-      if (tid < 256) {
-        const int e0 = 2 * tid, e1 = 2 * tid + 1;
-        if (e0 < K) dst[e0] = (e0 < int(nsel) && a0 != 0) ? int32_t(0xffffffffu - uint32_t(a0)) : -1;
-        if (e1 < K) dst[e1] = (e1 < int(nsel) && a1 != 0) ? int32_t(0xffffffffu - uint32_t(a1)) : -1;
-      }
-      return;
+    sort512_desc<NT>(a0, a1, sh);
+    if (tid < 256) {
+      if (2 * tid < K) emit(2 * tid, a0);
+      if (2 * tid + 1 < K) emit(2 * tid + 1, a1);
     }
-    bitonic_desc<NT>(sh, kp2);
-    for (int i = tid; i < K; i += NT) {
-      const uint64_t k = sh.sel[i];
-      dst[i] = (i < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
+    return;
+  }
+  bitonic_desc<NT>(sh, kp2);
+  for (int i = tid; i < K; i += NT) emit(i, sh.sel[i]);
+}
+
+// Merge of a row's S sorted chunk-winner lists (stride K) from their first m
+// keys each (S*m keys, m < K).  The row's K winners are exactly the K largest
+// of these when no list could hold further winners past its first m, which is
+// certain when the m-th key of every full list lies below the bin of the K-th
+// largest key.  Takes the first-pass/rank path; returns false, having written
+// nothing, when a list may hold more winners or the first pass does not apply
+// (the caller then merges the full lists).
+template <int NT, int KPT>
+__device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, int m, int K,
+                                            const uint64_t* __restrict__ keys, int32_t* __restrict__ pool_ids) {
+  static_assert(KPT <= 32, "selection masks are 32-bit");
+  const int tid = threadIdx.x;
+  const int n = S * m;
+  const uint64_t* src = keys + size_t(row) * S * K;
+  uint64_t k[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = j * NT + tid;
+    const int ii = i < n ? i : n - 1;
+    k[j] = __hip_atomic_load(src + size_t(ii / m) * K + ii % m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  uint32_t hi[KPT], lo[KPT];
+  uint32_t vmask = 0, lastmask = 0;  // valid keys; keys that end a list's head
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = j * NT + tid;
+    const bool in = i < n;
+    hi[j] = in ? uint32_t(k[j] >> 32) : 0u;
+    lo[j] = uint32_t(k[j]);
+    vmask |= hi[j] != 0 ? (1u << j) : 0u;
+    lastmask |= (in && i % m == m - 1) ? (1u << j) : 0u;
+  }
+  if (tid == 0) sh.flag = 0;
+  for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
+  uint32_t nvalid, kmax, kmin;
+  block_stats<NT, KPT>(hi, sh, nvalid, kmax, kmin);
+  if (nvalid <= uint32_t(K) || kmax == kmin) return false;
+  const float fmn = key_float(kmin);
+  const float scale = float(kBins) / (key_float(kmax) - fmn);
+  auto bin_of = [&](uint32_t key) -> uint32_t {
+    return min(uint32_t((key_float(key) - fmn) * scale), uint32_t(kBins - 1));
+  };
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((vmask >> j) & 1u) atomicAdd(&sh.hist[bin_of(hi[j])], 1u);
+  __syncthreads();
+  if ((tid >> 6) == 0) scan_find<NT, true>(sh, uint32_t(K));
+  __syncthreads();
+  const uint32_t t = sh.info[0], above = sh.info[1], cnt = sh.info[2], maxc = sh.info[3];
+  if (maxc > uint32_t(kRankCap)) return false;
+  // scatter the keys of bins >= t; flag a full list head that reaches bin t
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t d = bin_of(hi[j]);
+    if (((vmask >> j) & 1u) && d >= t) {
+      sh.sel[sh.sfx[d] + atomicAdd(&sh.hist[d], 1u)] = (uint64_t(hi[j]) << 32) | lo[j];
+      if ((lastmask >> j) & 1u) sh.flag = 1;
     }
   }
+  __syncthreads();
+  if (sh.flag) return false;
+  int32_t* dst = pool_ids + size_t(row) * K;
+  for (uint32_t sl = tid; sl < above + cnt; sl += NT) {
+    const uint64_t me = sh.sel[sl];
+    const uint32_t d = bin_of(uint32_t(me >> 32));
+    const uint32_t r0 = sh.sfx[d], nb = sh.hist[d];
+    uint32_t pos = r0;
+    for (uint32_t i = 0; i < nb; i += 4) {
+      const uint64_t a0 = sh.sel[r0 + i];
+      const uint64_t a1 = sh.sel[r0 + min(i + 1, nb - 1)];
+      const uint64_t a2 = sh.sel[r0 + min(i + 2, nb - 1)];
+      const uint64_t a3 = sh.sel[r0 + min(i + 3, nb - 1)];
+      pos += (a0 > me ? 1u : 0u) + (i + 1 < nb && a1 > me ? 1u : 0u) + (i + 2 < nb && a2 > me ? 1u : 0u) +
+             (i + 3 < nb && a3 > me ? 1u : 0u);
+    }
+    if (pos < uint32_t(K)) dst[pos] = int32_t(0xffffffffu - uint32_t(me));
+  }
+  return true;
+}
+
+template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
+                                                  const uint64_t* __restrict__ keys_in,
+                                                  int P, int chunk, int nsplit_in, int K,
+                                                  uint64_t* __restrict__ keys_out,
+                                                  int32_t* __restrict__ pool_ids) {
+  __shared__ TkShared<NT> sh;
+  topk_block<NT, KPT, FROM_SCORES, FINAL>(sh, blockIdx.y, blockIdx.x, gridDim.x, scores, keys_in, P, chunk,
+                                          nsplit_in, K, keys_out, pool_ids);
+}
+
+// Split rows in one launch: workgroup (c, row) selects chunk c's K winners,
+// publishes them (agent-scope stores, complete before it moves on), and takes
+// a ticket from the row's counter; the workgroup that takes the last ticket
+// (all chunks of the row are then published) resets the counter to zero and
+// merges the row's winner lists.  A counter that starts at zero is zero again
+// after every call.
+template <int NT, int KPT1, int KPTH, int KPT2>
+__global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict__ scores, int P, int chunk,
+                                                        int nsplit, int K, int m, uint64_t* __restrict__ keys,
+                                                        uint32_t* __restrict__ counters,
+                                                        int32_t* __restrict__ pool_ids) {
+  __shared__ TkShared<NT> sh;
+  const int row = blockIdx.y;
+  topk_block<NT, KPT1, true, false>(sh, row, blockIdx.x, nsplit, scores, nullptr, P, chunk, 0, K, keys, nullptr);
+  // every thread's winner stores are complete before the row's counter moves
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sh.ticket = __hip_atomic_fetch_add(&counters[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sh.ticket != uint32_t(nsplit - 1)) return;
+  // the last ticket: every chunk's winners are published; reset the counter
+  // for the next call and merge
+  if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (m < K && merge_heads<NT, KPTH>(sh, row, nsplit, m, K, keys, pool_ids)) return;
+  __syncthreads();
+  topk_block<NT, KPT2, false, true>(sh, row, 0, 1, nullptr, keys, P, 0, nsplit, K, nullptr, pool_ids);
 }
 
 struct TkPlan {
@@ -564,7 +691,14 @@ struct TkPlan {
   int chunk;   // pools per chunk
   int nt1, kpt1;  // first launch: threads and keys per thread
   int nt2, kpt2;  // merge launch
+  bool fused;     // split rows in one launch (512 threads, 8 keys per thread per chunk)
+  int kpt_m;      // fused: merge keys per thread (full lists)
+  int head;       // fused: keys taken first from the head of each sorted winner list
+  int kpt_h;      // fused: keys per thread of that first merge
 };
+
+constexpr int kFusedThreads = 512;
+constexpr int kFusedKpt = 8;  // chunk keys per thread in the fused launch (chunks <= 4096)
 
 static int pow2_at_least(long v) {
   int p = 1;
@@ -594,9 +728,29 @@ static TkPlan tk_plan(int Q, int P, int K) {
   pl.nsplit = nsplit;
   pl.chunk = (P + nsplit - 1) / nsplit;
   tk_shape(pl.chunk, pl.nt1, pl.kpt1);
-  if (nsplit > 1) tk_shape(long(nsplit) * K, pl.nt2, pl.kpt2);
+  pl.fused = false;
+  pl.kpt_m = 0;
+  if (nsplit > 1) {
+    tk_shape(long(nsplit) * K, pl.nt2, pl.kpt2);
+    const long merge = long(nsplit) * K;
+    if (pl.chunk <= kFusedThreads * kFusedKpt && merge <= kFusedThreads * 32) {
+      pl.fused = true;
+      pl.kpt_m = pow2_at_least((merge + kFusedThreads - 1) / kFusedThreads);
+      if (pl.kpt_m < 2) pl.kpt_m = 2;
+      // twice a list's expected share of the K winners, at least 32
+      int head = pow2_at_least((2L * K + nsplit - 1) / nsplit);
+      if (head < 32) head = 32;
+      pl.head = head < K ? head : K;
+      pl.kpt_h = pow2_at_least((long(nsplit) * pl.head + kFusedThreads - 1) / kFusedThreads);
+      if (pl.kpt_h < 2) pl.kpt_h = 2;
+      if (pl.kpt_h > 4) pl.head = K;  // heads of more than 2048 keys: merge the full lists
+    }
+  }
   return pl;
 }
+
+// workspace: the rows' merge counters, then the chunk winner lists
+static size_t tk_counter_bytes(int Q) { return (size_t(Q) * sizeof(uint32_t) + 255) & ~size_t(255); }
 
 template <int NT, bool FROM_SCORES, bool FINAL>
 static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, const uint64_t* keys_in,
@@ -634,7 +788,7 @@ using namespace dsa;
 extern "C" size_t dsa_topk_workspace_bytes(int Q, int P, int K) {
   if (Q <= 0 || P <= 0 || K <= 0) return 0;
   const TkPlan pl = tk_plan(Q, P, K);
-  return pl.nsplit > 1 ? size_t(Q) * pl.nsplit * K * sizeof(uint64_t) : 0;
+  return pl.nsplit > 1 ? tk_counter_bytes(Q) + size_t(Q) * pl.nsplit * K * sizeof(uint64_t) : 0;
 }
 
 extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids,
@@ -649,10 +803,31 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
   const size_t need = dsa_topk_workspace_bytes(Q, P, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
-  uint64_t* ws = static_cast<uint64_t*>(workspace);
   dim3 g1(pl.nsplit, Q);
   if (pl.nsplit == 1) {
     launch_tk_nt<true, true>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
+    return launch_status();
+  }
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  uint64_t* ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tk_counter_bytes(Q));
+  if (pl.fused) {
+#define DSA_TKF(KH, KM)                                                                                  \
+  hipLaunchKernelGGL((topk_split_kernel<kFusedThreads, kFusedKpt, KH, KM>), g1, dim3(kFusedThreads), 0, s, \
+                     scores, P, pl.chunk, pl.nsplit, K, pl.head, ws, counters, pool_ids)
+#define DSA_TKF_H(KM)       \
+  if (pl.kpt_h <= 2)        \
+    DSA_TKF(2, KM);         \
+  else                      \
+    DSA_TKF(4, KM)
+    switch (pl.kpt_m) {
+      case 2: DSA_TKF_H(2); break;
+      case 4: DSA_TKF_H(4); break;
+      case 8: DSA_TKF_H(8); break;
+      case 16: DSA_TKF_H(16); break;
+      default: DSA_TKF_H(32); break;
+    }
+#undef DSA_TKF_H
+#undef DSA_TKF
     return launch_status();
   }
   launch_tk_nt<true, false>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);

@@ -100,7 +100,8 @@ def dsa_topk_pools(scores, K: int, pool_ids=None, workspace=None):
         pool_ids = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
     need = dsa_topk_workspace_bytes(Q, P, K)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        # zero-filled: the workspace starts with per-row counters that every call returns to zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.load().dsa_topk_pools(_dev(scores, "scores", torch.float32), Q, P, K,

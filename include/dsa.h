@@ -160,7 +160,10 @@ int dsa_index_scores(const void* q, const float* w, float scale, const void* k_p
  *
  *   scores [Q, P] fp32     pool_ids [Q, K] int32 (out)
  *   workspace: device buffer of dsa_topk_workspace_bytes(Q, P, K) bytes
- *              (may be NULL when that is 0).
+ *              (may be NULL when that is 0).  It must be zero-filled before
+ *              its first use: it starts with one counter per row, which the
+ *              call leaves at zero again (the rest is scratch).  Calls that
+ *              share a workspace must not overlap.
  * Requires 1 <= K <= DSA_MAX_SELECT_K and P <= 524288.
  */
 size_t dsa_topk_workspace_bytes(int Q, int P, int K);

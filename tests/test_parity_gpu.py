@@ -264,6 +264,39 @@ def test_topk_shapes_ties_and_padding(Q, P, K, ties):
     check_topk(s.numpy(), K)
 
 
+def test_topk_workspace_reuse_across_calls_and_shapes():
+    # one zero-filled workspace for successive calls of different shapes: each
+    # call must leave its per-row counters (the workspace's first 4*Q bytes) at
+    # zero, or the next call's merge would start from a wrong count
+    shapes = [(4, 65536, 512), (2, 30000, 256), (3, 16384, 512), (4, 65536, 512)]
+    need = max(ops().dsa_topk_workspace_bytes(Q, P, K) for Q, P, K in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (Q, P, K) in enumerate(shapes):
+        s = synth.random_scores(Q, P, seed=90 + i, tie_levels=0 if i % 2 else 64, neg_inf_frac=0.1)
+        got = ops().dsa_topk_pools(dev(s), K, workspace=ws).cpu().numpy()
+        np.testing.assert_array_equal(got, O.topk_pools(s.numpy(), K))
+        assert (ws[: 4 * Q] == 0).all()
+
+
+def test_topk_clustered_winners():
+    # the merge of a split row first reads the head of each chunk's sorted
+    # winner list; rows whose K winners crowd into one or a few chunks must
+    # fall back to the full lists and still match
+    Q, P, K = 5, 65536, 512
+    rng = np.random.default_rng(11)
+    s = np.empty((Q, P), np.float32)
+    s[0] = np.arange(P, dtype=np.float32)                 # all winners in the last chunk
+    s[1] = -np.arange(P, dtype=np.float32)                # all winners in the first chunk
+    s[2] = rng.standard_normal(P).astype(np.float32)
+    s[2, 4096:4096 + 300] += 10.0                         # 300 winners in one chunk, the rest spread
+    s[3] = rng.standard_normal(P).astype(np.float32)
+    s[3, ::4096] = 50.0                                   # one sure winner per chunk
+    s[3, 8192:8192 + 200] = 20.0                          # 200 tied winners in one chunk
+    s[4] = np.round(rng.standard_normal(P) * 4).astype(np.float32)  # coarse ties everywhere
+    got = ops().dsa_topk_pools(dev(torch.from_numpy(s)), K).cpu().numpy()
+    np.testing.assert_array_equal(got, O.topk_pools(s, K))
+
+
 def test_topk_is_deterministic():
     s = dev(synth.random_scores(4, 65536, seed=5, tie_levels=100))
     a = ops().dsa_topk_pools(s, 512)
