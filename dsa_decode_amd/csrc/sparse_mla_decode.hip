@@ -37,8 +37,14 @@ constexpr int kMlaThreads = 256;
 
 struct MlaShared {
   uint16_t rows[kMlaSplit][kMlaDl];  // latent rows, 16-byte pieces swizzled per row (64 KiB)
-  uint16_t p[16][kMlaSplit];         // probabilities P[head][token], bf16
-  float red[2][16][16];              // per head: [max | sum][head][wave * 4 + lane group]
+  union {
+    uint16_t q[16][kMlaDl];          // the 16 heads' q_lat, swizzled like the rows (16 KiB)
+    struct {                         // after the logits: the softmax exchange
+      uint16_t p[16][kMlaSplit];     // P[head][token] relative to its wave's maximum, bf16
+      float m[16][4];                // per head: each wave's maximum (log2 domain)
+      float l[16][4];                // per head: each wave's sum of P
+    } x;
+  } u;
 };
 
 // Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Makes the
@@ -89,13 +95,13 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       myid = (bok && id >= 0 && id < T_max) ? id : -1;
     }
   }
-  // q_lat of head h as the B operand of the logits: k-step k covers latent
-  // channels 32k .. 32k+31, lane group kg holds channels 32k + 8kg .. +7
-  bf16x8 qop[16];
-  {
-    const uint16_t* qs = q_lat + (size_t(r) * Hm + h) * kMlaDl + 8 * kg;
+  // q_lat of the 16 heads once per workgroup, straight into LDS (wave w moves
+  // heads 4w .. 4w+3, one 1 KiB row per instruction, swizzled like the rows)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) qop[k] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + 32 * k));
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * w + i;
+    const uint16_t* src = q_lat + (size_t(r) * Hm + hg * 16 + hh) * kMlaDl + 8 * (lane ^ mla_swz(hh));
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.u.q[hh][0]), 16, 0, 0);
   }
   // gather: one row per instruction, lane i fills piece position i with piece
   // i ^ swz of the token's row; absent ids give a zero row
@@ -112,21 +118,28 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows are in LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // q and every wave's rows are in LDS
 
-  // logits of tokens 16w + 4kg + j (j < 4) for head ln, full latent width;
-  // two accumulators shorten the MFMA dependency chain
+  // logits of tokens 16w + 4kg + j (j < 4) for head ln, full latent width
+  // (A = kv rows, B = q^T, both from LDS); two accumulators shorten the MFMA
+  // dependency chain
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   {
-    const int t = 16 * w + ln, sw = mla_swz(t);
+    const int t = 16 * w + ln, sw = mla_swz(t), sq = mla_swz(ln);
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
       const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + kg) ^ sw) * 8]));
       const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + 4 + kg) ^ sw) * 8]));
-      acc0 = mfma16x16x32(a0, qop[k], acc0);
-      acc1 = mfma16x16x32(a1, qop[k + 1], acc1);
+      const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.u.q[ln][((4 * k + kg) ^ sq) * 8]));
+      const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.u.q[ln][((4 * k + 4 + kg) ^ sq) * 8]));
+      acc0 = mfma16x16x32(a0, b0, acc0);
+      acc1 = mfma16x16x32(a1, b1, acc1);
     }
   }
+  // softmax within the wave: its maximum over its 16 tokens per head, P
+  // relative to that maximum; the value contraction rescales by the waves'
+  // maxima, so no barrier separates the maxima from P
   float x[4];
   float m = -INFINITY;
 #pragma unroll
@@ -134,16 +147,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     x[j] = (vmask >> (4 * kg + j)) & 1u ? (acc0[j] + acc1[j]) * scale_log2 : -INFINITY;
     m = fmaxf(m, x[j]);
   }
-  sh.red[0][ln][4 * w + kg] = m;
-  __syncthreads();  // maxima published; every wave's rows are in LDS
-  {
-    const f32x4* rm = reinterpret_cast<const f32x4*>(&sh.red[0][ln][0]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 v = rm[i];
-      m = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-    }
-  }
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
   const float m_use = m == -INFINITY ? 0.f : m;
   float p[4], l = 0.f;
 #pragma unroll
@@ -151,14 +156,44 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
     l += p[j];
   }
-  sh.red[1][ln][4 * w + kg] = l;
-  *reinterpret_cast<u32x2*>(&sh.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
-  __syncthreads();  // P and the sums published
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  __syncthreads();  // every wave is done with q: its region takes the exchange
+  *reinterpret_cast<u32x2*>(&sh.u.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+  if (kg == 0) {
+    sh.u.x.m[ln][w] = m_use;
+    sh.u.x.l[ln][w] = l;
+  }
+  __syncthreads();  // P, the maxima and the sums published
 
+  // the row's maximum M; tokens of wave v carry the factor 2^(m_v - M)
+  const f32x4 mv = *reinterpret_cast<const f32x4*>(&sh.u.x.m[ln][0]);
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&sh.u.x.l[ln][0]);
+  float M = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) M = fmaxf(M, lv[v] > 0.f ? mv[v] : -INFINITY);
+  const float M_use = M == -INFINITY ? 0.f : M;
+  float fv[4];
+  l = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    fv[v] = lv[v] > 0.f ? __builtin_amdgcn_exp2f(mv[v] - M_use) : 0.f;
+    l = fmaf(fv[v], lv[v], l);
+  }
   // O^T[dl, head] over latent quarter w: A = kv^T (16 dl x 32 tokens) from two
-  // transposing reads, B = P^T (32 tokens x 16 heads)
-  const bf16x8 pb0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[ln][8 * kg]));
-  const bf16x8 pb1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[ln][32 + 8 * kg]));
+  // transposing reads, B = P^T (32 tokens x 16 heads); the 8 tokens of lane
+  // group kg in k-step ks belong to wave 2ks + kg/2
+  bf16x8 pb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.u.x.p[ln][32 * ks + 8 * kg]);
+    const float f = fv[2 * ks + (kg >> 1)];
+    u32x4 sc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sc[e] = pack2bf(__uint_as_float(raw[e] << 16) * f, __uint_as_float(raw[e] & 0xffff0000u) * f);
+    pb[ks] = as_bf16x8(sc);
+  }
   f32x4 o[8];
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
@@ -170,23 +205,15 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
       const u32x2 lo = lds_read_tr16(&sh.rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
       const u32x2 hi = lds_read_tr16(&sh.rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
-      a = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), ks ? pb1 : pb0, a);
+      a = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], a);
     }
     o[blk] = a;
   }
-  {
-    const f32x4* rs = reinterpret_cast<const f32x4*>(&sh.red[1][ln][0]);
-    l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 v = rs[i];
-      l += (v[0] + v[1]) + (v[2] + v[3]);
-    }
-  }
+  const float m_use_row = M_use;
 
   // o[blk][j] = sum_t p_t kv[t][dl = 128 w + 16 blk + 4 kg + j] for head h
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const float lse_v = l > 0.f ? (m_use + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  const float lse_v = l > 0.f ? (m_use_row + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
   if (nsplit == 1) {
     uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
 #pragma unroll
