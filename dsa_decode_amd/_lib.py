@@ -39,6 +39,7 @@ DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA
 DSA_F32, DSA_BF16 = 0, 1
 DSA_MAX_KPOOL = 8
 DSA_MAX_SELECT_K = 2048
+DSA_TOPK_COUNTER_BYTES = 262144
 
 _lib = None
 

@@ -749,8 +749,10 @@ static TkPlan tk_plan(int Q, int P, int K) {
   return pl;
 }
 
-// workspace: the rows' merge counters, then the chunk winner lists
-static size_t tk_counter_bytes(int Q) { return (size_t(Q) * sizeof(uint32_t) + 255) & ~size_t(255); }
+// workspace: a block of merge counters of fixed size (one per row, for every
+// Q the entry point accepts, so that the block sits at the same place for
+// every shape), then the chunk winner lists
+static_assert(DSA_TOPK_COUNTER_BYTES >= 65535 * sizeof(uint32_t), "one counter per row");
 
 template <int NT, bool FROM_SCORES, bool FINAL>
 static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, const uint64_t* keys_in,
@@ -788,7 +790,7 @@ using namespace dsa;
 extern "C" size_t dsa_topk_workspace_bytes(int Q, int P, int K) {
   if (Q <= 0 || P <= 0 || K <= 0) return 0;
   const TkPlan pl = tk_plan(Q, P, K);
-  return pl.nsplit > 1 ? tk_counter_bytes(Q) + size_t(Q) * pl.nsplit * K * sizeof(uint64_t) : 0;
+  return pl.nsplit > 1 ? DSA_TOPK_COUNTER_BYTES + size_t(Q) * pl.nsplit * K * sizeof(uint64_t) : 0;
 }
 
 extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids,
@@ -809,7 +811,7 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
     return launch_status();
   }
   uint32_t* counters = static_cast<uint32_t*>(workspace);
-  uint64_t* ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + tk_counter_bytes(Q));
+  uint64_t* ws = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + DSA_TOPK_COUNTER_BYTES);
   if (pl.fused) {
 #define DSA_TKF(KH, KM)                                                                                  \
   hipLaunchKernelGGL((topk_split_kernel<kFusedThreads, kFusedKpt, KH, KM>), g1, dim3(kFusedThreads), 0, s, \

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from .layout import pool_cache_pools
-from ._lib import DSA_BF16, DSA_F32, DsaError, check  # noqa: F401
+from ._lib import DSA_BF16, DSA_F32, DSA_TOPK_COUNTER_BYTES, DsaError, check  # noqa: F401
 
 _ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
 

@@ -50,6 +50,10 @@ extern "C" {
 #define DSA_ERR_WORKSPACE    -4  /* workspace missing or too small */
 #define DSA_ERR_HIP          -5  /* the HIP runtime reported an error at launch */
 
+/* Size of the counter block at the start of a dsa_topk_pools workspace: the
+ * same for every shape. */
+#define DSA_TOPK_COUNTER_BYTES 262144
+
 /* activation dtypes */
 #define DSA_F32   0
 #define DSA_BF16  1
@@ -160,10 +164,12 @@ int dsa_index_scores(const void* q, const float* w, float scale, const void* k_p
  *
  *   scores [Q, P] fp32     pool_ids [Q, K] int32 (out)
  *   workspace: device buffer of dsa_topk_workspace_bytes(Q, P, K) bytes
- *              (may be NULL when that is 0).  It must be zero-filled before
- *              its first use: it starts with one counter per row, which the
- *              call leaves at zero again (the rest is scratch).  Calls that
- *              share a workspace must not overlap.
+ *              (may be NULL when that is 0).  Its first
+ *              DSA_TOPK_COUNTER_BYTES bytes are merge counters: zero-fill
+ *              them before the first use; every call leaves them at zero, so
+ *              the buffer then serves calls of any shape that fit it (the
+ *              rest is scratch).  Calls that share a workspace must not
+ *              overlap.
  * Requires 1 <= K <= DSA_MAX_SELECT_K and P <= 524288.
  */
 size_t dsa_topk_workspace_bytes(int Q, int P, int K);
@@ -204,9 +210,11 @@ int dsa_expand_selection(const int32_t* pool_ids, int Q, int K, const int32_t* r
  *
  *   q_lat [Q, Hm, Dl] act    kv [B, T_max, Dl] act    token_ids [Q, W] int32
  *   out [Q, Hm, Dl] act (out)    lse [Q, Hm] fp32 (out, may be NULL)
- *   workspace: dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype) bytes.
- * Requires Dl in {64, 128, 256, 512} and 1 <= Hm <= 128; the bf16 MFMA path
- * is taken for Dl == 512 with Hm % 16 == 0.
+ *   workspace: device buffer of dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W,
+ *              dtype) bytes (may be NULL when that is 0), scratch for the
+ *              split partials; calls that share it must not overlap.
+ * Requires Dl in {64, 128, 256, 512}, 1 <= Hm <= 128 and W <= 16384; the bf16
+ * MFMA path is taken for Dl == 512 with Hm % 16 == 0.
  */
 size_t dsa_sparse_mla_workspace_bytes(int Q, int Hm, int Dl, int W, int dtype);
 int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_seq,

@@ -38,6 +38,26 @@ def test_status_strings_and_version(lib):
     assert lib.dsa_status_string(0) == b"ok"
 
 
+def test_binding_constants_match_header():
+    # every plain numeric #define of the header has the same value in the binding
+    from dsa_decode_amd import _lib
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defs = dict(re.findall(r"#define\s+(DSA_\w+)\s+(-?\d+)\s*$", text, flags=re.M))
+    assert {"DSA_TOPK_COUNTER_BYTES", "DSA_MAX_SELECT_K"} <= set(defs)
+    for name, value in defs.items():
+        if name in ("DSA_ABI_VERSION",):
+            continue
+        assert getattr(_lib, name) == int(value), name
+
+
+def test_split_workspace_sizes(lib):
+    from dsa_decode_amd._lib import DSA_TOPK_COUNTER_BYTES
+    assert lib.dsa_topk_workspace_bytes(4, 65536, 512) > DSA_TOPK_COUNTER_BYTES
+    assert lib.dsa_topk_workspace_bytes(1, 1000, 8) == 0                 # one chunk: no workspace
+    assert lib.dsa_sparse_mla_workspace_bytes(4, 64, 512, 2048, 1) > 0
+    assert lib.dsa_sparse_mla_workspace_bytes(4, 64, 512, 64, 1) == 0      # one slice: no workspace
+
+
 def _compress(lib, **kw):
     a = dict(k=FAKE, gate=FAKE, valid=FAKE, ape=FAKE, seq_len=FAKE, B=1, T_max=64, D=32, kpool=4,
              P_max=16, dtype=0, k_pool=FAKE, pool_start=FAKE, pool_valid=FAKE, n_pools=FAKE,

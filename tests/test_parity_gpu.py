@@ -266,8 +266,8 @@ def test_topk_shapes_ties_and_padding(Q, P, K, ties):
 
 def test_topk_workspace_reuse_across_calls_and_shapes():
     # one zero-filled workspace for successive calls of different shapes: each
-    # call must leave its per-row counters (the workspace's first 4*Q bytes) at
-    # zero, or the next call's merge would start from a wrong count
+    # call must leave the counter block at the workspace's start at zero, or
+    # the next call's merge would start from a wrong count
     shapes = [(4, 65536, 512), (2, 30000, 256), (3, 16384, 512), (4, 65536, 512)]
     need = max(ops().dsa_topk_workspace_bytes(Q, P, K) for Q, P, K in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
@@ -275,7 +275,7 @@ def test_topk_workspace_reuse_across_calls_and_shapes():
         s = synth.random_scores(Q, P, seed=90 + i, tie_levels=0 if i % 2 else 64, neg_inf_frac=0.1)
         got = ops().dsa_topk_pools(dev(s), K, workspace=ws).cpu().numpy()
         np.testing.assert_array_equal(got, O.topk_pools(s.numpy(), K))
-        assert (ws[: 4 * Q] == 0).all()
+        assert (ws[: ops().DSA_TOPK_COUNTER_BYTES] == 0).all()
 
 
 def test_topk_clustered_winners():
@@ -385,6 +385,63 @@ def test_mla_shapes_holes_and_empty_rows(Hm, Dl, dtype, W):
     tok = synth.random_token_ids(Q, W, [T, T], row_seq.tolist(), seed=W, hole_frac=0.2).numpy()
     tok[2, :] = -1                       # a row with nothing selected
     check_mla(q_lat, kv, row_seq, tok, Dl ** -0.5, dtype)
+
+
+@pytest.mark.parametrize("W", [1000, 5000, 16384])
+def test_mla_split_merge_levels(W):
+    # 16, 79 and 256 id slices per row, up to the largest W the entry point
+    # accepts: the merge of the slices' partials in batches with a running
+    # maximum
+    rng = np.random.default_rng(W)
+    B, T, Q, Hm = 2, 20000, 2, 64
+    q_lat = torch.from_numpy(rng.standard_normal((Q, Hm, 512)).astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(rng.standard_normal((B, T, 512)).astype(np.float32)).to(torch.bfloat16)
+    row_seq = np.array([1, 0], np.int32)
+    tok = synth.random_token_ids(Q, W, [T, T], row_seq.tolist(), seed=W, hole_frac=0.1).numpy()
+    check_mla(q_lat, kv, row_seq, tok, 512 ** -0.5, torch.bfloat16)
+
+
+def test_mla_one_dominant_token_per_row():
+    # every head of row r puts its softmax mass on one token, in a different id
+    # slice per row: the merge weights of the slices must carry it
+    # (q is aligned with that token's row, so the outputs keep the magnitude of
+    # a kv row and the bf16 bound still applies)
+    rng = np.random.default_rng(5)
+    B, T, Q, Hm, W = 1, 8192, 4, 32, 2048
+    kv = rng.standard_normal((B, T, 512)).astype(np.float32)
+    q = 0.1 * rng.standard_normal((Q, Hm, 512)).astype(np.float32)
+    tok = synth.random_token_ids(Q, W, [T], [0] * Q, seed=77).numpy()
+    for r, c in enumerate([0, 700, 1337, W - 1]):
+        row = kv[0, tok[r, c]]
+        q[r] += 40.0 * np.sqrt(512) * row / (row @ row)   # logit of that token: 40
+    o = check_mla(torch.from_numpy(q).to(torch.bfloat16), torch.from_numpy(kv).to(torch.bfloat16), [0] * Q, tok,
+                  512 ** -0.5, torch.bfloat16)
+    for r, c in enumerate([0, 700, 1337, W - 1]):
+        assert np.abs(o[r] - kv[0, tok[r, c]][None, :]).max() <= 2e-2
+
+
+def test_mla_workspace_reuse_across_calls_and_shapes():
+    # one workspace for successive calls of different shapes: partials of one
+    # call must not leak into the next; outputs start as NaN so that a merge
+    # that never ran shows
+    shapes = [(4, 64, 2048), (2, 128, 5000), (3, 16, 300), (4, 64, 2048), (1, 64, 16384), (130, 32, 200)]
+    need = max(ops().dsa_sparse_mla_workspace_bytes(Q, Hm, 512, W, ops().DSA_BF16) for Q, Hm, W in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    B, T = 2, 20000
+    for i, (Q, Hm, W) in enumerate(shapes):
+        rng = np.random.default_rng(40 + i)
+        q_lat = torch.from_numpy(rng.standard_normal((Q, Hm, 512)).astype(np.float32)).to(torch.bfloat16)
+        kv = torch.from_numpy(rng.standard_normal((B, T, 512)).astype(np.float32)).to(torch.bfloat16)
+        row_seq = (np.arange(Q) % B).astype(np.int32)
+        tok = synth.random_token_ids(Q, W, [T, T], row_seq.tolist(), seed=i, hole_frac=0.1).numpy()
+        out = torch.full((Q, Hm, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        o, lse = ops().dsa_sparse_mla_decode(dev(q_lat), dev(kv), dev(torch.from_numpy(row_seq)),
+                                             dev(torch.from_numpy(tok)), 512 ** -0.5, out=out, workspace=ws)
+        ref_o, ref_l = O.sparse_mla_decode(q_lat, kv, row_seq, tok, 512 ** -0.5)
+        g = o.float().cpu().numpy()
+        assert np.isfinite(g).all()
+        assert np.abs(g - ref_o).max() <= 2e-2
+        assert np.abs(lse.cpu().numpy() - ref_l).max() <= 2e-3 * np.abs(ref_l).max()
 
 
 def test_mla_permutation_invariant():
