@@ -297,7 +297,7 @@ def main() -> int:
         "tokens_per_s": round(steps_per_s * Q, 1),
         "stages_us": stages_us,
         "host_issue_us_per_step": round(host_issue_us, 2),
-        "roofline": {"bound": "hbm", "kernel": "index_scores_ring", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "index_scores_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "launch_us": round(score_us_mean, 3),
                      "algorithmic_bytes": bytes_per_launch},

@@ -115,51 +115,95 @@ __device__ __forceinline__ void stage_row_store(const RowIn& in, uint16_t (*ghi)
   }
 }
 
+// Sum of v over the four lanes (kg, ln), kg = 0..3, in every lane: the lane
+// swaps of 16- and 32-lane rows (same register as both operands: the two
+// results hold the value of the partner rows), no LDS.
+__device__ __forceinline__ float sum_lane_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // A tile's contribution: LayerNorm statistics on the matrix cores, the folded
 // head dots, relu, head weights and the sum over the lane's heads and the
 // wave's four lane groups.  Returns the score of pool (lane & 15) (in all lanes).
+// cQs = scale * QB, so scale * (r * dot + QB) = (scale * r) * dot + cQs (scale
+// > 0 is not required: relu is applied to the product).  diag_addr is the
+// byte address for ds_bpermute of the lane holding the Gram diagonal of pool
+// (lane & 15): 4 * (16 * ((lane & 15) >> 2) + (lane & 15)).
+// The matrix-core half of a tile: folded head dots, sum_c x_c (ones operand)
+// and the Gram block <x_m, x_n>.
 template <int NH>
-__device__ __forceinline__ float tile_score(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
-                                            const bf16x8 (&alo)[NH][4], const float (&cQ)[NH][4],
-                                            const float (&cW)[NH][4], float scale, float eps, int ln) {
+struct TileAcc {
+  f32x4 acc[NH], sacc, gacc;
+};
+
+template <int NH>
+__device__ __forceinline__ TileAcc<NH> tile_mfma(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
+                                                 const bf16x8 (&alo)[NH][4]) {
   const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-  f32x4 acc[NH];
+  TileAcc<NH> t;
 #pragma unroll
-  for (int mb = 0; mb < NH; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, gacc = {0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < NH; ++mb) t.acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  t.sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  t.gacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bf16x8 bx = as_bf16x8(x[i]);
 #pragma unroll
     for (int mb = 0; mb < NH; ++mb) {
-      acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
-      acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
+      t.acc[mb] = mfma16x16x32(ahi[mb][i], bx, t.acc[mb]);
+      t.acc[mb] = mfma16x16x32(alo[mb][i], bx, t.acc[mb]);
     }
-    sacc = mfma16x16x32(ones, bx, sacc);   // every row: sum_c x_c of pool (lane & 15)
-    gacc = mfma16x16x32(bx, bx, gacc);     // Gram block: <x_m, x_n>
+    t.sacc = mfma16x16x32(ones, bx, t.sacc);  // every row: sum_c x_c of pool (lane & 15)
+    t.gacc = mfma16x16x32(bx, bx, t.gacc);    // Gram block: <x_m, x_n>
   }
-  // diagonal <x_n, x_n> sits in lane 16*(n >> 2) + n, register n & 3
+  return t;
+}
+
+// The vector half: LayerNorm statistics, relu, head weights and the sum over
+// the lane's heads and the wave's four lane groups.
+template <int NH>
+__device__ __forceinline__ float tile_epilogue(const TileAcc<NH>& t, const float (&cQs)[NH][4],
+                                               const float (&cW)[NH][4], float scale, float eps, int ln,
+                                               int diag_addr) {
+  const f32x4 (&acc)[NH] = t.acc;
+  const f32x4 sacc = t.sacc, gacc = t.gacc;
+  // diagonal <x_n, x_n> sits in lane 16*(n >> 2) + n, register n & 3 (a
+  // branch-free pick of register ln & 3, then one lane permute)
   const int jd = ln & 3;
-  const float dg = jd == 0 ? gacc[0] : (jd == 1 ? gacc[1] : (jd == 2 ? gacc[2] : gacc[3]));
-  const float sumsq = __shfl(dg, 16 * (ln >> 2) + ln, kWave);
+  float dg = gacc[0];
+  dg = jd == 1 ? gacc[1] : dg;
+  dg = jd == 2 ? gacc[2] : dg;
+  dg = jd == 3 ? gacc[3] : dg;
+  const float sumsq = __int_as_float(__builtin_amdgcn_ds_bpermute(diag_addr, __float_as_int(dg)));
   const float mu = sacc[0] * (1.0f / kIsD);
   const float var = fmaxf(sumsq * (1.0f / kIsD) - mu * mu, 0.f);
-  const float rs = 1.0f / sqrtf(var + eps);
+  const float rs = scale * __builtin_amdgcn_rsqf(var + eps);  // v_rsq_f32: 1 ulp
   float part = 0.f;
 #pragma unroll
   for (int mb = 0; mb < NH; ++mb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, scale * fmaf(rs, acc[mb][j], cQ[mb][j])), part);
-  part += __shfl_xor(part, 16, kWave);
-  part += __shfl_xor(part, 32, kWave);
-  return part;
+    for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, fmaf(rs, acc[mb][j], cQs[mb][j])), part);
+  return sum_lane_groups(part);
 }
 
 template <int NH>
+__device__ __forceinline__ float tile_score(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
+                                            const bf16x8 (&alo)[NH][4], const float (&cQs)[NH][4],
+                                            const float (&cW)[NH][4], float scale, float eps, int ln,
+                                            int diag_addr) {
+  return tile_epilogue<NH>(tile_mfma<NH>(x, ahi, alo), cQs, cW, scale, eps, ln, diag_addr);
+}
+
+// A lane's operands for tile_score: g' hi/lo of its 16-head blocks, scale * QB
+// and w of the heads whose results it receives.
+template <int NH>
 __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], const uint16_t (*glo)[kIsLd],
-                                              const float* QB, const float* Wsh, int kg, int ln,
+                                              const float* QB, const float* Wsh, int kg, int ln, float scale,
                                               bf16x8 (&ahi)[NH][4], bf16x8 (&alo)[NH][4],
-                                              float (&cQ)[NH][4], float (&cW)[NH][4]) {
+                                              float (&cQs)[NH][4], float (&cW)[NH][4]) {
 #pragma unroll
   for (int mb = 0; mb < NH; ++mb) {
 #pragma unroll
@@ -169,7 +213,7 @@ __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], cons
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      cQ[mb][j] = QB[mb * 16 + 4 * kg + j];
+      cQs[mb][j] = scale * QB[mb * 16 + 4 * kg + j];
       cW[mb][j] = Wsh[mb * 16 + 4 * kg + j];
     }
   }
@@ -182,10 +226,10 @@ __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], cons
 // loads per lane covers 1 KiB of contiguous memory and lands directly in the
 // matrix-core operand layout; keys are read non-temporally (each byte is used
 // once).  The row's folded LayerNorm operands are staged once in LDS (8
-// threads per head) while the first ring of keys is in flight.  The candidate
-// test of the workgroup's pools is prepared in LDS from coalesced loads of
-// pool_start / pool_valid (first token if valid, else INT_MAX), and the scores
-// are gathered in LDS and written with coalesced stores.
+// threads per head) while the first ring of keys is in flight.  The scores
+// are gathered in LDS and written with coalesced stores; the candidate test
+// is applied there, from pool_start / pool_valid loaded (coalesced) at the
+// start and held in registers, so the metadata never delays the first tile.
 constexpr int kStreamRing = 4;           // tiles in flight per wave
 constexpr int kTileElems = 16 * kIsD;    // 4 KiB of bf16 keys
 
@@ -207,10 +251,11 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ uint16_t ghi[H][kIsLd];
   __shared__ uint16_t glo[H][kIsLd];
   __shared__ float sQB[H], sW[H];
-  __shared__ int sStart[kPools];  // first token of a valid pool, INT_MAX otherwise
   __shared__ float sOut[kPools];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
+  const int diag_addr = 4 * (16 * (ln >> 2) + ln);
   const int r = blockIdx.y;
   const int b = row_seq[r];
   const int pos = row_pos[r];
@@ -221,7 +266,8 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const size_t seq0 = size_t(ok ? b : 0) * P_max;
   const uint16_t* kseq = k_pool + size_t(ok ? b : 0) * P_tiles * kTileElems;
 
-  // operand and metadata loads first, then the first ring of key tiles
+  // operand loads first, then the metadata of the pools this thread stores
+  // (used only at the end), then the first ring of key tiles
   RowIn rin;
   if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
   int st[MP];
@@ -250,35 +296,42 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   // whole grid would wait for its operands before any key is requested)
   __builtin_amdgcn_sched_barrier(0);
   if (tid < H * 8) stage_row_store(rin, ghi, glo, sQB, sW, tid);
-#pragma unroll
-  for (int u = 0; u < MP; ++u) {
-    const int lp = u * kIsThreads + tid;
-    const int p = p0 + lp;
-    if (lp < kPools) sStart[lp] = (ok && p < P_max && vl[u] != 0) ? st[u] : INT_MAX;
-  }
   __syncthreads();
   bf16x8 ahi[NH][4], alo[NH][4];
   float cQ[NH][4], cW[NH][4];
-  load_operands<NH>(ghi, glo, sQB, sW, kg, ln, ahi, alo, cQ, cW);
-  const int last_ok = pos - (kp - 1);  // candidate iff its start <= last_ok
+  load_operands<NH>(ghi, glo, sQB, sW, kg, ln, scale, ahi, alo, cQ, cW);
+  // software pipeline: tile j+1's matrix-core work is issued before tile j's
+  // vector epilogue, which then runs while the matrix cores are busy; a ring
+  // slot is refilled once its tile's MFMAs are issued
+  TileAcc<NH> cur = tile_mfma<NH>(xb[0], ahi, alo);
+  if (R < NT) issue(0, R);
 #pragma unroll
   for (int j0 = 0; j0 < NT; j0 += R) {
 #pragma unroll
     for (int s = 0; s < R; ++s) {
       const int j = j0 + s;
-      const float sc = tile_score<NH>(xb[s], ahi, alo, cQ, cW, scale, eps, ln);
-      const int lp = (wave + kIsWaves * j) * 16 + ln;  // pool within the workgroup
-      if (kg == 0) sOut[lp] = sStart[lp] <= last_ok ? sc : -INFINITY;
-      issue(s, j + R);
+      TileAcc<NH> nxt;
+      if (j + 1 < NT) {
+        const int s1 = (s + 1) % R;
+        nxt = tile_mfma<NH>(xb[s1], ahi, alo);
+        if (j + 1 + R < NT) issue(s1, j + 1 + R);  // resolved at compile time (unrolled)
+      }
+      const float sc = tile_epilogue<NH>(cur, cQ, cW, scale, eps, ln, diag_addr);
+      // the four lane groups hold the same sum: all write it (no branch)
+      sOut[(wave + kIsWaves * j) * 16 + ln] = sc;
+      if (j + 1 < NT) cur = nxt;
     }
   }
   __syncthreads();
+  // candidate test (valid pool whose last token is at or before the row's
+  // position) and coalesced stores
+  const int last_ok = pos - (kp - 1);
   float* srow = scores + size_t(r) * P_max;
 #pragma unroll
   for (int u = 0; u < MP; ++u) {
     const int lp = u * kIsThreads + tid;
     const int p = p0 + lp;
-    if (lp < kPools && p < P_max) srow[p] = sOut[lp];
+    if (lp < kPools && p < P_max) srow[p] = (ok && vl[u] != 0 && st[u] <= last_ok) ? sOut[lp] : -INFINITY;
   }
 }
 
@@ -295,8 +348,10 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   __shared__ uint16_t glo[RPB][H][kIsLd];
   __shared__ float sQB[RPB][H], sW[RPB][H];
   __shared__ int s_pos[RPB], s_seq[RPB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
+  const int diag_addr = 4 * (16 * (ln >> 2) + ln);
   const int r_begin = blockIdx.y * rows_per_group;
   const int r_end = min(Q, r_begin + rows_per_group);
   const int p_wave = blockIdx.x * (kIsWaves * kTiles * 16) + wave * (kTiles * 16);
@@ -350,10 +405,10 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
       }
       bf16x8 ahi[NH][4], alo[NH][4];
       float cQ[NH][4], cW[NH][4];
-      load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, ahi, alo, cQ, cW);
+      load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, scale, ahi, alo, cQ, cW);
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
-        const float sc = tile_score<NH>(xk[t], ahi, alo, cQ, cW, scale, eps, ln);
+        const float sc = tile_score<NH>(xk[t], ahi, alo, cQ, cW, scale, eps, ln, diag_addr);
         const int p = p_wave + t * 16 + ln;
         if (kg == 0 && p < P_max) {
           const bool cand = ok && pvk[t] != 0 && psk[t] + kp - 1 <= pos;
@@ -442,10 +497,11 @@ static IsPlan is_plan(int Q, int P_max) {
   IsPlan pl{false, 8, 1};
   const long ntile = (P_max + 15) / 16;
   if (Q <= 64) {
-    // decode: 16 tiles per wave (1024 pools per workgroup) while that gives
-    // >= 256 workgroups (one per CU: fewer key bytes in flight stream better
-    // than more), else 4 tiles, else 1
-    if (long(Q) * ((ntile + 63) / 64) >= 256) pl.tw = 16;
+    // decode: 8 tiles per wave (512 pools per workgroup, two workgroups per
+    // CU) while that gives >= 256 workgroups, else 4 tiles, else 1.  Measured
+    // at 4 x 65536 pools: 8 tiles with a 4-deep ring beat 16 tiles (4- or
+    // 6-deep) and deeper rings at 8 (more key bytes in flight stream worse)
+    if (long(Q) * ((ntile + 31) / 32) >= 256) pl.tw = 8;
     else if (long(Q) * ((ntile + 15) / 16) >= 128) pl.tw = 4;
     else pl.tw = 1;
     return pl;
@@ -488,11 +544,11 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
                      scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,   \
                      row_seq, row_pos, B, P_max, kpool, scores)
       if (H == 32) {
-        if (pl.tw == 16) DSA_IS_STREAM(2, 16);
+        if (pl.tw == 8) DSA_IS_STREAM(2, 8);
         else if (pl.tw == 4) DSA_IS_STREAM(2, 4);
         else DSA_IS_STREAM(2, 1);
       } else {
-        if (pl.tw == 16) DSA_IS_STREAM(1, 16);
+        if (pl.tw == 8) DSA_IS_STREAM(1, 8);
         else if (pl.tw == 4) DSA_IS_STREAM(1, 4);
         else DSA_IS_STREAM(1, 1);
       }

@@ -10,16 +10,21 @@
 // MFMA path (bf16, Dl = 512, Hm a multiple of 16).  A workgroup handles one
 // row, one group of 16 heads and a contiguous slice ("split") of 64 ids of the
 // row's list, with 4 waves:
-//   - wave w gathers the latent rows of ids 16w .. 16w+15 straight into LDS
-//     (one 1 KiB row per load instruction, 16 bytes per lane; the row swizzle
-//     is applied through the source addresses);
-//   - it forms the logits of those 16 tokens for the 16 heads over the full
-//     latent width on the matrix cores (kv rows x q^T), so no partial logits
-//     cross waves: only the per-head max and sum do, through LDS;
-//   - the probabilities P (bf16) are shared through LDS, and wave w
-//     accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over all 64
-//     tokens, reading kv^T with the transposing LDS reads.
-// The swizzle makes both LDS read patterns bank-conflict free.  68 KiB of LDS
+//   - the 16 heads' q_lat (16 KiB) and the 64 listed latent rows (64 KiB) are
+//     moved straight into LDS by the load-to-LDS path, one 1 KiB row per load
+//     instruction (16 bytes per lane, the row swizzle applied through the
+//     source addresses); wave w gathers the rows of ids 16w .. 16w+15;
+//   - wave w forms the logits of its 16 tokens for the 16 heads over the full
+//     latent width on the matrix cores (kv rows x q^T, both from LDS), so no
+//     partial logits cross waves;
+//   - softmax: each wave takes its own maximum per head and forms P relative
+//     to it; P (bf16) and the per-wave maxima and sums go through LDS (in the
+//     space q held), and the value contraction scales the P operand by
+//     2^(m_wave - m_row): no barrier waits for a row maximum before P is
+//     formed (one barrier frees q's space, one publishes P);
+//   - wave w accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over
+//     all 64 tokens, reading kv^T with the transposing LDS reads.
+// The swizzle makes both LDS read patterns bank-conflict free.  80 KiB of LDS
 // keeps two workgroups per CU.  The head groups of one (row, split) read the
 // same latent rows; their workgroup ids are spaced by a multiple of 8 so that
 // they share an XCD and its L2.  Splits write normalised partial outputs,

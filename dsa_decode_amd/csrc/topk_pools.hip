@@ -10,19 +10,27 @@
 // distinct, so "the K largest keys" is the wanted set and "keys descending"
 // the wanted order.
 //
-// Selection is a radix select inside one workgroup over keys held in
-// registers, latency first (a decode row has only a few workgroups in flight):
-//  * the bits common to the largest and smallest hi are skipped, then 11-bit
-//    digits of hi are histogrammed in LDS until the bin holding the K-th key is
-//    exactly consumed (two passes for distinct scores);
-//  * the histogram is scanned by one wave with DPP prefix sums and ballots;
-//  * only when the K-th score is tied do keys go further: by position (a
-//    ballot rank) when they come straight from the scores, by the lo digits
-//    when they come from chunk winners.
-// Long rows are split into chunks whose K largest keys go to a workspace; a
-// merge launch selects the K largest of the chunk winners (the K largest of a
-// union are among the K largest of each part, so this is exact).  The final K
-// keys are sorted with a bitonic network and written as pool ids, -1 padded.
+// Selection runs inside one workgroup over keys held in registers, latency
+// first (a decode row has only a few workgroups in flight):
+//  * a first pass histograms the candidates into 2048 bins of equal width
+//    between the smallest and the largest score (the map is monotone, so the
+//    bins keep the key order and tied scores share a bin); one wave scans the
+//    histogram with DPP prefix sums and finds the bin of the K-th key;
+//  * when every bin from that one up holds at most 64 keys, those keys are
+//    scattered bin by bin into LDS and each is placed directly: output
+//    position = keys in higher bins + its rank among its bin mates;
+//  * otherwise (a large tie, or scores spread too widely for equal bins) a
+//    radix select on 11-bit digits of the key bits below those common to all
+//    candidates finds the K-th key; a tie at the K-th score is broken by
+//    position (ballot ranks) for raw scores and by the lo bits for chunk
+//    winners; the selected keys are then sorted by a bitonic network.
+// Long rows are split into chunks whose K largest keys (sorted) go to a
+// workspace; the K largest of the chunk winners are the row's (the K largest
+// of a union are among the K largest of each part, so this is exact).  For
+// the decode shapes this runs in one launch: the chunk workgroups publish
+// their winners and the last one to finish merges them, first from the heads
+// of the sorted lists (exact whenever no list can hold winners past its head)
+// and else from the full lists.  Otherwise a second launch merges.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
