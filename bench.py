@@ -1,7 +1,8 @@
 """DSA decode step benchmark on one MI355X.
 
 A step is one decode token for every sequence of the batch through the whole
-hot path: dsa_index_scores -> dsa_topk_pools -> dsa_expand_selection ->
+hot path: dsa_index_scores -> dsa_topk_pools_expand (the top-k selection and
+its expansion to token ids in one launch: both outputs are written) ->
 dsa_sparse_mla_decode, on the long-context workload (4 sequences of 262144
 tokens, kpool 4 -> 65536 pools each, 32 index heads x 128, select_k 512 pools =
 2048 tokens, 64-head absorbed MLA over a 512-wide latent, bf16).  The pooled-key
@@ -10,7 +11,7 @@ cache comes from an untimed dsa_kpool_compress over synthetic tokens.
 Inputs are resident in HBM before the timed region.  Eight replicas of the
 pool cache and of the latent cache (about 8.5 GiB) rotate from step to step, so
 the 256 MB last-level cache cannot serve a step from the previous one.  Each
-step launches the four stages from argument tuples bound once per replica
+step launches the three calls from argument tuples bound once per replica
 (``--mode graph`` replays HIP graphs captured per replica instead); HIP events
 on the launch stream bracket the score kernel of every timed step, which gives
 that kernel's per-launch time for the roofline line.  They are timing-only
@@ -95,6 +96,8 @@ def _parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 64 MiB device copy first (a known-size kernel for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-topk-expand", action="store_true",
+                    help="run dsa_topk_pools and dsa_expand_selection as two calls instead of the fused call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
     return ap.parse_args()
 
@@ -191,8 +194,11 @@ def main() -> int:
             bound.append(dict(
                 scores=ops.bind_index_scores(q, w, ip["scale"], r["k_pool"], r["pool_start"], r["pool_valid"],
                                              gamma, beta, ip["eps"], row_seq, row_pos, wl.kp, r["scores"]),
-                rest=[ops.bind_topk_pools(r["scores"], K, r["ids"], tk_ws),
-                      ops.bind_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, r["tok"]),
+                rest=([ops.bind_topk_pools(r["scores"], K, r["ids"], tk_ws),
+                       ops.bind_expand_selection(r["ids"], row_seq, r["pool_start"], wl.kp, r["tok"])]
+                      if args.split_topk_expand else
+                      [ops.bind_topk_pools_expand(r["scores"], K, r["ids"], row_seq, r["pool_start"], wl.kp,
+                                                  r["tok"], tk_ws)]) + [
                       ops.bind_sparse_mla_decode(q_lat, r["kv"], row_seq, r["tok"], mi["sm_scale"], r["out"],
                                                  r["lse"], mla_ws)]))
 
@@ -251,13 +257,14 @@ def main() -> int:
     score_us_mean = float(np.mean(score_us))
 
     # per-stage breakdown (separate instrumented pass, eager launches, events around each stage)
-    stage_names = ["index_scores", "topk_pools", "expand_selection", "sparse_mla_decode"]
+    stage_names = (["index_scores", "topk_pools", "expand_selection", "sparse_mla_decode"] if args.split_topk_expand
+                   else ["index_scores", "topk_pools_expand", "sparse_mla_decode"])
     stage_t = {n: [] for n in stage_names}
     with torch.cuda.stream(stream):
         for i in range(min(64, args.steps)):
             b = bound[i % REPLICAS]
             calls = [b["scores"]] + b["rest"]
-            e = TimingEvents(5)
+            e = TimingEvents(len(stage_names) + 1)
             e.record(0, stream.cuda_stream)
             for k, c in enumerate(calls):
                 c()

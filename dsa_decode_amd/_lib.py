@@ -29,6 +29,8 @@ SIGNATURES = {
                                c_void_p]),
     "dsa_expand_selection": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_int,
                                      c_int, c_void_p, c_int, c_void_p]),
+    "dsa_topk_pools_expand": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int,
+                                      c_int, c_int, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "dsa_sparse_mla_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "dsa_sparse_mla_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p,

@@ -384,6 +384,31 @@ __device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Selection followed by expansion (dsa_topk_pools_expand): the thread that
+// places a row's j-th pool id also writes that pool's token ids, with the
+// rules of dsa_expand_selection (kpool consecutive ids from pool_start, -1 for
+// an absent or nonexistent pool); the columns past K*kpool are written -1.
+struct ExpandArgs {
+  const int32_t* row_seq;
+  const int32_t* pool_start;
+  int B, P_max, kp;
+  int32_t* token_ids;  // nullptr: no expansion
+  int W;
+};
+
+__device__ __forceinline__ void expand_one(int row, int j, int32_t pid, const ExpandArgs& ex) {
+  const int b = ex.row_seq[row];
+  int32_t ps = -1;
+  if (pid >= 0 && pid < ex.P_max && b >= 0 && b < ex.B) ps = ex.pool_start[size_t(b) * ex.P_max + pid];
+  int32_t* t = ex.token_ids + size_t(row) * ex.W + size_t(j) * ex.kp;
+  for (int sl = 0; sl < ex.kp; ++sl) t[sl] = ps >= 0 ? ps + sl : -1;
+}
+
+template <int NT>
+__device__ __forceinline__ void expand_pad(int row, int K, const ExpandArgs& ex) {
+  for (int col = K * ex.kp + int(threadIdx.x); col < ex.W; col += NT) ex.token_ids[size_t(row) * ex.W + col] = -1;
+}
+
 // One workgroup's selection: chunk c of row `row` (FROM_SCORES: pools c*chunk
 // .. of the scores; otherwise the nsplit_in chunk winner lists of the row) ->
 // its K largest keys, written to chunk slot c of keys_out (partial) or sorted
@@ -391,7 +416,8 @@ __device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
 template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
 __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int nchunk, const float* __restrict__ scores,
                            const uint64_t* __restrict__ keys_in, int P, int chunk, int nsplit_in, int K,
-                           uint64_t* __restrict__ keys_out, int32_t* __restrict__ pool_ids) {
+                           uint64_t* __restrict__ keys_out, int32_t* __restrict__ pool_ids,
+                           const ExpandArgs& ex) {
   static_assert(KPT <= 32, "selection masks are 32-bit");
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t hi[KPT];
@@ -497,8 +523,12 @@ __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int
                    (i + 3 < n && a3 > me ? 1u : 0u);
           }
           if (pos < uint32_t(K)) {
-            if constexpr (FINAL) dst[pos] = int32_t(0xffffffffu - uint32_t(me));
-            else publish(out + pos, me);
+            if constexpr (FINAL) {
+              dst[pos] = int32_t(0xffffffffu - uint32_t(me));
+              if (ex.token_ids) expand_one(row, int(pos), int32_t(0xffffffffu - uint32_t(me)), ex);
+            } else {
+              publish(out + pos, me);
+            }
           }
         }
         return;
@@ -556,8 +586,13 @@ __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int
   uint64_t* out = FINAL ? nullptr : keys_out + (size_t(row) * nchunk + c) * K;
   int32_t* dst = FINAL ? pool_ids + size_t(row) * K : nullptr;
   auto emit = [&](int e, uint64_t k) {
-    if constexpr (FINAL) dst[e] = (e < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
-    else publish(out + e, e < int(nsel) ? k : 0);
+    if constexpr (FINAL) {
+      const int32_t pid = (e < int(nsel) && k != 0) ? int32_t(0xffffffffu - uint32_t(k)) : -1;
+      dst[e] = pid;
+      if (ex.token_ids) expand_one(row, e, pid, ex);
+    } else {
+      publish(out + e, e < int(nsel) ? k : 0);
+    }
   };
   if (kp2 == 512) {
     uint64_t a0 = 0, a1 = 0;
@@ -583,7 +618,8 @@ __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int
 // (the caller then merges the full lists).
 template <int NT, int KPT>
 __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, int m, int K,
-                                            const uint64_t* __restrict__ keys, int32_t* __restrict__ pool_ids) {
+                                            const uint64_t* __restrict__ keys, int32_t* __restrict__ pool_ids,
+                                            const ExpandArgs& ex) {
   static_assert(KPT <= 32, "selection masks are 32-bit");
   const int tid = threadIdx.x;
   const int n = S * m;
@@ -649,7 +685,10 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
       pos += (a0 > me ? 1u : 0u) + (i + 1 < nb && a1 > me ? 1u : 0u) + (i + 2 < nb && a2 > me ? 1u : 0u) +
              (i + 3 < nb && a3 > me ? 1u : 0u);
     }
-    if (pos < uint32_t(K)) dst[pos] = int32_t(0xffffffffu - uint32_t(me));
+    if (pos < uint32_t(K)) {
+      dst[pos] = int32_t(0xffffffffu - uint32_t(me));
+      if (ex.token_ids) expand_one(row, int(pos), int32_t(0xffffffffu - uint32_t(me)), ex);
+    }
   }
   return true;
 }
@@ -659,10 +698,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   const uint64_t* __restrict__ keys_in,
                                                   int P, int chunk, int nsplit_in, int K,
                                                   uint64_t* __restrict__ keys_out,
-                                                  int32_t* __restrict__ pool_ids) {
+                                                  int32_t* __restrict__ pool_ids, ExpandArgs ex) {
   __shared__ TkShared<NT> sh;
+  if constexpr (FINAL)
+    if (ex.token_ids) expand_pad<NT>(blockIdx.y, K, ex);
   topk_block<NT, KPT, FROM_SCORES, FINAL>(sh, blockIdx.y, blockIdx.x, gridDim.x, scores, keys_in, P, chunk,
-                                          nsplit_in, K, keys_out, pool_ids);
+                                          nsplit_in, K, keys_out, pool_ids, ex);
 }
 
 // Split rows in one launch: workgroup (c, row) selects chunk c's K winners,
@@ -675,10 +716,11 @@ template <int NT, int KPT1, int KPTH, int KPT2>
 __global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict__ scores, int P, int chunk,
                                                         int nsplit, int K, int m, uint64_t* __restrict__ keys,
                                                         uint32_t* __restrict__ counters,
-                                                        int32_t* __restrict__ pool_ids) {
+                                                        int32_t* __restrict__ pool_ids, ExpandArgs ex) {
   __shared__ TkShared<NT> sh;
   const int row = blockIdx.y;
-  topk_block<NT, KPT1, true, false>(sh, row, blockIdx.x, nsplit, scores, nullptr, P, chunk, 0, K, keys, nullptr);
+  topk_block<NT, KPT1, true, false>(sh, row, blockIdx.x, nsplit, scores, nullptr, P, chunk, 0, K, keys, nullptr,
+                                    ExpandArgs{});
   // every thread's winner stores are complete before the row's counter moves
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -689,9 +731,10 @@ __global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict_
   // the last ticket: every chunk's winners are published; reset the counter
   // for the next call and merge
   if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (m < K && merge_heads<NT, KPTH>(sh, row, nsplit, m, K, keys, pool_ids)) return;
+  if (ex.token_ids) expand_pad<NT>(row, K, ex);
+  if (m < K && merge_heads<NT, KPTH>(sh, row, nsplit, m, K, keys, pool_ids, ex)) return;
   __syncthreads();
-  topk_block<NT, KPT2, false, true>(sh, row, 0, 1, nullptr, keys, P, 0, nsplit, K, nullptr, pool_ids);
+  topk_block<NT, KPT2, false, true>(sh, row, 0, 1, nullptr, keys, P, 0, nsplit, K, nullptr, pool_ids, ex);
 }
 
 struct TkPlan {
@@ -764,10 +807,11 @@ static_assert(DSA_TOPK_COUNTER_BYTES >= 65535 * sizeof(uint32_t), "one counter p
 
 template <int NT, bool FROM_SCORES, bool FINAL>
 static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, const uint64_t* keys_in,
-                      int P, int chunk, int nsplit_in, int K, uint64_t* keys_out, int32_t* pool_ids) {
+                      int P, int chunk, int nsplit_in, int K, uint64_t* keys_out, int32_t* pool_ids,
+                      const ExpandArgs& ex) {
 #define DSA_TK(KPT)                                                                                \
   hipLaunchKernelGGL((topk_kernel<NT, KPT, FROM_SCORES, FINAL>), grid, dim3(NT), 0, s, scores,    \
-                     keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids)
+                     keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex)
   switch (kpt) {
     case 1: DSA_TK(1); break;
     case 2: DSA_TK(2); break;
@@ -782,13 +826,13 @@ static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, co
 template <bool FROM_SCORES, bool FINAL>
 static void launch_tk_nt(int nt, int kpt, dim3 grid, hipStream_t s, const float* scores,
                          const uint64_t* keys_in, int P, int chunk, int nsplit_in, int K,
-                         uint64_t* keys_out, int32_t* pool_ids) {
+                         uint64_t* keys_out, int32_t* pool_ids, const ExpandArgs& ex) {
   if (nt == 256)
-    launch_tk<256, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+    launch_tk<256, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
   else if (nt == 512)
-    launch_tk<512, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+    launch_tk<512, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
   else
-    launch_tk<1024, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids);
+    launch_tk<1024, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
 }
 
 }  // namespace dsa
@@ -801,8 +845,10 @@ extern "C" size_t dsa_topk_workspace_bytes(int Q, int P, int K) {
   return pl.nsplit > 1 ? DSA_TOPK_COUNTER_BYTES + size_t(Q) * pl.nsplit * K * sizeof(uint64_t) : 0;
 }
 
-extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+// The selection launches shared by dsa_topk_pools and dsa_topk_pools_expand
+// (ex.token_ids == nullptr: selection only).
+static int topk_run(const float* scores, int Q, int P, int K, int32_t* pool_ids, void* workspace,
+                    size_t workspace_bytes, hipStream_t s, const ExpandArgs& ex) {
   if (!scores || !pool_ids) return DSA_ERR_NULL;
   if (Q <= 0 || P <= 0 || K <= 0) return DSA_ERR_SHAPE;
   if (K > DSA_MAX_SELECT_K) return DSA_ERR_UNSUPPORTED;
@@ -812,10 +858,9 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
   if (pl.nsplit > kTkMaxSplit || pl.kpt1 > 32 || pl.kpt2 > 32) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa_topk_workspace_bytes(Q, P, K);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
   dim3 g1(pl.nsplit, Q);
   if (pl.nsplit == 1) {
-    launch_tk_nt<true, true>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids);
+    launch_tk_nt<true, true>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, nullptr, pool_ids, ex);
     return launch_status();
   }
   uint32_t* counters = static_cast<uint32_t*>(workspace);
@@ -823,7 +868,7 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
   if (pl.fused) {
 #define DSA_TKF(KH, KM)                                                                                  \
   hipLaunchKernelGGL((topk_split_kernel<kFusedThreads, kFusedKpt, KH, KM>), g1, dim3(kFusedThreads), 0, s, \
-                     scores, P, pl.chunk, pl.nsplit, K, pl.head, ws, counters, pool_ids)
+                     scores, P, pl.chunk, pl.nsplit, K, pl.head, ws, counters, pool_ids, ex)
 #define DSA_TKF_H(KM)       \
   if (pl.kpt_h <= 2)        \
     DSA_TKF(2, KM);         \
@@ -840,10 +885,28 @@ extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t*
 #undef DSA_TKF
     return launch_status();
   }
-  launch_tk_nt<true, false>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr);
+  const ExpandArgs none{};
+  launch_tk_nt<true, false>(pl.nt1, pl.kpt1, g1, s, scores, nullptr, P, pl.chunk, 0, K, ws, nullptr, none);
   int st = launch_status();
   if (st) return st;
   dim3 g2(1, Q);
-  launch_tk_nt<false, true>(pl.nt2, pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids);
+  launch_tk_nt<false, true>(pl.nt2, pl.kpt2, g2, s, nullptr, ws, P, 0, pl.nsplit, K, nullptr, pool_ids, ex);
   return launch_status();
+}
+
+extern "C" int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_run(scores, Q, P, K, pool_ids, workspace, workspace_bytes, as_stream(stream), ExpandArgs{});
+}
+
+extern "C" int dsa_topk_pools_expand(const float* scores, int Q, int P, int K, int32_t* pool_ids,
+                                     const int32_t* row_seq, const int32_t* pool_start, int B, int P_max,
+                                     int kpool, int32_t* token_ids, int W, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!row_seq || !pool_start || !token_ids) return DSA_ERR_NULL;
+  if (B <= 0 || P_max <= 0 || kpool <= 0 || W <= 0) return DSA_ERR_SHAPE;
+  if (kpool > DSA_MAX_KPOOL) return DSA_ERR_UNSUPPORTED;
+  if (K > 0 && long(W) < long(K) * kpool) return DSA_ERR_SHAPE;
+  const ExpandArgs ex{row_seq, pool_start, B, P_max, kpool, token_ids, W};
+  return topk_run(scores, Q, P, K, pool_ids, workspace, workspace_bytes, as_stream(stream), ex);
 }

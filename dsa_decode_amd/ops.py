@@ -110,6 +110,29 @@ def dsa_topk_pools(scores, K: int, pool_ids=None, workspace=None):
     return pool_ids
 
 
+def dsa_topk_pools_expand(scores, K: int, row_seq, pool_start, kpool: int, W: int, pool_ids=None,
+                          token_ids=None, workspace=None):
+    """dsa_topk_pools then dsa_expand_selection in one launch -> (pool_ids [Q, K],
+    token_ids [Q, W])."""
+    Q, P = scores.shape
+    B, P_max = pool_start.shape
+    if pool_ids is None:
+        pool_ids = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
+    if token_ids is None:
+        token_ids = torch.empty((Q, W), dtype=torch.int32, device=scores.device)
+    need = dsa_topk_workspace_bytes(Q, P, K)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dsa_topk_pools_expand(
+        _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
+        _dev(row_seq, "row_seq", torch.int32), _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool,
+        _dev(token_ids, "token_ids", torch.int32), W, ws_ptr, ws_bytes, _stream())
+    check("dsa_topk_pools_expand", st)
+    return pool_ids, token_ids
+
+
 def dsa_expand_selection(pool_ids, row_seq, pool_start, kpool: int, W: int, token_ids=None):
     """-> token_ids [Q, W] int32 (-1 = invalid, every column written)."""
     Q, K = pool_ids.shape
@@ -190,6 +213,16 @@ def bind_topk_pools(scores, K, pool_ids, workspace) -> BoundCall:
     Q, P = scores.shape
     return BoundCall("dsa_topk_pools", (
         _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
+
+
+def bind_topk_pools_expand(scores, K, pool_ids, row_seq, pool_start, kpool, token_ids, workspace) -> BoundCall:
+    Q, P = scores.shape
+    B, P_max = pool_start.shape
+    return BoundCall("dsa_topk_pools_expand", (
+        _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
+        _dev(row_seq, "row_seq", torch.int32), _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool,
+        _dev(token_ids, "token_ids", torch.int32), token_ids.shape[1],
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
 
 

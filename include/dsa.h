@@ -195,6 +195,23 @@ int dsa_expand_selection(const int32_t* pool_ids, int Q, int K, const int32_t* r
                          int32_t* token_ids, int W, void* stream);
 
 /*
+ * dsa_topk_pools_expand -- dsa_topk_pools followed by dsa_expand_selection, in
+ * one launch.  "Module glm5next_dsa", "Shape of the pipeline" (the selected
+ * [Q, select_k] pool ids become [Q, out_width] token ids) and "Traps carried
+ * from Slice 8" (the -1 sentinel destination fully written).
+ *
+ * Writes exactly what the two calls write: pool_ids [Q, K] as dsa_topk_pools
+ * and token_ids [Q, W] as dsa_expand_selection applied to those pool ids.  The
+ * workgroup that finishes a row's selection also expands it, so the decode
+ * path saves one launch.  Arguments, workspace (dsa_topk_workspace_bytes, with
+ * its counter block) and requirements are those of the two calls.
+ */
+int dsa_topk_pools_expand(const float* scores, int Q, int P, int K, int32_t* pool_ids,
+                          const int32_t* row_seq, const int32_t* pool_start, int B, int P_max,
+                          int kpool, int32_t* token_ids, int W, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * dsa_sparse_mla_decode -- absorbed NoPE MLA decode over the selected tokens.
  * "Module glm5next_dsa", "Shape of the pipeline" (NoPE MLA restricted to the
  * selected tokens) and "Traps carried from Slice 8" (NoPE: the rotary slice is

@@ -116,6 +116,20 @@ def test_expand_refuses_bad_arguments(lib):
     assert lib.dsa_expand_selection(FAKE, 1, 8, FAKE, FAKE, 1, 64, 9, FAKE, 72, None) == DSA_ERR_UNSUPPORTED
 
 
+def test_topk_expand_refuses_bad_arguments(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
+    call = lambda **kw: lib.dsa_topk_pools_expand(*dict(dict(
+        s=FAKE, Q=4, P=65536, K=512, ids=FAKE, rs=FAKE, ps=FAKE, B=4, P_max=65536, kp=4, tok=FAKE,
+        W=2048, ws=None, wsb=0, stream=None), **kw).values())
+    assert call(tok=None) == DSA_ERR_NULL
+    assert call(ps=None) == DSA_ERR_NULL
+    assert call(s=None) == DSA_ERR_NULL
+    assert call(W=2047) == DSA_ERR_SHAPE            # W < K * kpool
+    assert call(kp=9, W=8 * 512 * 2) == DSA_ERR_UNSUPPORTED
+    assert call(K=4096, W=4096 * 4) == DSA_ERR_UNSUPPORTED
+    assert call() == DSA_ERR_WORKSPACE              # split rows need the workspace
+
+
 def test_mla_refuses_bad_arguments_and_sizes_workspace(lib):
     from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
     call = lambda **kw: lib.dsa_sparse_mla_decode(*dict(dict(

@@ -278,6 +278,41 @@ def test_topk_workspace_reuse_across_calls_and_shapes():
         assert (ws[: ops().DSA_TOPK_COUNTER_BYTES] == 0).all()
 
 
+@pytest.mark.parametrize("Q,P,K,kp,W,ties", [
+    (4, 65536, 512, 4, 2048, 0),     # decode shape: split rows merged in one launch
+    (3, 30000, 256, 4, 1100, 64),    # split rows, forced ties, padded width
+    (2, 1000, 8, 3, 30, 0),          # one chunk per row
+    (260, 33000, 64, 4, 256, 0),     # many rows: chunk launch + merge launch
+])
+def test_topk_pools_expand_matches_oracle(Q, P, K, kp, W, ties):
+    # the fused entry point writes exactly what dsa_topk_pools then
+    # dsa_expand_selection write: pool ids bit-exact with the oracle's top-k
+    # and token ids bit-exact with the oracle's expansion of those ids, with
+    # pools that do not exist, an invalid row, rows with fewer candidates
+    # than K, and every token column written (canary fill)
+    rng = np.random.default_rng(Q * 7 + P)
+    s = synth.random_scores(Q, P, seed=Q + P + K, tie_levels=ties, neg_inf_frac=0.2).numpy()
+    s[0, : P - K // 2] = -np.inf                    # row 0: fewer candidates than K
+    B = 3
+    pool_start = (np.arange(P, dtype=np.int64) * kp + rng.integers(0, 7, size=(B, 1))).astype(np.int32)
+    pool_start[rng.random((B, P)) < 0.1] = -1       # pools that do not exist
+    row_seq = rng.integers(0, B, size=Q).astype(np.int32)
+    row_seq[Q - 1] = B                              # a row naming no sequence
+    ref_ids = O.topk_pools(s, K)
+    # the oracle expands rows of existing sequences; a row naming none gets
+    # -1 throughout (the boundary turns the precondition violation into -1)
+    ref_tok = O.expand_selection(ref_ids[:-1], row_seq[:-1], pool_start, kp, W)
+    ref_tok = np.concatenate([ref_tok, np.full((1, W), -1, np.int32)])
+    ids = torch.full((Q, K), 0x7fffffff, dtype=torch.int32, device="cuda")
+    tok = torch.full((Q, W), 0x7fffffff, dtype=torch.int32, device="cuda")
+    ops().dsa_topk_pools_expand(dev(torch.from_numpy(s)), K, dev(torch.from_numpy(row_seq)),
+                                dev(torch.from_numpy(pool_start)), kp, W, pool_ids=ids, token_ids=tok)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    got = tok.cpu().numpy()
+    assert not (got == 0x7fffffff).any(), "unwritten slots in the token-id destination"
+    np.testing.assert_array_equal(got, ref_tok)
+
+
 def test_topk_clustered_winners():
     # the merge of a split row first reads the head of each chunk's sorted
     # winner list; rows whose K winners crowd into one or a few chunks must
