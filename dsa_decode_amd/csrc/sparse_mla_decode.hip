@@ -24,7 +24,7 @@
 //     formed (one barrier frees q's space, one publishes P);
 //   - wave w accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over
 //     all 64 tokens, reading kv^T with the transposing LDS reads.
-// The swizzle makes both LDS read patterns bank-conflict free.  80 KiB of LDS
+// The swizzle spreads both LDS read patterns over the banks.  80 KiB of LDS
 // keeps two workgroups per CU.  The head groups of one (row, split) read the
 // same latent rows; their workgroup ids are spaced by a multiple of 8 so that
 // they share an XCD and its L2.  Splits write normalised partial outputs,
@@ -45,17 +45,22 @@ struct MlaShared {
   union {
     uint16_t q[16][kMlaDl];          // the 16 heads' q_lat, swizzled like the rows (16 KiB)
     struct {                         // after the logits: the softmax exchange
-      uint16_t p[16][kMlaSplit];     // P[head][token] relative to its wave's maximum, bf16
+      uint16_t p[16][kMlaSplit + 8]; // P[head][token] relative to its wave's maximum, bf16
+                                     // (rows padded to 144 B: the 16 heads' rows start in
+                                     // different banks)
       float m[16][4];                // per head: each wave's maximum (log2 domain)
       float l[16][4];                // per head: each wave's sum of P
     } x;
   } u;
 };
 
-// Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Makes the
-// logits reads (16 consecutive rows x 4 pieces) and the transposing reads
-// (rows 8g + e, g, e < 4, x 2 adjacent pieces) bank-conflict free.
-__device__ __forceinline__ int mla_swz(int t) { return (t & 11) | ((((t >> 2) ^ (t >> 4)) & 1) << 2); }
+// Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Over any 8
+// consecutive rows the swizzle takes 8 distinct values mod 8 (and over 16 rows
+// 16 distinct values), so the logits reads (one piece of 16 consecutive rows
+// per lane group) hit distinct banks; rows 8g .. 8g+3 (and 8g+4 .. 8g+7) take
+// values whose halves (v >> 1) differ, so the transposing reads (4 rows x 2
+// adjacent pieces per 16 lanes) do too.
+__device__ __forceinline__ int mla_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
