@@ -98,6 +98,7 @@ struct TkShared {
   alignas(16) uint32_t hist[kBins];
   alignas(16) uint32_t sfx[kBins];  // first pass: keys in higher bins, per bin
   uint64_t sel[DSA_MAX_SELECT_K + kRankCap];
+  int32_t sel_ps[DSA_MAX_SELECT_K + kRankCap];  // merge with expansion: pool_start of sel[i]
   uint32_t red[NW][4];
   uint32_t tie[32 * NW];  // per (key slot, wave): tied keys, then their exclusive prefix
   uint32_t info[4];
@@ -396,12 +397,21 @@ struct ExpandArgs {
   int W;
 };
 
-__device__ __forceinline__ void expand_one(int row, int j, int32_t pid, const ExpandArgs& ex) {
+// pool_start of pool pid for the row's sequence (-1: absent or nonexistent)
+__device__ __forceinline__ int32_t expand_start(int row, int32_t pid, const ExpandArgs& ex) {
   const int b = ex.row_seq[row];
   int32_t ps = -1;
   if (pid >= 0 && pid < ex.P_max && b >= 0 && b < ex.B) ps = ex.pool_start[size_t(b) * ex.P_max + pid];
+  return ps;
+}
+
+__device__ __forceinline__ void expand_write(int row, int j, int32_t ps, const ExpandArgs& ex) {
   int32_t* t = ex.token_ids + size_t(row) * ex.W + size_t(j) * ex.kp;
   for (int sl = 0; sl < ex.kp; ++sl) t[sl] = ps >= 0 ? ps + sl : -1;
+}
+
+__device__ __forceinline__ void expand_one(int row, int j, int32_t pid, const ExpandArgs& ex) {
+  expand_write(row, j, expand_start(row, pid, ex), ex);
 }
 
 template <int NT>
@@ -642,6 +652,13 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
     vmask |= hi[j] != 0 ? (1u << j) : 0u;
     lastmask |= (in && i % m == m - 1) ? (1u << j) : 0u;
   }
+  // with expansion: every winner is among these keys, so their pool starts
+  // are requested now and arrive while the selection runs
+  int32_t ps[KPT];
+  if (ex.token_ids) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) ps[j] = (vmask >> j) & 1u ? expand_start(row, int32_t(0xffffffffu - lo[j]), ex) : -1;
+  }
   if (tid == 0) sh.flag = 0;
   for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
   uint32_t nvalid, kmax, kmin;
@@ -665,7 +682,9 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
   for (int j = 0; j < KPT; ++j) {
     const uint32_t d = bin_of(hi[j]);
     if (((vmask >> j) & 1u) && d >= t) {
-      sh.sel[sh.sfx[d] + atomicAdd(&sh.hist[d], 1u)] = (uint64_t(hi[j]) << 32) | lo[j];
+      const uint32_t at = sh.sfx[d] + atomicAdd(&sh.hist[d], 1u);
+      sh.sel[at] = (uint64_t(hi[j]) << 32) | lo[j];
+      if (ex.token_ids) sh.sel_ps[at] = ps[j];
       if ((lastmask >> j) & 1u) sh.flag = 1;
     }
   }
@@ -687,7 +706,7 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
     }
     if (pos < uint32_t(K)) {
       dst[pos] = int32_t(0xffffffffu - uint32_t(me));
-      if (ex.token_ids) expand_one(row, int(pos), int32_t(0xffffffffu - uint32_t(me)), ex);
+      if (ex.token_ids) expand_write(row, int(pos), sh.sel_ps[sl], ex);
     }
   }
   return true;
