@@ -96,6 +96,9 @@ def _parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 64 MiB device copy first (a known-size kernel for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["long", "prefill"], default="long",
+                    help="long: the decode step (the headline line); prefill: the 4096-row prefill chunk's "
+                         "scores + top-k + expand, reported against the MFMA roofline")
     ap.add_argument("--split-topk-expand", action="store_true",
                     help="run dsa_topk_pools and dsa_expand_selection as two calls instead of the fused call")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle's timed CPU work")
@@ -157,6 +160,8 @@ def main() -> int:
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.workload == "prefill":
+        return bench_prefill(args)
 
     wl = synth.workload("long")
     Q, P, K, W = wl.Q, wl.P_max, wl.K, wl.W
@@ -347,6 +352,90 @@ def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
     return {"value": round(steps / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{rows_done} decode rows of the same workload (scores over 65536 pools, top-k, "
                       f"expand, sparse MLA per row) in {el:.1f} s; 4 rows = 1 step"}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def bench_prefill(args) -> int:
+    """The prefill chunk (4096 query rows at the end of a 131072-token sequence,
+    32768 pools): dsa_index_scores over every (row, pool) pair on the matrix
+    cores, then dsa_topk_pools_expand.  Inputs follow the workload recipe: q on
+    the 1/8 grid, pooled keys from a 256-row codebook on the 1/8 grid (exact
+    score ties straddle the cut), pool metadata from dsa_kpool_compress over
+    the synthetic tokens.  The score kernel is timed per launch with events;
+    its roofline uses the algorithmic flops (2*H*D per candidate pair)."""
+    import numpy as np
+    import torch
+
+    from dsa_decode_amd import ops, synth
+    from dsa_decode_amd.layout import tile_pool_cache
+
+    dev = lambda t: t.contiguous().cuda()
+    wl = synth.workload("prefill")
+    Q, P, K, W = wl.Q, wl.P_max, wl.K, wl.W
+    ti = synth.token_inputs(wl)
+    comp = ops.dsa_kpool_compress(dev(ti["k"]), dev(ti["gate"]), dev(ti["valid"]), dev(ti["ape"]),
+                                  dev(ti["seq_len"]), wl.kp, P)
+    del ti
+    ip = synth.index_params(wl)
+    k_pool = dev(tile_pool_cache(synth.codebook_keys(wl)))
+    q, w, gamma, beta = dev(ip["q"]), dev(ip["w"]), dev(ip["gamma"]), dev(ip["beta"])
+    row_seq, row_pos = dev(ip["row_seq"]), dev(ip["row_pos"])
+    scores = torch.empty((Q, P), dtype=torch.float32, device="cuda")
+    ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
+    tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
+    tk_ws = torch.zeros(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    # candidate pairs: valid pools whose last token is at or before the row's position
+    ps = comp["pool_start"][0].cpu().numpy().astype(np.int64)
+    pv = comp["pool_valid"][0].cpu().numpy() != 0
+    last = np.sort(ps[pv] + wl.kp - 1)
+    pairs = int(np.searchsorted(last, ip["row_pos"].numpy().astype(np.int64), side="right").sum())
+    flops = 2 * wl.H * wl.D * pairs
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sc = ops.bind_index_scores(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"], gamma, beta,
+                                   ip["eps"], row_seq, row_pos, wl.kp, scores)
+        tk = ops.bind_topk_pools_expand(scores, K, ids, row_seq, comp["pool_start"], wl.kp, tok, tk_ws)
+        for _ in range(args.warmup):
+            sc()
+            tk()
+        stream.synchronize()
+        tev = TimingEvents(4 * args.steps)
+        sh = stream.cuda_stream
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            tev.record(4 * i, sh)
+            sc()
+            tev.record(4 * i + 1, sh)
+            tk()
+            tev.record(4 * i + 2, sh)
+        stream.synchronize()
+        t1 = time.perf_counter()
+    score_us = float(np.mean([tev.elapsed_us(4 * i, 4 * i + 1) for i in range(args.steps)]))
+    topk_us = float(np.mean([tev.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
+    tev.close()
+    ms = (t1 - t0) * 1e3 / args.steps
+    achieved = flops / (score_us * 1e-6) / 1e12
+    line = {
+        "metric": "DSA prefill chunk (index_scores + top-k + expand) chunks/s; % MFMA roofline",
+        "value": round(1e3 / ms, 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill chunk: 4096 rows at positions 126976..131071 of a 131072-token "
+                               "sequence, kpool 4 (32768 pools), 32 index heads x 128, select_k 512, bf16, "
+                               "q and keys on the 1/8 grid (forced ties)",
+                   "rows": Q, "pools": P, "select_k": K},
+        "stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2)},
+        "roofline": {"bound": "mfma", "kernel": "index_scores_rows", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "launch_us": round(score_us, 2), "algorithmic_flops": flops, "candidate_pairs": pairs},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 if __name__ == "__main__":

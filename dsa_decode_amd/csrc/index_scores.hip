@@ -162,6 +162,23 @@ __device__ __forceinline__ TileAcc<NH> tile_mfma(const u32x4 (&x)[4], const bf16
   return t;
 }
 
+// The folded head dots of a tile alone (its statistics formed elsewhere).
+template <int NH>
+__device__ __forceinline__ void head_mfma(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
+                                          const bf16x8 (&alo)[NH][4], f32x4 (&acc)[NH]) {
+#pragma unroll
+  for (int mb = 0; mb < NH; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x8 bx = as_bf16x8(x[i]);
+#pragma unroll
+    for (int mb = 0; mb < NH; ++mb) {
+      acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
+      acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
+    }
+  }
+}
+
 // The vector half: LayerNorm statistics, relu, head weights and the sum over
 // the lane's heads and the wave's four lane groups.
 template <int NH>
@@ -335,7 +352,15 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-template <int NH, int kTiles, int RPB>
+// Prefill kernel.  A workgroup keeps 4 x 64 pools' keys in registers (wave w:
+// 4 tiles) and runs a group of rows of one sequence over them, staging the
+// folded operands of RPB rows at a time in LDS.  The LayerNorm statistics of
+// a pool do not depend on the row, so they are formed once per tile when the
+// keys are loaded; each (row, tile) then costs the 16 head MFMAs and a short
+// epilogue, the MFMAs of tile t+1 issued before the epilogue of tile t.  After
+// the lane-group sum every lane holds a tile's scores: lane (kg, ln) keeps
+// tile kg's, so a row's 64 pools per wave go out in one 256-byte store.
+template <int NH, int RPB>
 __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
@@ -344,6 +369,7 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int rows_per_group,
     float* __restrict__ scores) {
   constexpr int H = NH * 16;
+  constexpr int kTiles = 4;  // one per lane group (the store mapping relies on it)
   __shared__ uint16_t ghi[RPB][H][kIsLd];
   __shared__ uint16_t glo[RPB][H][kIsLd];
   __shared__ float sQB[RPB][H], sW[RPB][H];
@@ -355,26 +381,48 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   const int r_begin = blockIdx.y * rows_per_group;
   const int r_end = min(Q, r_begin + rows_per_group);
   const int p_wave = blockIdx.x * (kIsWaves * kTiles * 16) + wave * (kTiles * 16);
+  const int p_mine = p_wave + lane;  // the pool whose score this lane stores (tile kg, pool ln)
 
-  // keys of this wave's tiles for the sequence of the group's first row; a row
-  // of another sequence reloads them (correct, slower)
+  // keys of this wave's tiles for the sequence of the group's first row, and
+  // 1/sigma of their pools; a row of another sequence reloads them (correct,
+  // slower)
   int b_loaded = row_seq[r_begin];
   u32x4 xk[kTiles][4];
-  int psk[kTiles], pvk[kTiles];
+  float rsig[kTiles];
+  int ps_mine = 0, pv_mine = 0;
   const int P_tiles = pool_tiles(P_max);
   auto load_keys = [&](int b) {
+    const bool bok = b >= 0 && b < B;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      const int p = p_wave + t * 16 + ln;
-      const bool in = p < P_max && b >= 0 && b < B;
-      const size_t pi = in ? size_t(b) * P_max + p : 0;
       const int tile = (p_wave >> 4) + t;
-      const size_t ti = (b >= 0 && b < B && tile < P_tiles) ? size_t(b) * P_tiles + tile : 0;
+      const size_t ti = (bok && tile < P_tiles) ? size_t(b) * P_tiles + tile : 0;
       const uint16_t* src = k_pool + ti * (16 * kIsD) + 8 * lane;
 #pragma unroll
       for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + 512 * i);
-      psk[t] = pool_start[pi];
-      pvk[t] = pool_valid[pi];
+    }
+    const size_t pi = (bok && p_mine < P_max) ? size_t(b) * P_max + p_mine : 0;
+    ps_mine = pool_start[pi];
+    pv_mine = pool_valid[pi];
+    const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 bx = as_bf16x8(xk[t][i]);
+        sacc = mfma16x16x32(ones, bx, sacc);
+        gacc = mfma16x16x32(bx, bx, gacc);
+      }
+      const int jd = ln & 3;
+      float dg = gacc[0];
+      dg = jd == 1 ? gacc[1] : dg;
+      dg = jd == 2 ? gacc[2] : dg;
+      dg = jd == 3 ? gacc[3] : dg;
+      const float sumsq = __int_as_float(__builtin_amdgcn_ds_bpermute(diag_addr, __float_as_int(dg)));
+      const float mu = sacc[0] * (1.0f / kIsD);
+      const float var = fmaxf(sumsq * (1.0f / kIsD) - mu * mu, 0.f);
+      rsig[t] = scale * __builtin_amdgcn_rsqf(var + eps);
     }
   };
   load_keys(b_loaded);
@@ -397,7 +445,6 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
       const int r = rb + rr;
       const int b = s_seq[rr];
       const int pos = s_pos[rr];
-      float* srow = scores + size_t(r) * P_max;
       const bool ok = b >= 0 && b < B;
       if (ok && b != b_loaded) {
         b_loaded = b;
@@ -406,14 +453,28 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
       bf16x8 ahi[NH][4], alo[NH][4];
       float cQ[NH][4], cW[NH][4];
       load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, scale, ahi, alo, cQ, cW);
+      float mine = 0.f;
+      f32x4 cur[NH];
+      head_mfma<NH>(xk[0], ahi, alo, cur);
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
-        const float sc = tile_score<NH>(xk[t], ahi, alo, cQ, cW, scale, eps, ln, diag_addr);
-        const int p = p_wave + t * 16 + ln;
-        if (kg == 0 && p < P_max) {
-          const bool cand = ok && pvk[t] != 0 && psk[t] + kp - 1 <= pos;
-          srow[p] = cand ? sc : -INFINITY;
+        f32x4 nxt[NH];
+        if (t + 1 < kTiles) head_mfma<NH>(xk[t + 1], ahi, alo, nxt);
+        float part = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NH; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, fmaf(rsig[t], cur[mb][j], cQ[mb][j])), part);
+        const float sc = sum_lane_groups(part);
+        mine = kg == t ? sc : mine;
+        if (t + 1 < kTiles) {
+#pragma unroll
+          for (int mb = 0; mb < NH; ++mb) cur[mb] = nxt[mb];
         }
+      }
+      if (p_mine < P_max) {
+        const bool cand = ok && pv_mine != 0 && ps_mine + kp - 1 <= pos;
+        scores[size_t(r) * P_max + p_mine] = cand ? mine : -INFINITY;
       }
     }
   }
@@ -558,7 +619,7 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
     dim3 grid(ceil_div(P_max, kIsWaves * 4 * 16), ceil_div(Q, pl.rows_per_group));
     if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
 #define DSA_IS_ROWS(NH)                                                                               \
-  hipLaunchKernelGGL((index_scores_rows<NH, 4, 4>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
+  hipLaunchKernelGGL((index_scores_rows<NH, 4>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
                      w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
                      ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
     if (H == 32) DSA_IS_ROWS(2);
