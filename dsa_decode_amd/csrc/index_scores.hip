@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // epilogue, the MFMAs of tile t+1 issued before the epilogue of tile t.  After
 // the lane-group sum every lane holds a tile's scores: lane (kg, ln) keeps
 // tile kg's, so a row's 64 pools per wave go out in one 256-byte store.
-template <int NH, int RPB>
+template <int NH, int RPB, int KT>
 __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
@@ -369,7 +369,9 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
     const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int rows_per_group,
     float* __restrict__ scores) {
   constexpr int H = NH * 16;
-  constexpr int kTiles = 4;  // one per lane group (the store mapping relies on it)
+  constexpr int kTiles = KT;  // tiles per wave: 4 or 8 (lane group kg stores tiles kg, kg + 4)
+  constexpr int NS = KT / 4;  // score stores per row and lane
+  static_assert(KT == 4 || KT == 8, "tiles per wave");
   __shared__ uint16_t ghi[RPB][H][kIsLd];
   __shared__ uint16_t glo[RPB][H][kIsLd];
   __shared__ float sQB[RPB][H], sW[RPB][H];
@@ -381,7 +383,10 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   const int r_begin = blockIdx.y * rows_per_group;
   const int r_end = min(Q, r_begin + rows_per_group);
   const int p_wave = blockIdx.x * (kIsWaves * kTiles * 16) + wave * (kTiles * 16);
-  const int p_mine = p_wave + lane;  // the pool whose score this lane stores (tile kg, pool ln)
+  // the pools whose scores this lane stores: tile kg + 4 u, pool ln
+  int p_mine[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) p_mine[u] = p_wave + 64 * u + lane;
 
   // keys of this wave's tiles for the sequence of the group's first row, and
   // 1/sigma of their pools; a row of another sequence reloads them (correct,
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   int b_loaded = row_seq[r_begin];
   u32x4 xk[kTiles][4];
   float rsig[kTiles];
-  int ps_mine = 0, pv_mine = 0;
+  int ps_mine[NS], pv_mine[NS];
   const int P_tiles = pool_tiles(P_max);
   auto load_keys = [&](int b) {
     const bool bok = b >= 0 && b < B;
@@ -401,9 +406,12 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
 #pragma unroll
       for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + 512 * i);
     }
-    const size_t pi = (bok && p_mine < P_max) ? size_t(b) * P_max + p_mine : 0;
-    ps_mine = pool_start[pi];
-    pv_mine = pool_valid[pi];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const size_t pi = (bok && p_mine[u] < P_max) ? size_t(b) * P_max + p_mine[u] : 0;
+      ps_mine[u] = pool_start[pi];
+      pv_mine[u] = pool_valid[pi];
+    }
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
@@ -453,7 +461,9 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
       bf16x8 ahi[NH][4], alo[NH][4];
       float cQ[NH][4], cW[NH][4];
       load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, scale, ahi, alo, cQ, cW);
-      float mine = 0.f;
+      float mine[NS];
+#pragma unroll
+      for (int u = 0; u < NS; ++u) mine[u] = 0.f;
       f32x4 cur[NH];
       head_mfma<NH>(xk[0], ahi, alo, cur);
 #pragma unroll
@@ -466,15 +476,18 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
 #pragma unroll
           for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, fmaf(rsig[t], cur[mb][j], cQ[mb][j])), part);
         const float sc = sum_lane_groups(part);
-        mine = kg == t ? sc : mine;
+        mine[t >> 2] = kg == (t & 3) ? sc : mine[t >> 2];
         if (t + 1 < kTiles) {
 #pragma unroll
           for (int mb = 0; mb < NH; ++mb) cur[mb] = nxt[mb];
         }
       }
-      if (p_mine < P_max) {
-        const bool cand = ok && pv_mine != 0 && ps_mine + kp - 1 <= pos;
-        scores[size_t(r) * P_max + p_mine] = cand ? mine : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        if (p_mine[u] < P_max) {
+          const bool cand = ok && pv_mine[u] != 0 && ps_mine[u] + kp - 1 <= pos;
+          scores[size_t(r) * P_max + p_mine[u]] = cand ? mine[u] : -INFINITY;
+        }
       }
     }
   }
@@ -547,6 +560,7 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 }
 
 // Launch shapes of the MFMA path.
+constexpr int kRowsTiles = 4;  // prefill kernel: key tiles per wave (256 pools per workgroup; 8 needs 316 registers, one wave per SIMD, and measured 10 % slower)
 // Decode launch shape (tuned on MI355X at 4 x 65536 pools)
 struct IsPlan {
   bool rows;  // false: decode kernel (one row per grid row)
@@ -569,7 +583,7 @@ static IsPlan is_plan(int Q, int P_max) {
   }
   // many rows: groups of rows of one sequence share the keys held in registers
   pl.rows = true;
-  const long chunks = (P_max + 255) / 256;
+  const long chunks = (P_max + kIsWaves * kRowsTiles * 16 - 1) / (kIsWaves * kRowsTiles * 16);
   int groups = int((2048 + chunks - 1) / chunks);
   if (groups < 1) groups = 1;
   const int per = (Q + groups - 1) / groups;
@@ -616,10 +630,10 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
 #undef DSA_IS_STREAM
       return launch_status();
     }
-    dim3 grid(ceil_div(P_max, kIsWaves * 4 * 16), ceil_div(Q, pl.rows_per_group));
+    dim3 grid(ceil_div(P_max, kIsWaves * kRowsTiles * 16), ceil_div(Q, pl.rows_per_group));
     if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
 #define DSA_IS_ROWS(NH)                                                                               \
-  hipLaunchKernelGGL((index_scores_rows<NH, 4>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
+  hipLaunchKernelGGL((index_scores_rows<NH, 4, kRowsTiles>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
                      w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
                      ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
     if (H == 32) DSA_IS_ROWS(2);
