@@ -125,15 +125,14 @@ __device__ __forceinline__ float sum_lane_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// A tile's contribution: LayerNorm statistics on the matrix cores, the folded
-// head dots, relu, head weights and the sum over the lane's heads and the
-// wave's four lane groups.  Returns the score of pool (lane & 15) (in all lanes).
-// cQs = scale * QB, so scale * (r * dot + QB) = (scale * r) * dot + cQs (scale
-// > 0 is not required: relu is applied to the product).  diag_addr is the
-// byte address for ds_bpermute of the lane holding the Gram diagonal of pool
-// (lane & 15): 4 * (16 * ((lane & 15) >> 2) + (lane & 15)).
-// The matrix-core half of a tile: folded head dots, sum_c x_c (ones operand)
-// and the Gram block <x_m, x_n>.
+// A tile's contribution is split in a matrix-core half (tile_mfma: LayerNorm
+// statistics and the folded head dots) and a vector half (tile_epilogue: relu,
+// head weights and the sum over the lane's heads and the wave's four lane
+// groups), so that the decode loop can issue the next tile's MFMAs before the
+// current tile's epilogue.
+//
+// The matrix-core half: folded head dots, sum_c x_c (ones operand) and the
+// Gram block <x_m, x_n>.
 template <int NH>
 struct TileAcc {
   f32x4 acc[NH], sacc, gacc;
@@ -180,7 +179,12 @@ __device__ __forceinline__ void head_mfma(const u32x4 (&x)[4], const bf16x8 (&ah
 }
 
 // The vector half: LayerNorm statistics, relu, head weights and the sum over
-// the lane's heads and the wave's four lane groups.
+// the lane's heads and the wave's four lane groups.  Returns the score of pool
+// (lane & 15) in all lanes.  cQs = scale * QB, so scale * (r * dot + QB) =
+// (scale * r) * dot + cQs (relu is applied to the product, so the sign of
+// scale does not matter).  diag_addr is the ds_bpermute byte address of the
+// lane holding the Gram diagonal of pool (lane & 15):
+// 4 * (16 * ((lane & 15) >> 2) + (lane & 15)).
 template <int NH>
 __device__ __forceinline__ float tile_epilogue(const TileAcc<NH>& t, const float (&cQs)[NH][4],
                                                const float (&cW)[NH][4], float scale, float eps, int ln,
@@ -206,15 +210,7 @@ __device__ __forceinline__ float tile_epilogue(const TileAcc<NH>& t, const float
   return sum_lane_groups(part);
 }
 
-template <int NH>
-__device__ __forceinline__ float tile_score(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
-                                            const bf16x8 (&alo)[NH][4], const float (&cQs)[NH][4],
-                                            const float (&cW)[NH][4], float scale, float eps, int ln,
-                                            int diag_addr) {
-  return tile_epilogue<NH>(tile_mfma<NH>(x, ahi, alo), cQs, cW, scale, eps, ln, diag_addr);
-}
-
-// A lane's operands for tile_score: g' hi/lo of its 16-head blocks, scale * QB
+// A lane's operands for the head MFMAs and the epilogue: g' hi/lo of its 16-head blocks, scale * QB
 // and w of the heads whose results it receives.
 template <int NH>
 __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], const uint16_t (*glo)[kIsLd],
