@@ -10,21 +10,22 @@
 // MFMA path (bf16, Dl = 512, Hm a multiple of 16).  A workgroup handles one
 // row, one group of 16 heads and a contiguous slice ("split") of 64 ids of the
 // row's list, with 4 waves:
-//   - the 16 heads' q_lat (16 KiB) and the 64 listed latent rows (64 KiB) are
-//     moved straight into LDS by the load-to-LDS path, one 1 KiB row per load
-//     instruction (16 bytes per lane, the row swizzle applied through the
-//     source addresses); wave w gathers the rows of ids 16w .. 16w+15;
+//   - the 64 listed latent rows (64 KiB) are moved straight into LDS by the
+//     load-to-LDS path, one 1 KiB row per load instruction (16 bytes per lane,
+//     the row swizzle applied through the source addresses); wave w gathers
+//     the rows of ids 16w .. 16w+15.  Each wave loads the 16 heads' q_lat
+//     (16 KiB, read from L2 by every split of the row) into registers;
 //   - wave w forms the logits of its 16 tokens for the 16 heads over the full
-//     latent width on the matrix cores (kv rows x q^T, both from LDS), so no
-//     partial logits cross waves;
+//     latent width on the matrix cores (kv rows from LDS x q^T from
+//     registers), so no partial logits cross waves;
 //   - softmax: each wave takes its own maximum per head and forms P relative
-//     to it; P (bf16) and the per-wave maxima and sums go through LDS (in the
-//     space q held), and the value contraction scales the P operand by
-//     2^(m_wave - m_row): no barrier waits for a row maximum before P is
-//     formed (one barrier frees q's space, one publishes P);
+//     to it; P (bf16) and the per-wave maxima and sums go through LDS, and
+//     the value contraction scales the P operand by 2^(m_wave - m_row): no
+//     barrier waits for a row maximum before P is formed (one barrier
+//     publishes P);
 //   - wave w accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over
 //     all 64 tokens, reading kv^T with the transposing LDS reads.
-// The swizzle spreads both LDS read patterns over the banks.  80 KiB of LDS
+// The swizzle spreads both LDS read patterns over the banks.  67 KiB of LDS
 // keeps two workgroups per CU.  The head groups of one (row, split) read the
 // same latent rows; their workgroup ids are spaced by a multiple of 8 so that
 // they share an XCD and its L2.  Splits write normalised partial outputs,
@@ -42,16 +43,13 @@ constexpr int kMlaThreads = 256;
 
 struct MlaShared {
   uint16_t rows[kMlaSplit][kMlaDl];  // latent rows, 16-byte pieces swizzled per row (64 KiB)
-  union {
-    uint16_t q[16][kMlaDl];          // the 16 heads' q_lat, swizzled like the rows (16 KiB)
-    struct {                         // after the logits: the softmax exchange
-      uint16_t p[16][kMlaSplit + 8]; // P[head][token] relative to its wave's maximum, bf16
+  struct {                           // the softmax exchange
+    uint16_t p[16][kMlaSplit + 8];   // P[head][token] relative to its wave's maximum, bf16
                                      // (rows padded to 144 B: the 16 heads' rows start in
                                      // different banks)
-      float m[16][4];                // per head: each wave's maximum (log2 domain)
-      float l[16][4];                // per head: each wave's sum of P
-    } x;
-  } u;
+    float m[16][4];                  // per head: each wave's maximum (log2 domain)
+    float l[16][4];                  // per head: each wave's sum of P
+  } x;
 };
 
 // Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Over any 8
@@ -105,13 +103,14 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       myid = (bok && id >= 0 && id < T_max) ? id : -1;
     }
   }
-  // q_lat of the 16 heads once per workgroup, straight into LDS (wave w moves
-  // heads 4w .. 4w+3, one 1 KiB row per instruction, swizzled like the rows)
+  // q_lat of the 16 heads straight into registers in the matrix-core B layout
+  // (lane (kg, ln): head ln, 16-byte piece 4j + kg of the latent for k-step j);
+  // every split of the row reads the same 16 KiB, so it comes from L2
+  u32x4 qv[16];
+  {
+    const uint16_t* qrow = q_lat + (size_t(r) * Hm + hg * 16 + ln) * kMlaDl + 8 * kg;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hh = 4 * w + i;
-    const uint16_t* src = q_lat + (size_t(r) * Hm + hg * 16 + hh) * kMlaDl + 8 * (lane ^ mla_swz(hh));
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.u.q[hh][0]), 16, 0, 0);
+    for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
   }
   // gather: one row per instruction, lane i fills piece position i with piece
   // i ^ swz of the token's row; absent ids give a zero row
@@ -129,22 +128,20 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // q and every wave's rows are in LDS
+  __syncthreads();  // every wave's rows are in LDS
 
   // logits of tokens 16w + 4kg + j (j < 4) for head ln, full latent width
-  // (A = kv rows, B = q^T, both from LDS); two accumulators shorten the MFMA
-  // dependency chain
+  // (A = kv rows from LDS, B = q^T from registers); two accumulators shorten
+  // the MFMA dependency chain
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   {
-    const int t = 16 * w + ln, sw = mla_swz(t), sq = mla_swz(ln);
+    const int t = 16 * w + ln, sw = mla_swz(t);
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
       const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + kg) ^ sw) * 8]));
       const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + 4 + kg) ^ sw) * 8]));
-      const bf16x8 b0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.u.q[ln][((4 * k + kg) ^ sq) * 8]));
-      const bf16x8 b1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.u.q[ln][((4 * k + 4 + kg) ^ sq) * 8]));
-      acc0 = mfma16x16x32(a0, b0, acc0);
-      acc1 = mfma16x16x32(a1, b1, acc1);
+      acc0 = mfma16x16x32(a0, as_bf16x8(qv[k]), acc0);
+      acc1 = mfma16x16x32(a1, as_bf16x8(qv[k + 1]), acc1);
     }
   }
   // softmax within the wave: its maximum over its 16 tokens per head, P
@@ -168,17 +165,16 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  __syncthreads();  // every wave is done with q: its region takes the exchange
-  *reinterpret_cast<u32x2*>(&sh.u.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+  *reinterpret_cast<u32x2*>(&sh.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
   if (kg == 0) {
-    sh.u.x.m[ln][w] = m_use;
-    sh.u.x.l[ln][w] = l;
+    sh.x.m[ln][w] = m_use;
+    sh.x.l[ln][w] = l;
   }
   __syncthreads();  // P, the maxima and the sums published
 
   // the row's maximum M; tokens of wave v carry the factor 2^(m_v - M)
-  const f32x4 mv = *reinterpret_cast<const f32x4*>(&sh.u.x.m[ln][0]);
-  const f32x4 lv = *reinterpret_cast<const f32x4*>(&sh.u.x.l[ln][0]);
+  const f32x4 mv = *reinterpret_cast<const f32x4*>(&sh.x.m[ln][0]);
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&sh.x.l[ln][0]);
   float M = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 4; ++v) M = fmaxf(M, lv[v] > 0.f ? mv[v] : -INFINITY);
@@ -196,7 +192,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   bf16x8 pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.u.x.p[ln][32 * ks + 8 * kg]);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.x.p[ln][32 * ks + 8 * kg]);
     const float f = fv[2 * ks + (kg >> 1)];
     u32x4 sc;
 #pragma unroll
