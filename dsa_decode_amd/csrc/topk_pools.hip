@@ -12,10 +12,11 @@
 //
 // Selection runs inside one workgroup over keys held in registers, latency
 // first (a decode row has only a few workgroups in flight):
-//  * a first pass histograms the candidates into 2048 bins of equal width
-//    between the smallest and the largest score (the map is monotone, so the
-//    bins keep the key order and tied scores share a bin); one wave scans the
-//    histogram with DPP prefix sums and finds the bin of the K-th key;
+//  * a first pass histograms the candidates into bins of equal width between
+//    the smallest and the largest score (512 to 2048 bins, about 4 keys per
+//    bin on average; the map is monotone, so the bins keep the key order and
+//    tied scores share a bin); one wave scans the histogram with DPP prefix
+//    sums and finds the bin of the K-th key;
 //  * when every bin from that one up holds at most 64 keys, those keys are
 //    scattered bin by bin into LDS and each is placed directly: output
 //    position = keys in higher bins + its rank among its bin mates;
@@ -57,6 +58,14 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 constexpr int kDig = 11;              // radix digit width
 constexpr int kBins = 1 << kDig;      // 2048 bins, 32 per lane of the scanning wave
 constexpr int kRankCap = 64;          // largest bin that is ordered by pairwise ranks
+
+// Bins of the first (linear) pass for n keys: about 4 keys per bin on average,
+// between 512 and kBins (the single-wave scan of the histogram is on the
+// critical path, and its cost follows the number of bins).
+template <int N>
+constexpr int first_pass_bins() {
+  return N <= 2048 ? 512 : (N <= 4096 ? 1024 : kBins);
+}
 
 // ---------------------------------------------------------------- wave helpers
 // v from lane (lane - n) of the same row of 16 lanes, 0 for the first n lanes
@@ -149,14 +158,17 @@ __device__ __forceinline__ void block_stats(const uint32_t (&hi)[KPT], TkShared<
 // With SFX it also writes, for every bin, the number of keys in higher bins
 // to sh.sfx, and the largest count of a bin at or above the found one to
 // sh.info[3].
-template <int NT, bool SFX = false>
+template <int NT, bool SFX = false, int NB = kBins>
 __device__ __forceinline__ void scan_find(TkShared<NT>& sh, uint32_t need) {
+  static_assert(NB == 512 || NB == 1024 || NB == 2048, "bins scanned");
+  constexpr int BPL = NB / kWave;  // bins per lane
+  constexpr int V = BPL / 4;
   const int lane = threadIdx.x & 63;
-  u32x4* hv = reinterpret_cast<u32x4*>(&sh.hist[32 * lane]);  // bins 32*lane .. 32*lane+31
-  u32x4 cv[8];
+  u32x4* hv = reinterpret_cast<u32x4*>(&sh.hist[BPL * lane]);  // bins BPL*lane .. BPL*lane+BPL-1
+  u32x4 cv[V];
   uint32_t tot = 0, lmax = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < V; ++i) {
     cv[i] = hv[i];
     tot += (cv[i][0] + cv[i][1]) + (cv[i][2] + cv[i][3]);
     if (SFX) lmax = max(lmax, max(max(cv[i][0], cv[i][1]), max(cv[i][2], cv[i][3])));
@@ -167,8 +179,8 @@ __device__ __forceinline__ void scan_find(TkShared<NT>& sh, uint32_t need) {
   const uint64_t b = __ballot(above + tot >= need);
   const int L = 63 - __builtin_clzll(b);
   const uint32_t aboveL = __builtin_amdgcn_readlane(above, L);
-  // lane L's 32 bins, highest first, over lanes 0..31
-  const uint32_t x = lane < 32 ? sh.hist[32 * L + 31 - lane] : 0u;
+  // lane L's BPL bins, highest first, over lanes 0..BPL-1
+  const uint32_t x = lane < BPL ? sh.hist[BPL * L + BPL - 1 - lane] : 0u;
   const uint32_t xin = wave_incl_sum(x);
   const uint64_t b2 = __ballot(aboveL + xin >= need);
   const int i = __builtin_ctzll(b2);
@@ -176,10 +188,10 @@ __device__ __forceinline__ void scan_find(TkShared<NT>& sh, uint32_t need) {
   const uint32_t xin_i = __builtin_amdgcn_readlane(xin, i);
   uint32_t maxc = 0;
   if (SFX) {
-    u32x4* sv = reinterpret_cast<u32x4*>(&sh.sfx[32 * lane]);
+    u32x4* sv = reinterpret_cast<u32x4*>(&sh.sfx[BPL * lane]);
     uint32_t run = above;
 #pragma unroll
-    for (int k = 7; k >= 0; --k) {
+    for (int k = V - 1; k >= 0; --k) {
       u32x4 o;
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
@@ -193,9 +205,9 @@ __device__ __forceinline__ void scan_find(TkShared<NT>& sh, uint32_t need) {
     maxc = wave_max_u32(max(lane > L ? lmax : 0u, lane <= i ? x : 0u));
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) hv[k] = u32x4{0u, 0u, 0u, 0u};
+  for (int k = 0; k < V; ++k) hv[k] = u32x4{0u, 0u, 0u, 0u};
   if (lane == 0) {
-    sh.info[0] = uint32_t(32 * L + 31 - i);
+    sh.info[0] = uint32_t(BPL * L + BPL - 1 - i);
     sh.info[1] = aboveL + xin_i - xi;
     sh.info[2] = xi;
     sh.info[3] = maxc;
@@ -488,20 +500,21 @@ __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int
     if (kmax == kmin) {
       st = {kmax, 0, nvalid, uint32_t(K)};  // every candidate has the same score
     } else {
-      // First pass: 2048 bins of equal width in score between the smallest
+      // First pass: NB1 bins of equal width in score between the smallest
       // and the largest candidate (fp32 subtraction and scaling are monotone,
       // so bins keep the key order, ties included).  It also leaves, per bin,
       // the number of keys in higher bins.
       const float fmn = key_float(kmin);
-      const float scale = float(kBins) / (key_float(kmax) - fmn);  // 0 if the range overflows
+      constexpr int NB1 = first_pass_bins<NT * KPT>();
+      const float scale = float(NB1) / (key_float(kmax) - fmn);  // 0 if the range overflows
       auto bin_of = [&](uint32_t k) -> uint32_t {
-        return min(uint32_t((key_float(k) - fmn) * scale), uint32_t(kBins - 1));
+        return min(uint32_t((key_float(k) - fmn) * scale), uint32_t(NB1 - 1));
       };
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
         if ((vmask >> j) & 1u) atomicAdd(&sh.hist[bin_of(hi[j])], 1u);
       __syncthreads();
-      if ((tid >> 6) == 0) scan_find<NT, true>(sh, uint32_t(K));
+      if ((tid >> 6) == 0) scan_find<NT, true, NB1>(sh, uint32_t(K));
       __syncthreads();
       const uint32_t t = sh.info[0], above = sh.info[1], cnt = sh.info[2], maxc = sh.info[3];
       if (maxc <= uint32_t(kRankCap)) {
@@ -665,15 +678,16 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
   block_stats<NT, KPT>(hi, sh, nvalid, kmax, kmin);
   if (nvalid <= uint32_t(K) || kmax == kmin) return false;
   const float fmn = key_float(kmin);
-  const float scale = float(kBins) / (key_float(kmax) - fmn);
+  constexpr int NB1 = first_pass_bins<NT * KPT>();
+  const float scale = float(NB1) / (key_float(kmax) - fmn);
   auto bin_of = [&](uint32_t key) -> uint32_t {
-    return min(uint32_t((key_float(key) - fmn) * scale), uint32_t(kBins - 1));
+    return min(uint32_t((key_float(key) - fmn) * scale), uint32_t(NB1 - 1));
   };
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if ((vmask >> j) & 1u) atomicAdd(&sh.hist[bin_of(hi[j])], 1u);
   __syncthreads();
-  if ((tid >> 6) == 0) scan_find<NT, true>(sh, uint32_t(K));
+  if ((tid >> 6) == 0) scan_find<NT, true, NB1>(sh, uint32_t(K));
   __syncthreads();
   const uint32_t t = sh.info[0], above = sh.info[1], cnt = sh.info[2], maxc = sh.info[3];
   if (maxc > uint32_t(kRankCap)) return false;
