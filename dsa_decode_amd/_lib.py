@@ -20,6 +20,9 @@ SIGNATURES = {
     "dsa_kpool_compress": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_int, c_int, c_int, c_int, c_int, c_int,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dsa_kpool_append": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dsa_index_scores": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                  c_int, c_int, c_int, c_int, c_int, c_int, c_int,

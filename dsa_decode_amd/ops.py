@@ -63,6 +63,24 @@ def dsa_kpool_compress(k, gate, valid, ape, seq_len, kpool: int, P_max: int, out
     return out
 
 
+def dsa_kpool_append(k, gate, valid, ape, seq_len, kpool: int, state, max_new_pools: int = 1):
+    """Advance the indexer state `state` (the dict dsa_kpool_compress returns:
+    k_pool, pool_start, pool_valid, n_pools, first_valid) in place to the new
+    lengths seq_len; forms at most max_new_pools pools per sequence."""
+    B, T_max, D = k.shape
+    P_max = state["pool_start"].shape[1]
+    _check_pool_cache(state["k_pool"], B, P_max, D)
+    st = _lib.load().dsa_kpool_append(
+        _dev(k, "k", k.dtype), _dev(gate, "gate", k.dtype), _dev(valid, "valid", torch.uint8),
+        _dev(ape, "ape", torch.float32), _dev(seq_len, "seq_len", torch.int32),
+        B, T_max, D, kpool, P_max, int(max_new_pools), _act_code(k),
+        _dev(state["k_pool"], "k_pool", k.dtype), _dev(state["pool_start"], "pool_start", torch.int32),
+        _dev(state["pool_valid"], "pool_valid", torch.uint8), _dev(state["n_pools"], "n_pools", torch.int32),
+        _dev(state["first_valid"], "first_valid", torch.int32), _stream())
+    check("dsa_kpool_append", st)
+    return state
+
+
 def dsa_index_scores(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamma, ln_beta,
                      ln_eps: float, row_seq, row_pos, kpool: int, scores=None):
     """-> scores [Q, P_max] fp32 (-inf = not a candidate); k_pool is the
@@ -243,3 +261,16 @@ def bind_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale, out, lse, wo
         _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, T_max, token_ids.shape[1], float(sm_scale),
         _act_code(kv), _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
+
+
+def bind_kpool_append(k, gate, valid, ape, seq_len, kpool, state, max_new_pools=1) -> BoundCall:
+    B, T_max, D = k.shape
+    P_max = state["pool_start"].shape[1]
+    _check_pool_cache(state["k_pool"], B, P_max, D)
+    return BoundCall("dsa_kpool_append", (
+        _dev(k, "k", k.dtype), _dev(gate, "gate", k.dtype), _dev(valid, "valid", torch.uint8),
+        _dev(ape, "ape", torch.float32), _dev(seq_len, "seq_len", torch.int32),
+        B, T_max, D, kpool, P_max, int(max_new_pools), _act_code(k),
+        _dev(state["k_pool"], "k_pool", k.dtype), _dev(state["pool_start"], "pool_start", torch.int32),
+        _dev(state["pool_valid"], "pool_valid", torch.uint8), _dev(state["n_pools"], "n_pools", torch.int32),
+        _dev(state["first_valid"], "first_valid", torch.int32), _stream()))

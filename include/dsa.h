@@ -122,6 +122,37 @@ int dsa_kpool_compress(const void* k, const void* gate, const uint8_t* valid, co
                        int32_t* n_pools, int32_t* first_valid, void* stream);
 
 /*
+ * dsa_kpool_append -- the per-sequence indexer state, advanced after tokens
+ * are appended.  "Module glm5next_dsa", module list ("state": the per-sequence
+ * DSA indexer state, the cache the selector reads every decode step) and the
+ * compress rules quoted above dsa_kpool_compress.
+ *
+ * The state of sequence b is first_valid[b], n_pools[b] and its rows of
+ * k_pool / pool_start / pool_valid.  On entry they must be exactly what
+ * dsa_kpool_compress (or earlier calls of this function) left for a length
+ * L_old <= seq_len[b], with the token data k, gate, valid of rows t < L_old
+ * unchanged since.  A fresh sequence starts from dsa_kpool_compress with
+ * seq_len = 0 (or the same bytes: k_pool 0, pool_start -1, pool_valid 0,
+ * n_pools 0, first_valid 0).  The call moves the anchor over tokens that are
+ * still invalid, forms the pools that became whole (at most max_new_pools
+ * per sequence; later calls continue where this one stopped) and updates
+ * first_valid and n_pools in place.  When no pool is left pending, the state
+ * equals the output of dsa_kpool_compress at the new lengths bit for bit (the
+ * same per-pool arithmetic).  Tensors, layouts, dtype and the limits on
+ * kpool, D and P_max are those of dsa_kpool_compress; max_new_pools >= 1.
+ * One workgroup per sequence: meant for decode steps that add a few tokens.
+ * A length that shrank is a precondition violation; the rows past the new
+ * pool count are then cleared.
+ *
+ *   n_pools, first_valid [B] int32: in/out state
+ *   k_pool, pool_start, pool_valid: in/out (only changed rows are written)
+ */
+int dsa_kpool_append(const void* k, const void* gate, const uint8_t* valid, const float* ape,
+                     const int32_t* seq_len, int B, int T_max, int D, int kpool, int P_max,
+                     int max_new_pools, int dtype, void* k_pool, int32_t* pool_start,
+                     uint8_t* pool_valid, int32_t* n_pools, int32_t* first_valid, void* stream);
+
+/*
  * dsa_index_scores -- indexer scores with candidate validity.
  * "Module glm5next_dsa", "Shape of the pipeline" (-> [Q, P] scores + candidate
  * validity) and "Traps carried from Slice 8" (indexer.k_norm is a LayerNorm:

@@ -78,6 +78,26 @@ def test_compress_refuses_bad_arguments(lib):
     assert _compress(lib, dtype=7) == DSA_ERR_UNSUPPORTED
 
 
+def _append(lib, **kw):
+    a = dict(k=FAKE, gate=FAKE, valid=FAKE, ape=FAKE, seq_len=FAKE, B=1, T_max=64, D=32, kpool=4,
+             P_max=16, max_new=1, dtype=0, k_pool=FAKE, pool_start=FAKE, pool_valid=FAKE, n_pools=FAKE,
+             first_valid=FAKE, stream=None)
+    a.update(kw)
+    return lib.dsa_kpool_append(*a.values())
+
+
+def test_append_refuses_bad_arguments(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED
+    assert _append(lib, gate=None) == DSA_ERR_NULL
+    assert _append(lib, n_pools=None) == DSA_ERR_NULL
+    assert _append(lib, max_new=0) == DSA_ERR_SHAPE
+    assert _append(lib, T_max=0) == DSA_ERR_SHAPE
+    assert _append(lib, P_max=15) == DSA_ERR_SHAPE
+    assert _append(lib, kpool=9, P_max=64) == DSA_ERR_UNSUPPORTED
+    assert _append(lib, D=12) == DSA_ERR_UNSUPPORTED
+    assert _append(lib, dtype=3) == DSA_ERR_UNSUPPORTED
+
+
 def _scores(lib, **kw):
     a = dict(q=FAKE, w=FAKE, scale=0.1, k_pool=FAKE, pool_start=FAKE, pool_valid=FAKE, g=FAKE, b=FAKE,
              eps=1e-5, row_seq=FAKE, row_pos=FAKE, Q=1, H=4, D=32, B=1, P_max=16, kpool=4, dtype=0,
