@@ -243,6 +243,183 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
 }
 
+// Many-rows path (prefill chunks): one workgroup per (row, group of 16 heads)
+// runs over all of the row's ids, 64 at a time, with an online softmax, so no
+// partial output leaves the workgroup and no combine launch follows.  Each
+// 64-id block takes the decode kernel's steps (gather into LDS, full-width
+// logits of each wave's 16 tokens, per-wave maxima, the value contraction of
+// latent quarter w); the running maximum M, sum l and the O^T accumulators
+// carry from block to block, rescaled by 2^(M_old - M_new) as the maximum
+// grows.  Workgroup ids put the head groups of a row on one XCD (ids congruent
+// mod 8), so a gathered latent row is fetched into that L2 once and read there
+// by the other groups.  Used when there are enough (row, head group) pairs to
+// fill the chip without splitting the ids.
+constexpr int kMlaRowsMinWgs = 1024;
+
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))) void mla_rows_mfma(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Q, int Hm, int B,
+    int T_max, int W, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ MlaShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, ln = lane & 15;
+  const int HG = Hm >> 4;
+  const int rest = blockIdx.x >> 3;
+  const int hg = rest % HG;
+  const int r = (rest / HG) * 8 + (blockIdx.x & 7);
+  if (r >= Q) return;  // padding workgroups (uniform exit)
+  const int h = hg * 16 + ln;
+  const int b = row_seq[r];
+  const bool bok = b >= 0 && b < B;
+  const size_t seq_base = size_t(bok ? b : 0) * T_max;
+  const int32_t* ids_row = token_ids + size_t(r) * W;
+  const int nblk = (W + kMlaSplit - 1) / kMlaSplit;
+
+  // ids of this wave's 16 tokens of block blk (lanes 0..15), -1 when absent
+  auto load_id = [&](int blk) {
+    int id = -1;
+    if (lane < 16) {
+      const int c = blk * kMlaSplit + 16 * w + lane;
+      if (c < W) {
+        const int v = ids_row[c];
+        id = (bok && v >= 0 && v < T_max) ? v : -1;
+      }
+    }
+    return id;
+  };
+  int myid = load_id(0);
+  // q_lat of the 16 heads in registers, matrix-core B layout (as in the decode kernel)
+  u32x4 qv[16];
+  {
+    const uint16_t* qrow = q_lat + (size_t(r) * Hm + h) * kMlaDl + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
+  }
+  float M_run = -INFINITY, l_run = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ib = 0; ib < nblk; ++ib) {
+    // gather the block's 64 rows (wave w: ids 16w .. 16w+15)
+    uint32_t vmask = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = __builtin_amdgcn_readlane(myid, i);
+      const int t = 16 * w + i;
+      if (id >= 0) {
+        vmask |= 1u << i;
+        const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[t][0]), 16, 0, 0);
+      } else {
+        *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    const int next_id = ib + 1 < nblk ? load_id(ib + 1) : -1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave's rows are in LDS
+
+    // logits of tokens 16w + 4kg + j for head ln over the full latent width
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int t = 16 * w + ln, sw = mla_swz(t);
+#pragma unroll
+      for (int k = 0; k < 16; k += 2) {
+        const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + kg) ^ sw) * 8]));
+        const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + 4 + kg) ^ sw) * 8]));
+        acc0 = mfma16x16x32(a0, as_bf16x8(qv[k]), acc0);
+        acc1 = mfma16x16x32(a1, as_bf16x8(qv[k + 1]), acc1);
+      }
+    }
+    // the wave's maximum per head over its 16 tokens and P relative to it
+    float x[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = (vmask >> (4 * kg + j)) & 1u ? (acc0[j] + acc1[j]) * scale_log2 : -INFINITY;
+      m = fmaxf(m, x[j]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float p[4], l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
+      l += p[j];
+    }
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    *reinterpret_cast<u32x2*>(&sh.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+    if (kg == 0) {
+      sh.x.m[ln][w] = m_use;
+      sh.x.l[ln][w] = l;
+    }
+    __syncthreads();  // P, the maxima and the sums published
+
+    // online merge: new running maximum, rescale of what is accumulated, and
+    // the factor 2^(m_v - M) of each wave's tokens
+    const f32x4 mv = *reinterpret_cast<const f32x4*>(&sh.x.m[ln][0]);
+    const f32x4 lv = *reinterpret_cast<const f32x4*>(&sh.x.l[ln][0]);
+    float Mb = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Mb = fmaxf(Mb, lv[v] > 0.f ? mv[v] : -INFINITY);
+    const float M_new = fmaxf(M_run, Mb);
+    const float M_use = M_new == -INFINITY ? 0.f : M_new;
+    const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
+    float fv[4];
+    float lb = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      fv[v] = lv[v] > 0.f ? __builtin_amdgcn_exp2f(mv[v] - M_use) : 0.f;
+      lb = fmaf(fv[v], lv[v], lb);
+    }
+    l_run = fmaf(l_run, alpha, lb);
+    M_run = M_new;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.x.p[ln][32 * ks + 8 * kg]);
+      const float f = fv[2 * ks + (kg >> 1)];
+      u32x4 sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc[e] = pack2bf(__uint_as_float(raw[e] << 16) * f, __uint_as_float(raw[e] & 0xffff0000u) * f);
+      pb[ks] = as_bf16x8(sc);
+    }
+    // O^T over latent quarter w, accumulated on top of the rescaled running sum
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      const int col = 128 * w + 16 * blk + 4 * (ln & 3);
+      const int pc = col >> 3, off = col & 7;
+      f32x4 a = o[blk] * alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
+        const u32x2 lo = lds_read_tr16(&sh.rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
+        const u32x2 hi = lds_read_tr16(&sh.rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
+        a = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], a);
+      }
+      o[blk] = a;
+    }
+    myid = next_id;
+    __syncthreads();  // rows and P are free for the next block
+  }
+
+  const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+  uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    u32x2 pkd;
+    pkd[0] = pack2bf(o[blk][0] * inv, o[blk][1] * inv);
+    pkd[1] = pack2bf(o[blk][2] * inv, o[blk][3] * inv);
+    *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
+  }
+  if (w == 0 && kg == 0 && lse)
+    lse[size_t(r) * Hm + h] = l_run > 0.f ? (M_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
+}
+
 // Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  One
 // wave per (row, head group, latent quarter, 16-channel block): lane (kg, ln)
 // owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken 32 at
@@ -365,16 +542,22 @@ __global__ __launch_bounds__(256) void mla_decode_generic(
 
 struct MlaPlan {
   bool mfma;
+  bool rows;   // many rows: one workgroup per (row, head group) over all ids
   int nsplit;  // id slices of kMlaSplit per row
   int ns8;     // nsplit rounded up to a multiple of 8 (XCD spacing)
 };
 
 static MlaPlan mla_plan(int Q, int Hm, int Dl, int W, int dtype) {
-  MlaPlan pl{false, 1, 1};
+  MlaPlan pl{false, false, 1, 1};
   if (!(dtype == DSA_BF16 && Dl == kMlaDl && Hm % 16 == 0 && Hm <= 128)) return pl;
   pl.mfma = true;
   pl.nsplit = (W + kMlaSplit - 1) / kMlaSplit;
   pl.ns8 = (pl.nsplit + 7) / 8 * 8;
+  if (pl.nsplit > 1 && long(Q) * (Hm / 16) >= kMlaRowsMinWgs) {
+    pl.rows = true;
+    pl.nsplit = 1;
+    pl.ns8 = 1;
+  }
   return pl;
 }
 
@@ -419,6 +602,14 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
                          (float*)out, lse);
     return launch_status();
   }
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (pl.rows) {
+    const long nwg = (long(Q) + 7) / 8 * 8 * (Hm / 16);
+    hipLaunchKernelGGL(mla_rows_mfma, dim3(unsigned(nwg)), dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
+                       (const uint16_t*)kv, row_seq, token_ids, Q, Hm, B, T_max, W, scale_log2,
+                       (uint16_t*)out, lse);
+    return launch_status();
+  }
   uint16_t* part_o = nullptr;
   float* part_lse = nullptr;
   if (pl.nsplit > 1) {
@@ -426,7 +617,6 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
     part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                         align256(size_t(Q) * pl.nsplit * Hm * Dl * sizeof(uint16_t)));
   }
-  const float scale_log2 = sm_scale * 1.4426950408889634f;
   dim3 grid((Hm / 16) * pl.ns8, Q);
   hipLaunchKernelGGL(mla_decode_mfma, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
                      (const uint16_t*)kv, row_seq, token_ids, Hm, B, T_max, W, pl.nsplit, pl.ns8,

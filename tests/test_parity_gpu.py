@@ -436,6 +436,63 @@ def test_mla_split_merge_levels(W):
     check_mla(q_lat, kv, row_seq, tok, 512 ** -0.5, torch.bfloat16)
 
 
+def _distinct_ids_below(rng, Q, W, limits, hole_frac=0.0):
+    """Per row q, W distinct random token ids in [0, limits[q]) (fewer when the
+    range is smaller; the rest -1), with a fraction turned into -1 holes."""
+    out = np.full((Q, W), -1, np.int32)
+    for qi in range(Q):
+        n = int(limits[qi])
+        take = min(W, n)
+        if take == n:
+            ids = rng.permutation(n)
+        else:
+            ids = np.unique(rng.integers(0, n, size=2 * take + 64))
+            while ids.size < take:
+                ids = np.unique(np.concatenate([ids, rng.integers(0, n, size=take)]))
+            ids = rng.permutation(ids)[:take]
+        out[qi, :take] = ids
+    if hole_frac > 0:
+        out[rng.random(out.shape) < hole_frac] = -1
+    return out
+
+
+@pytest.mark.parametrize("Q,Hm,W", [(256, 64, 1000), (1024, 16, 130), (300, 64, 2048)])
+def test_mla_many_rows_path(Q, Hm, W):
+    # enough (row, head group) pairs that each workgroup runs over all of its
+    # row's ids with the online softmax (no split partials): ragged last
+    # blocks, holes, empty rows, rows whose first blocks are all holes, and a
+    # row count that is not a multiple of 8
+    rng = np.random.default_rng(Q + W)
+    B, T = 3, 6000
+    q_lat = torch.from_numpy(rng.standard_normal((Q, Hm, 512)).astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(rng.standard_normal((B, T, 512)).astype(np.float32)).to(torch.bfloat16)
+    row_seq = (np.arange(Q) % B).astype(np.int32)
+    tok = _distinct_ids_below(rng, Q, W, np.full(Q, T), hole_frac=0.15)
+    tok[5, :] = -1                          # nothing selected
+    tok[7, : min(W, 200)] = -1              # the first blocks empty, later ones not
+    tok[9, 1:] = -1                         # a single token
+    rows = sorted({0, 5, 7, 9, Q - 1} | set(rng.choice(Q, 12, replace=False).tolist()))
+    lib = ops()._lib.load()
+    assert lib.dsa_sparse_mla_workspace_bytes(Q, Hm, 512, W, 1) == 0   # no split partials
+    check_mla(q_lat, kv, row_seq, tok, 512 ** -0.5, torch.bfloat16, rows=rows)
+
+
+def test_mla_prefill_chunk_full_size_sampled_rows():
+    # the prefill chunk's shape: 4096 rows at positions 126976 .. 131071 of one
+    # 131072-token sequence, 2048 ids per row (causal: ids at or before the
+    # row's position), 64 heads over the 512 latent; sampled rows against the
+    # oracle, every row finite and lse finite
+    wl = synth.workload("prefill")
+    rng = np.random.default_rng(4096)
+    mi = synth.mla_inputs(wl)
+    ip = synth.index_params(wl)
+    pos = ip["row_pos"].numpy()
+    tok = _distinct_ids_below(rng, wl.Q, wl.W, pos + 1)
+    rows = [0, 1, 777, 2048, 4095] + rng.choice(wl.Q, 5, replace=False).tolist()
+    g = check_mla(mi["q_lat"], mi["kv"], ip["row_seq"].numpy(), tok, mi["sm_scale"], torch.bfloat16, rows=rows)
+    assert np.isfinite(g).all()
+
+
 def test_mla_one_dominant_token_per_row():
     # every head of row r puts its softmax mass on one token, in a different id
     # slice per row: the merge weights of the slices must carry it
