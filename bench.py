@@ -354,13 +354,47 @@ def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
                       f"expand, sparse MLA per row) in {el:.1f} s; 4 rows = 1 step"}
 
 
+def cpu_baseline_prefill(wl, ip, mi, comp, k_pool, budget_s: float) -> dict:
+    """The oracle (as it is) on a bounded sample of the prefill chunk: rows of the
+    chunk, each through scores over the 32768 pools -> top-k -> expand -> sparse
+    MLA, until about budget_s of CPU work; scaled to chunks/s (4096 rows/chunk)."""
+    import numpy as np
+    from oracle import dsa_oracle as O
+    from dsa_decode_amd.layout import untile_pool_cache
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    kp_host = untile_pool_cache(k_pool.cpu(), wl.P_max)
+    ps, pv = comp["pool_start"].cpu(), comp["pool_valid"].cpu()
+    rows_done = 0
+    t0 = time.perf_counter()
+    while True:
+        r = (rows_done * 997) % wl.Q
+        s = O.index_scores(ip["q"], ip["w"], ip["scale"], kp_host, ps, pv, ip["gamma"], ip["beta"], ip["eps"],
+                           ip["row_seq"], ip["row_pos"], wl.kp, rows=[r])
+        ids = O.topk_pools(s, wl.K)
+        tok = O.expand_selection(ids, ip["row_seq"].numpy()[[r]], ps.numpy(), wl.kp, wl.W)
+        O.sparse_mla_decode(mi["q_lat"][[r]], mi["kv"], ip["row_seq"][[r]], tok, mi["sm_scale"])
+        rows_done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(rows_done / wl.Q / el, 6), "unit": "chunks/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} rows of the prefill chunk (scores over 32768 pools, top-k, expand, sparse "
+                      f"MLA per row) in {el:.1f} s; 4096 rows = 1 chunk"}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 
 def bench_prefill(args) -> int:
     """The prefill chunk (4096 query rows at the end of a 131072-token sequence,
     32768 pools): dsa_index_scores over every (row, pool) pair on the matrix
-    cores, then dsa_topk_pools_expand.  Inputs follow the workload recipe: q on
+    cores, then dsa_topk_pools_expand, then dsa_sparse_mla_decode over the
+    selected tokens (the many-rows path).  Inputs follow the workload recipe: q on
     the 1/8 grid, pooled keys from a 256-row codebook on the 1/8 grid (exact
     score ties straddle the cut), pool metadata from dsa_kpool_compress over
     the synthetic tokens.  The score kernel is timed per launch with events;
@@ -386,6 +420,12 @@ def bench_prefill(args) -> int:
     ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
     tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
     tk_ws = torch.zeros(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    mi = synth.mla_inputs(wl)
+    q_lat, kv = dev(mi["q_lat"]), dev(mi["kv"])
+    out = torch.empty((Q, wl.Hm, wl.Dl), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Q, wl.Hm), dtype=torch.float32, device="cuda")
+    mla_ws = torch.empty(max(1, ops.dsa_sparse_mla_workspace_bytes(Q, wl.Hm, wl.Dl, W, ops.DSA_BF16)),
+                         dtype=torch.uint8, device="cuda")
     # candidate pairs: valid pools whose last token is at or before the row's position
     ps = comp["pool_start"][0].cpu().numpy().astype(np.int64)
     pv = comp["pool_valid"][0].cpu().numpy() != 0
@@ -398,9 +438,11 @@ def bench_prefill(args) -> int:
         sc = ops.bind_index_scores(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"], gamma, beta,
                                    ip["eps"], row_seq, row_pos, wl.kp, scores)
         tk = ops.bind_topk_pools_expand(scores, K, ids, row_seq, comp["pool_start"], wl.kp, tok, tk_ws)
+        ml = ops.bind_sparse_mla_decode(q_lat, kv, row_seq, tok, mi["sm_scale"], out, lse, mla_ws)
         for _ in range(args.warmup):
             sc()
             tk()
+            ml()
         stream.synchronize()
         tev = TimingEvents(4 * args.steps)
         sh = stream.cuda_stream
@@ -411,15 +453,31 @@ def bench_prefill(args) -> int:
             tev.record(4 * i + 1, sh)
             tk()
             tev.record(4 * i + 2, sh)
+            ml()
+            tev.record(4 * i + 3, sh)
         stream.synchronize()
         t1 = time.perf_counter()
     score_us = float(np.mean([tev.elapsed_us(4 * i, 4 * i + 1) for i in range(args.steps)]))
     topk_us = float(np.mean([tev.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
+    mla_us = float(np.mean([tev.elapsed_us(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
     tev.close()
     ms = (t1 - t0) * 1e3 / args.steps
     achieved = flops / (score_us * 1e-6) / 1e12
+    # sparse MLA: per (row, listed id) 2*Hm*Dl flops for the logits and as many for the values
+    listed = int((tok >= 0).sum().item())
+    mla_flops = 4 * wl.Hm * wl.Dl * listed
+    mla_achieved = mla_flops / (mla_us * 1e-6) / 1e12
+    kernels = {
+        "index_scores_rows": {"launch_us": round(score_us, 2), "achieved": round(achieved, 1),
+                              "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
+        "mla_rows_mfma": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
+                          "frac": round(mla_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": mla_flops,
+                          "listed_ids": listed},
+    }
+    dom = "index_scores_rows" if score_us >= mla_us else "mla_rows_mfma"
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, ip, mi, comp, k_pool, args.cpu_seconds)
     line = {
-        "metric": "DSA prefill chunk (index_scores + top-k + expand) chunks/s; % MFMA roofline",
+        "metric": "DSA prefill chunk (index_scores + top-k + expand + sparse MLA) chunks/s; % MFMA roofline",
         "value": round(1e3 / ms, 2), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -427,12 +485,14 @@ def bench_prefill(args) -> int:
                                "sequence, kpool 4 (32768 pools), 32 index heads x 128, select_k 512, bf16, "
                                "q and keys on the 1/8 grid (forced ties)",
                    "rows": Q, "pools": P, "select_k": K},
-        "stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2)},
-        "roofline": {"bound": "mfma", "kernel": "index_scores_rows", "achieved": round(achieved, 1),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "launch_us": round(score_us, 2), "algorithmic_flops": flops, "candidate_pairs": pairs},
-        "cpu_baseline": None,
+        "stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2),
+                      "sparse_mla_decode": round(mla_us, 2)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+                     "traffic": None, "launch_us": kernels[dom]["launch_us"],
+                     "algorithmic_flops": kernels[dom]["algorithmic_flops"], "candidate_pairs": pairs},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
