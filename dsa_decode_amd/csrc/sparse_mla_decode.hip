@@ -41,7 +41,7 @@ constexpr int kMlaDl = 512;
 constexpr int kMlaSplit = 64;   // ids per workgroup
 constexpr int kMlaThreads = 256;
 
-struct MlaShared {
+struct alignas(16) MlaShared {
   uint16_t rows[kMlaSplit][kMlaDl];  // latent rows, 16-byte pieces swizzled per row (64 KiB)
   struct {                           // the softmax exchange
     uint16_t p[16][kMlaSplit + 8];   // P[head][token] relative to its wave's maximum, bf16
@@ -420,6 +420,210 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     lse[size_t(r) * Hm + h] = l_run > 0.f ? (M_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Many-rows path for 64 heads: one workgroup per row holds all 64 heads, so
+// each gathered latent row lands in LDS once for every head of the row.  Per
+// 64-id block:
+//   - every wave holds the block's 64 ids (one per lane; a ballot gives the
+//     validity of all 64) and gathers the rows of ids 16w .. 16w+15 into LDS;
+//     the rows of block i+1 are gathered into the second buffer while block i
+//     is computed;
+//   - wave w forms the logits of heads 16w .. 16w+15 over all 64 tokens (kv
+//     rows from LDS x q^T from registers, four token tiles), so the softmax of
+//     its heads needs no other wave: it keeps the running maximum and sum of
+//     its heads, writes P relative to the new maximum (bf16) and the rescale
+//     factor 2^(M_old - M_new) of each head to LDS;
+//   - wave w then accumulates latent quarter w of O^T for all 64 heads (kv^T
+//     from the transposing LDS reads, each fragment used for the four head
+//     tiles; P^T from LDS), rescaling its accumulators by the heads' factors.
+// The final sums cross waves once through LDS.  LDS: two 64 KiB row buffers
+// + 9 KiB of P; one workgroup per CU (the 128 accumulators per lane and the
+// row's q_lat in registers allow one wave per SIMD).
+struct alignas(16) Mla64Shared {
+  uint16_t rows[2][kMlaSplit][kMlaDl];  // latent rows, pieces swizzled by mla_swz
+  uint16_t p[64][kMlaSplit + 8];        // P[head][token], rows padded to 144 B
+  float alpha[64];                      // per head: rescale of the running sums in this block
+  float l[64];                          // per head: final sum of P
+};
+
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))) void mla_rows64_mfma(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Q, int B, int T_max,
+    int W, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int Hm = 64;
+  __shared__ Mla64Shared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, ln = lane & 15;
+  const int r = blockIdx.x;
+  const int b = row_seq[r];
+  const bool bok = b >= 0 && b < B;
+  const size_t seq_base = size_t(bok ? b : 0) * T_max;
+  const int32_t* ids_row = token_ids + size_t(r) * W;
+  const int nblk = (W + kMlaSplit - 1) / kMlaSplit;
+
+  // raw id of token `lane` of block blk (-1 past the list) and its check
+  // (-1 when absent or out of range), kept apart so that the next block's id
+  // load is not waited for right after the gather it would otherwise follow
+  auto load_raw = [&](int blk) {
+    const int c = blk * kMlaSplit + lane;
+    return (blk < nblk && c < W) ? ids_row[c] : -1;
+  };
+  auto check_id = [&](int v) { return (bok && v >= 0 && v < T_max) ? v : -1; };
+  // rows 16w .. 16w+15 of the block whose ids `ids` holds, into buffer `buf`
+  auto gather = [&](int ids, int buf) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * w + i;
+      const int id = __builtin_amdgcn_readlane(ids, t);
+      if (id >= 0) {
+        const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[buf][t][0]), 16,
+                                         0, 0);
+      } else {
+        *reinterpret_cast<u32x4*>(&sh.rows[buf][t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  int cur_id = check_id(load_raw(0));
+  // q_lat of heads 16w .. 16w+15 in registers (lane (kg, ln): head 16w + ln,
+  // 16-byte piece 4j + kg of the latent for k-step j)
+  const int hq = 16 * w + ln;
+  u32x4 qv[16];
+  {
+    const uint16_t* qrow = q_lat + (size_t(r) * Hm + hq) * kMlaDl + 8 * kg;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
+  }
+  gather(cur_id, 0);
+  int nxt_raw = load_raw(1);
+  float M_run = -INFINITY, l_run = 0.f;  // head hq
+  f32x4 o[4][8];                         // [head tile][16-wide latent block of quarter w]
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[ht][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // logits reads: token row 16t + ln has swizzle mla_swz(ln), so the piece of
+  // k-step k is 4 * (k ^ s2) + (kg ^ s1): four lane bases, the rest constant
+  const int swl = mla_swz(ln);
+  int lbase[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) lbase[kk] = ln * kMlaDl + (4 * (kk ^ (swl >> 2)) + (kg ^ (swl & 3))) * 8;
+
+  for (int ib = 0; ib < nblk; ++ib) {
+    const int cur = ib & 1;
+    const uint64_t vmask = __ballot(cur_id >= 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // block ib's rows are in LDS; every wave is done with block ib - 1
+    if (ib + 1 < nblk) {
+      cur_id = check_id(nxt_raw);
+      gather(cur_id, cur ^ 1);
+      nxt_raw = load_raw(ib + 2);
+    }
+    const uint16_t* rows = &sh.rows[cur][0][0];
+
+    // logits of tokens 16t + 4kg + j (t < 4, j < 4) for head hq
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[k & 3] + 16 * t * kMlaDl + (k >> 2) * 128));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[k]), acc[t]);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 16 * t + 4 * kg + j;
+        acc[t][j] = (vmask >> tok) & 1ull ? acc[t][j] * scale_log2 : -INFINITY;
+        m = fmaxf(m, acc[t][j]);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const float M_new = fmaxf(M_run, m);
+    const float M_use = M_new == -INFINITY ? 0.f : M_new;
+    const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
+    float lb = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(acc[t][j] - M_use);
+        lb += p[j];
+      }
+      *reinterpret_cast<u32x2*>(&sh.p[hq][16 * t + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+    }
+    lb += __shfl_xor(lb, 16, kWave);
+    lb += __shfl_xor(lb, 32, kWave);
+    l_run = fmaf(l_run, alpha, lb);
+    M_run = M_new;
+    if (kg == 0) sh.alpha[hq] = alpha;
+    // P and the rescale factors of all 64 heads published: LDS writes done,
+    // then the barrier alone (a full __syncthreads would also wait for the
+    // next block's gather, which must stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // O^T over latent quarter w for the four head tiles: A = kv^T (16 dl x 32
+    // tokens, two transposing reads), B = P^T (32 tokens x 16 heads)
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const float av = sh.alpha[16 * ht + ln];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[ht][k] *= av;
+    }
+    // the piece of column block blk in token rows t0 (t1 = t0 + 4) is
+    // 16w + 2 (blk ^ s3) + e (e ^ 1 for t1); s3 is recomputed per block so
+    // that the 32 addresses are not held across the loop
+    int s3 = (ln >> 2) + 4 * (kg & 1);
+    asm volatile("" : "+v"(s3));
+    const int e = (ln & 3) >> 1, off = 4 * (ln & 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+        pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][32 * ks + 8 * kg]));
+      const int t0 = 32 * ks + 8 * kg + (ln >> 2);
+      const uint16_t* r0 = rows + t0 * kMlaDl + off;
+      const uint16_t* r1 = r0 + 4 * kMlaDl;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int pc = 16 * w + 2 * (blk ^ s3);
+        const u32x2 lo = lds_read_tr16(r0 + (pc + e) * 8);
+        const u32x2 hi = lds_read_tr16(r1 + (pc + (e ^ 1)) * 8);
+        const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) o[ht][blk] = mfma16x16x32(av, pb[ht], o[ht][blk]);
+      }
+    }
+  }
+
+  if (kg == 0) sh.l[hq] = l_run;
+  if (kg == 0 && lse)
+    lse[size_t(r) * Hm + hq] = l_run > 0.f ? (M_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = 16 * ht + ln;
+    const float lh = sh.l[h];
+    const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+    uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      u32x2 pkd;
+      pkd[0] = pack2bf(o[ht][blk][0] * inv, o[ht][blk][1] * inv);
+      pkd[1] = pack2bf(o[ht][blk][2] * inv, o[ht][blk][3] * inv);
+      *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
+    }
+  }
+}
+
 // Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  One
 // wave per (row, head group, latent quarter, 16-channel block): lane (kg, ln)
 // owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken 32 at
@@ -603,6 +807,12 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
     return launch_status();
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (pl.rows && Hm == 64) {
+    hipLaunchKernelGGL(mla_rows64_mfma, dim3(Q), dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
+                       (const uint16_t*)kv, row_seq, token_ids, Q, B, T_max, W, scale_log2, (uint16_t*)out,
+                       lse);
+    return launch_status();
+  }
   if (pl.rows) {
     const long nwg = (long(Q) + 7) / 8 * 8 * (Hm / 16);
     hipLaunchKernelGGL(mla_rows_mfma, dim3(unsigned(nwg)), dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
