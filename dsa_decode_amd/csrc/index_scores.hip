@@ -233,7 +233,9 @@ __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], cons
 }
 
 // Decode kernel.  A workgroup owns 4*NT consecutive 16-pool tiles of one row
-// (wave w takes tiles w, w+4, ...); each wave runs through its tiles with a
+// (wave w takes the NT consecutive tiles w*NT ..: each wave streams one
+// contiguous 4*NT KiB stretch of the pool cache, which measured faster than
+// interleaving the waves tile by tile); each wave runs through its tiles with a
 // kStreamRing-deep register ring (the next tiles' key loads in flight while one
 // is computed).  In the tile-interleaved pool cache each of a tile's 4 key
 // loads per lane covers 1 KiB of contiguous memory and lands directly in the
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   u32x4 xb[R][4];
   auto issue = [&](int slot, int j) {
-    const int t = t0 + wave + kIsWaves * j;
+    const int t = t0 + wave * NT + j;
     const bool in = j < NT && t < P_tiles;
     const uint16_t* src = kseq + size_t(in ? t : 0) * kTileElems + 8 * lane;
 #pragma unroll
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
       }
       const float sc = tile_epilogue<NH>(cur, cQ, cW, scale, eps, ln, diag_addr);
       // the four lane groups hold the same sum: all write it (no branch)
-      sOut[(wave + kIsWaves * j) * 16 + ln] = sc;
+      sOut[(wave * NT + j) * 16 + ln] = sc;
       if (j + 1 < NT) cur = nxt;
     }
   }
