@@ -209,3 +209,36 @@ def random_token_ids(Q: int, W: int, n_tokens: list, row_seq: list, seed: int, *
             ids[rng.random(take) < hole_frac] = -1
         out[qi, :take] = ids
     return torch.from_numpy(out)
+
+
+def paged_latent(kv: torch.Tensor, page_size: int, seed: int, *, fp8: bool = False,
+                 spare_pages: int = 3) -> dict:
+    """A latent cache [B, T_max, Dl] laid out in pages for the paged decode.
+
+    Returns kv_pages [num_pages, page_size, Dl] (bf16, or uint8 OCP FP8 E4M3
+    codes when fp8), kv_scale [num_pages, page_size] fp32 (fp8 only: the row's
+    max |value| / 448, so codes span the format's range) and block_table
+    [B, T_max / page_size] int32: page j of sequence b sits at a random
+    physical page (a seeded permutation, with spare_pages unused pages mixed in).
+    """
+    B, T, Dl = kv.shape
+    assert T % page_size == 0
+    per = T // page_size
+    num_pages = B * per + spare_pages
+    perm = _rng(seed, 31).permutation(num_pages)[: B * per].astype(np.int32)
+    block_table = torch.from_numpy(perm.reshape(B, per).copy())
+    rows = kv.reshape(B * per, page_size, Dl)
+    if not fp8:
+        pages = torch.zeros((num_pages, page_size, Dl), dtype=kv.dtype)
+        pages[torch.from_numpy(perm.astype(np.int64))] = rows
+        return dict(kv_pages=pages, kv_scale=None, block_table=block_table, num_pages=num_pages)
+    x = rows.float()
+    amax = x.abs().amax(dim=-1, keepdim=True).clamp_min(1e-30)
+    scale = (amax / 448.0).float()
+    codes = (x / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    pages = torch.zeros((num_pages, page_size, Dl), dtype=torch.uint8)
+    sc = torch.ones((num_pages, page_size), dtype=torch.float32)
+    idx = torch.from_numpy(perm.astype(np.int64))
+    pages[idx] = codes
+    sc[idx] = scale[..., 0]
+    return dict(kv_pages=pages, kv_scale=sc, block_table=block_table, num_pages=num_pages)

@@ -37,6 +37,15 @@ design notes of the repository):
       argument.
   R11 Pools p >= n_pools (and every pool of a sequence with no valid token) are
       written as k_pool = 0, pool_start = -1, pool_valid = 0.
+  R12 Paged latent cache (the page names a paged decode and an fp8 variant of
+      it only by file name): physical pages [num_pages, page_size, Dl]; a page
+      table [B, max_pages] maps page j of sequence b to a physical page, so
+      token t of sequence b is row t % page_size of page
+      block_table[b, t // page_size].  A token whose page index or table entry
+      is out of range counts as absent (like -1).
+  R13 fp8 latent cache: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias
+      7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN) and one
+      fp32 scale per token row; the latent value is decode(code) * scale.
 """
 from __future__ import annotations
 
@@ -270,3 +279,62 @@ def sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, rows=None)
         out[i] = (e @ V) / l
         lse[i] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# paged and fp8 latent cache (readings R12, R13): the attention above over a
+# latent cache stored in pages, optionally as fp8 E4M3 codes with a scale per
+# token row.  [DSA] module list: "attend", the launcher of the selected-index
+# NoPE MLA *paged* decode; "Constants": mla_paged_decode{,_fp8}.
+# --------------------------------------------------------------------------
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """OCP FP8 E4M3 code -> exact float64: sign * 2^(e-7) * (1 + m/8) for
+    e = 1..15 (except e = 15, m = 7: NaN), sign * 2^-6 * m/8 for e = 0."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def paged_latent_rows(kv_pages, kv_scale=None) -> np.ndarray:
+    """Physical latent rows [num_pages * page_size, Dl] in float64: bf16/fp32
+    pages widened exactly, or fp8 E4M3 codes (uint8) decoded and multiplied by
+    their row's scale (kv_scale [num_pages, page_size])."""
+    if kv_scale is None:
+        kv = f64(kv_pages)
+        return kv.reshape(-1, kv.shape[-1])
+    codes = np.asarray(kv_pages.numpy() if hasattr(kv_pages, "numpy") else kv_pages, dtype=np.uint8)
+    vals = fp8_e4m3_decode(codes).reshape(-1, codes.shape[-1])
+    return vals * f64(kv_scale).reshape(-1, 1)
+
+
+def paged_token_rows(token_ids, row_seq, block_table, page_size: int, num_pages: int) -> np.ndarray:
+    """Physical row of each listed token (R12): -1 for -1 entries and for tokens
+    whose page index or page-table entry is out of range."""
+    tok = _i(token_ids); row_seq = _i(row_seq); bt = _i(block_table)
+    max_pages = bt.shape[1]
+    out = np.full(tok.shape, -1, dtype=np.int64)
+    for r in range(tok.shape[0]):
+        b = int(row_seq[r])
+        for c in range(tok.shape[1]):
+            t = int(tok[r, c])
+            if t < 0 or t // page_size >= max_pages:
+                continue
+            pg = int(bt[b, t // page_size])
+            if 0 <= pg < num_pages:
+                out[r, c] = pg * page_size + t % page_size
+    return out
+
+
+def sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_size: int, row_seq, token_ids,
+                            sm_scale: float, rows=None):
+    """sparse_mla_decode over a paged (optionally fp8) latent cache: each listed
+    token is resolved to its physical row (R12), the rows are dequantized (R13),
+    and the same softmax attention is taken over them."""
+    num_pages = int(np.asarray(kv_pages.shape)[0])
+    phys = paged_token_rows(token_ids, row_seq, block_table, page_size, num_pages)
+    flat = paged_latent_rows(kv_pages, kv_scale)[None]         # one "sequence" holding every row
+    return sparse_mla_decode(q_lat, flat, np.zeros_like(_i(row_seq)), phys, sm_scale, rows=rows)

@@ -405,3 +405,67 @@ def test_expand_id_naming_no_pool_gives_sentinel():
     pool_start = np.array([[2, 6, -1, -1]])
     tok = O.expand_selection(np.array([[1, 2, -1]]), [0], pool_start, 4, 14)
     assert tok.tolist() == [[6, 7, 8, 9] + [-1] * 10]
+
+
+# ------------------------------------------------------------------ paged / fp8 latent (R12, R13)
+def test_fp8_e4m3_decode_matches_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert ((got == ref) | (np.isnan(got) & np.isnan(ref))).all()
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.signbit(got[0x80]) and got[0x80] == 0
+
+
+def _paged_case(fp8: bool, seed: int = 5):
+    rng = np.random.default_rng(seed)
+    B, T, Dl, Hm, W, ps = 2, 96, 64, 4, 40, 16
+    kv = torch.from_numpy(rng.standard_normal((B, T, Dl)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((3, Hm, Dl)).astype(np.float32)).to(torch.bfloat16)
+    row_seq = np.array([1, 0, 1], np.int32)
+    tok = synth.random_token_ids(3, W, [T, T], row_seq.tolist(), seed=seed, hole_frac=0.1).numpy()
+    return kv, q, row_seq, tok, synth.paged_latent(kv, ps, seed, fp8=fp8), ps
+
+
+def test_paged_latent_equals_contiguous_cache():
+    # bf16 pages behind a shuffled page table give exactly the contiguous cache's attention
+    kv, q, row_seq, tok, pg, ps = _paged_case(False)
+    o1, l1 = O.sparse_mla_decode(q, kv, row_seq, tok, 0.125)
+    o2, l2 = O.sparse_mla_decode_paged(q, pg["kv_pages"], None, pg["block_table"], ps, row_seq, tok, 0.125)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_paged_out_of_range_page_is_an_absent_token():
+    kv, q, row_seq, tok, pg, ps = _paged_case(False, seed=6)
+    bt = pg["block_table"].clone()
+    t0 = int(tok[0][tok[0] >= 0][0])
+    bt[row_seq[0], t0 // ps] = pg["num_pages"] + 7            # a table entry past the pages
+    tok_far = tok.copy()
+    tok_far[1, 0] = bt.shape[1] * ps + 3                      # a token past the table
+    o, l = O.sparse_mla_decode_paged(q, pg["kv_pages"], None, bt, ps, row_seq, tok_far, 0.125)
+    ref_tok = tok.copy()
+    for r in np.flatnonzero(row_seq == row_seq[0]):          # every row of that sequence
+        ref_tok[r][(ref_tok[r] >= 0) & (ref_tok[r] // ps == t0 // ps)] = -1
+    ref_tok[1, 0] = -1
+    ro, rl = O.sparse_mla_decode(q, kv, row_seq, ref_tok, 0.125)
+    np.testing.assert_array_equal(o, ro)
+    np.testing.assert_array_equal(l, rl)
+
+
+def test_fp8_paged_latent_is_the_dequantized_cache():
+    # fp8 codes times their row scale (decoded here by torch's float8 type, not the
+    # oracle's decoder) as a contiguous cache give the same attention
+    kv, q, row_seq, tok, pg, ps = _paged_case(True, seed=7)
+    deq = (pg["kv_pages"].view(torch.float8_e4m3fn).double() * pg["kv_scale"].double()[..., None])
+    B, T, Dl = kv.shape
+    dense = deq[pg["block_table"].reshape(-1).long()].reshape(B, T, Dl)
+    o1, l1 = O.sparse_mla_decode(q, dense.numpy(), row_seq, tok, 0.125)
+    o2, l2 = O.sparse_mla_decode_paged(q, pg["kv_pages"], pg["kv_scale"], pg["block_table"], ps, row_seq, tok,
+                                       0.125)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+    # and the quantisation itself stays within E4M3's half-ulp of the bf16 cache (2^-4 relative)
+    err = np.abs(dense.numpy() - kv.double().numpy())
+    assert (err <= np.abs(kv.double().numpy()) * 2.0 ** -4 + pg["kv_scale"].max().item() * 2.0 ** -9).all()
