@@ -38,10 +38,14 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "dsa_sparse_mla_paged_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "dsa_sparse_mla_decode_paged": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                            c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_float,
+                                            c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_MAX_KPOOL = 8
 DSA_MAX_SELECT_K = 2048
 DSA_TOPK_COUNTER_BYTES = 262144

@@ -76,11 +76,27 @@ __device__ __forceinline__ size_t part_off(size_t rs, int HG, int hg, int dq, in
   return ((((rs * HG + hg) * 4 + dq) * 8 + blk) * 64 + lane) * 4;
 }
 
+// Where the latent rows live.  kKvRows: the cache [B, T_max, Dl] bf16 (token t
+// of sequence b is row b*T_max + t).  kKvPaged: bf16 pages [num_pages,
+// page_size, Dl] behind a page table [B, max_pages] (token t of sequence b is
+// row t % page_size of page block_table[b, t / page_size]).  kKvPagedFp8: the
+// same pages holding OCP FP8 E4M3 codes with one fp32 scale per row, widened
+// to bf16 (value * scale, rounded to nearest even) on the way into LDS.
+enum KvLayout { kKvRows = 0, kKvPaged = 1, kKvPagedFp8 = 2 };
+
+struct KvPages {
+  const int32_t* block_table;
+  const float* scale;
+  int max_pages, page_size, num_pages;
+};
+
+template <int KV>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_mfma(
-    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
+    const uint16_t* __restrict__ q_lat, const void* __restrict__ kv_v, KvPages pages,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Hm, int B,
     int T_max, int W, int nsplit, int ns8, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+  const uint16_t* __restrict__ kv = static_cast<const uint16_t*>(kv_v);
   __shared__ MlaShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,13 +110,23 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   const bool bok = b >= 0 && b < B;
   const size_t seq_base = size_t(bok ? b : 0) * T_max;
 
-  // ids of this wave's 16 tokens (lanes 0..15), -1 when absent or out of range
+  // ids of this wave's 16 tokens (lanes 0..15), -1 when absent or out of
+  // range; for a paged cache, the token's physical row (and its fp8 scale)
   int myid = -1;
+  float mysc = 1.f;
   if (lane < 16) {
     const int c = sp * kMlaSplit + 16 * w + lane;
     if (c < W) {
       const int id = token_ids[size_t(r) * W + c];
-      myid = (bok && id >= 0 && id < T_max) ? id : -1;
+      if (KV == kKvRows) {
+        myid = (bok && id >= 0 && id < T_max) ? id : -1;
+      } else if (bok && id >= 0 && id / pages.page_size < pages.max_pages) {
+        const int pg = pages.block_table[size_t(b) * pages.max_pages + id / pages.page_size];
+        if (pg >= 0 && pg < pages.num_pages) {
+          myid = pg * pages.page_size + id % pages.page_size;
+          if (KV == kKvPagedFp8) mysc = pages.scale[myid];
+        }
+      }
     }
   }
   // q_lat of the 16 heads straight into registers in the matrix-core B layout
@@ -115,16 +141,46 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   // gather: one row per instruction, lane i fills piece position i with piece
   // i ^ swz of the token's row; absent ids give a zero row
   uint32_t vmask = 0;
+  if (KV != kKvPagedFp8) {
+    const size_t base = KV == kKvRows ? seq_base : 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int id = __builtin_amdgcn_readlane(myid, i);
-    const int t = 16 * w + i;
-    if (id >= 0) {
-      vmask |= 1u << i;
-      const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[t][0]), 16, 0, 0);
-    } else {
-      *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) {
+      const int id = __builtin_amdgcn_readlane(myid, i);
+      const int t = 16 * w + i;
+      if (id >= 0) {
+        vmask |= 1u << i;
+        const uint16_t* src = kv + (base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[t][0]), 16, 0,
+                                         0);
+      } else {
+        *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
+    // fp8 rows (512 B): lane p loads the 8 codes of piece p of every row
+    // first, then widens them (hardware E4M3 decode, times the row's scale,
+    // rounded to bf16) into piece position p ^ swz of the row
+    const uint8_t* kv8 = static_cast<const uint8_t*>(kv_v);
+    u32x2 raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = __builtin_amdgcn_readlane(myid, i);
+      raw[i] = id >= 0 ? *reinterpret_cast<const u32x2*>(kv8 + size_t(id) * kMlaDl + 8 * lane) : u32x2{0u, 0u};
+      vmask |= (id >= 0 ? 1u : 0u) << i;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * w + i;
+      const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysc), i));
+      u32x4 v;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[i][h2]), false);
+        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[i][h2]), true);
+        v[2 * h2] = pack2bf(a[0] * sc, a[1] * sc);
+        v[2 * h2 + 1] = pack2bf(c2[0] * sc, c2[1] * sc);
+      }
+      *reinterpret_cast<u32x4*>(&sh.rows[t][8 * (lane ^ mla_swz(t))]) = v;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -828,12 +884,65 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
                                         align256(size_t(Q) * pl.nsplit * Hm * Dl * sizeof(uint16_t)));
   }
   dim3 grid((Hm / 16) * pl.ns8, Q);
-  hipLaunchKernelGGL(mla_decode_mfma, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
-                     (const uint16_t*)kv, row_seq, token_ids, Hm, B, T_max, W, pl.nsplit, pl.ns8,
+  hipLaunchKernelGGL(mla_decode_mfma<kKvRows>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat, kv,
+                     KvPages{nullptr, nullptr, 0, 1, 0}, row_seq, token_ids, Hm, B, T_max, W, pl.nsplit, pl.ns8,
                      scale_log2, (uint16_t*)out, lse, part_o, part_lse);
   int st = launch_status();
   if (st || pl.nsplit == 1) return st;
   hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, pl.nsplit,
                      Hm, (uint16_t*)out, lse);
+  return launch_status();
+}
+
+extern "C" size_t dsa_sparse_mla_paged_workspace_bytes(int Q, int Hm, int Dl, int W) {
+  if (Q <= 0 || Hm <= 0 || Dl <= 0 || W <= 0) return 0;
+  const int nsplit = (W + kMlaSplit - 1) / kMlaSplit;
+  if (nsplit == 1) return 0;
+  return align256(size_t(Q) * nsplit * Hm * Dl * sizeof(uint16_t)) + align256(size_t(Q) * nsplit * Hm * sizeof(float));
+}
+
+extern "C" int dsa_sparse_mla_decode_paged(const void* q_lat, const void* kv_pages, const float* kv_scale,
+                                           const int32_t* block_table, int max_pages, int page_size,
+                                           int num_pages, const int32_t* row_seq, const int32_t* token_ids,
+                                           int Q, int Hm, int Dl, int B, int W, float sm_scale, int kv_dtype,
+                                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!q_lat || !kv_pages || !block_table || !row_seq || !token_ids || !out) return DSA_ERR_NULL;
+  if (kv_dtype == DSA_FP8_E4M3 && !kv_scale) return DSA_ERR_NULL;
+  if (Q <= 0 || Hm <= 0 || Dl <= 0 || B <= 0 || W <= 0 || max_pages <= 0 || page_size <= 0 || num_pages <= 0)
+    return DSA_ERR_SHAPE;
+  if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (Dl != kMlaDl || Hm % 16 != 0 || Hm > 128 || Q > 65535) return DSA_ERR_UNSUPPORTED;
+  if (long(W) > long(kMlaSplit) * kMaxSplit) return DSA_ERR_UNSUPPORTED;
+  if (long(num_pages) * page_size > 2147483647L || long(max_pages) * page_size > 2147483647L)
+    return DSA_ERR_UNSUPPORTED;
+  const int nsplit = (W + kMlaSplit - 1) / kMlaSplit;
+  const int ns8 = (nsplit + 7) / 8 * 8;
+  const size_t need = dsa_sparse_mla_paged_workspace_bytes(Q, Hm, Dl, W);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  uint16_t* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (nsplit > 1) {
+    part_o = static_cast<uint16_t*>(workspace);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(size_t(Q) * nsplit * Hm * Dl * sizeof(uint16_t)));
+  }
+  hipStream_t s = as_stream(stream);
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const KvPages pg{block_table, kv_scale, max_pages, page_size, num_pages};
+  const int T_logical = max_pages * page_size;
+  dim3 grid((Hm / 16) * ns8, Q);
+  if (kv_dtype == DSA_BF16)
+    hipLaunchKernelGGL(mla_decode_mfma<kKvPaged>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat, kv_pages,
+                       pg, row_seq, token_ids, Hm, B, T_logical, W, nsplit, ns8, scale_log2, (uint16_t*)out, lse,
+                       part_o, part_lse);
+  else
+    hipLaunchKernelGGL(mla_decode_mfma<kKvPagedFp8>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
+                       kv_pages, pg, row_seq, token_ids, Hm, B, T_logical, W, nsplit, ns8, scale_log2,
+                       (uint16_t*)out, lse, part_o, part_lse);
+  int st = launch_status();
+  if (st || nsplit == 1) return st;
+  hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, nsplit, Hm,
+                     (uint16_t*)out, lse);
   return launch_status();
 }

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from .layout import pool_cache_pools
-from ._lib import DSA_BF16, DSA_F32, DSA_TOPK_COUNTER_BYTES, DsaError, check  # noqa: F401
+from ._lib import DSA_BF16, DSA_F32, DSA_FP8_E4M3, DSA_TOPK_COUNTER_BYTES, DsaError, check  # noqa: F401
 
 _ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
 
@@ -193,6 +193,48 @@ def dsa_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, out=No
         _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
         ws_ptr, ws_bytes, _stream())
     check("dsa_sparse_mla_decode", st)
+    return out, lse
+
+
+def dsa_sparse_mla_paged_workspace_bytes(Q: int, Hm: int, Dl: int, W: int) -> int:
+    return int(_lib.load().dsa_sparse_mla_paged_workspace_bytes(Q, Hm, Dl, W))
+
+
+def dsa_sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_size: int, row_seq, token_ids,
+                                sm_scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Sparse MLA over a paged latent cache: kv_pages [num_pages, page_size, Dl]
+    bf16, or uint8 OCP FP8 E4M3 codes with kv_scale [num_pages, page_size] fp32;
+    block_table [B, max_pages] int32.  -> (out [Q, Hm, Dl] bf16, lse [Q, Hm])."""
+    Q, Hm, Dl = q_lat.shape
+    num_pages, ps, Dl2 = kv_pages.shape
+    if Dl2 != Dl or ps != page_size:
+        raise ValueError("kv_pages disagrees with q_lat / page_size")
+    B, max_pages = block_table.shape
+    W = token_ids.shape[1]
+    if kv_pages.dtype == torch.bfloat16:
+        code, sc_ptr = DSA_BF16, None
+    elif kv_pages.dtype == torch.uint8:
+        if kv_scale is None or tuple(kv_scale.shape) != (num_pages, page_size):
+            raise ValueError("fp8 pages need kv_scale [num_pages, page_size]")
+        code, sc_ptr = DSA_FP8_E4M3, _dev(kv_scale, "kv_scale", torch.float32)
+    else:
+        raise ValueError(f"kv_pages dtype {kv_pages.dtype} not supported")
+    if out is None:
+        out = torch.empty((Q, Hm, Dl), dtype=torch.bfloat16, device=q_lat.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Q, Hm), dtype=torch.float32, device=q_lat.device)
+    need = dsa_sparse_mla_paged_workspace_bytes(Q, Hm, Dl, W)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.load().dsa_sparse_mla_decode_paged(
+        _dev(q_lat, "q_lat", torch.bfloat16), _dev(kv_pages, "kv_pages"), sc_ptr,
+        _dev(block_table, "block_table", torch.int32), max_pages, page_size, num_pages,
+        _dev(row_seq, "row_seq", torch.int32), _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, W,
+        float(sm_scale), code, _dev(out, "out", torch.bfloat16),
+        _dev(lse, "lse", torch.float32) if lse is not None else None, ws_ptr, ws_bytes, _stream())
+    check("dsa_sparse_mla_decode_paged", st)
     return out, lse
 
 

@@ -57,6 +57,9 @@ extern "C" {
 /* activation dtypes */
 #define DSA_F32   0
 #define DSA_BF16  1
+/* latent-cache code type of dsa_sparse_mla_decode_paged only: OCP FP8 E4M3
+ * bytes with one fp32 scale per token row */
+#define DSA_FP8_E4M3  2
 
 /*
  * The pool cache.  dsa_kpool_compress writes the pooled keys k_pool[b,p,c]
@@ -269,6 +272,35 @@ int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_
                           const int32_t* token_ids, int Q, int Hm, int Dl, int B, int T_max,
                           int W, float sm_scale, int dtype, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_decode_paged -- dsa_sparse_mla_decode over a paged latent
+ * cache, optionally stored as fp8.  "Module glm5next_dsa", module list
+ * ("attend": the launcher of the selected-index NoPE MLA *paged* decode) and
+ * "Constants" (the reference's mla_paged_decode and mla_paged_decode_fp8
+ * kernels).  The pages name the paged and fp8 variants but print no layout;
+ * this one is:
+ *   kv_pages     [num_pages, page_size, Dl]: bf16 (kv_dtype DSA_BF16) or OCP
+ *                FP8 E4M3 codes, one byte each (kv_dtype DSA_FP8_E4M3)
+ *   kv_scale     [num_pages, page_size] fp32: the latent value of an fp8 code
+ *                is decode(code) * scale of its row; NULL for bf16 pages
+ *   block_table  [B, max_pages] int32: physical page of page j of sequence b
+ * Token t of sequence b (the ids of token_ids, as in dsa_sparse_mla_decode)
+ * is row t % page_size of page block_table[b, t / page_size]; a token whose
+ * page index is >= max_pages or whose table entry is outside [0, num_pages)
+ * counts as absent, like -1.  fp8 rows are widened to bf16 (value * scale,
+ * rounded to nearest even) as they are gathered; the attention is then that of
+ * dsa_sparse_mla_decode.  q_lat and out are bf16; Dl must be 512, Hm a
+ * multiple of 16 up to 128.  Every row runs the split-ids path, so W > 64
+ * needs the workspace sized by dsa_sparse_mla_paged_workspace_bytes.  Other
+ * arguments, ownership and errors as for dsa_sparse_mla_decode.
+ */
+size_t dsa_sparse_mla_paged_workspace_bytes(int Q, int Hm, int Dl, int W);
+int dsa_sparse_mla_decode_paged(const void* q_lat, const void* kv_pages, const float* kv_scale,
+                                const int32_t* block_table, int max_pages, int page_size, int num_pages,
+                                const int32_t* row_seq, const int32_t* token_ids, int Q, int Hm, int Dl,
+                                int B, int W, float sm_scale, int kv_dtype, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

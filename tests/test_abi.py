@@ -164,3 +164,28 @@ def test_mla_refuses_bad_arguments_and_sizes_workspace(lib):
     assert call() == DSA_ERR_WORKSPACE
     assert call(ws=FAKE, wsb=need - 1) == DSA_ERR_WORKSPACE
     assert lib.dsa_sparse_mla_workspace_bytes(1, 4, 64, 32, 0) == 0   # fp32 path: no split
+
+
+def _paged(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, scale=FAKE, bt=FAKE, max_pages=4, page_size=64, num_pages=8, row_seq=FAKE,
+             tok=FAKE, Q=2, Hm=64, Dl=512, B=2, W=128, sm=0.04, dtype=2, out=FAKE, lse=None, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dsa_sparse_mla_decode_paged(*a.values())
+
+
+def test_paged_mla_refuses_bad_arguments_and_sizes_workspace(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
+    assert _paged(lib, bt=None) == DSA_ERR_NULL
+    assert _paged(lib, scale=None) == DSA_ERR_NULL            # fp8 pages need their scales
+    assert _paged(lib, page_size=0) == DSA_ERR_SHAPE
+    assert _paged(lib, num_pages=0) == DSA_ERR_SHAPE
+    assert _paged(lib, dtype=0) == DSA_ERR_UNSUPPORTED        # fp32 pages are not a paged format
+    assert _paged(lib, Dl=256) == DSA_ERR_UNSUPPORTED
+    assert _paged(lib, Hm=24) == DSA_ERR_UNSUPPORTED
+    assert _paged(lib, ws=None) == DSA_ERR_WORKSPACE
+    assert _paged(lib, ws_bytes=16) == DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 128) > 0
+    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 64) == 0   # one id slice
+    # the paged entry splits the ids for any row count (no many-rows path)
+    assert lib.dsa_sparse_mla_paged_workspace_bytes(4096, 64, 512, 2048) > 0

@@ -1,0 +1,99 @@
+"""GPU parity of the sparse MLA over a paged latent cache, bf16 or fp8 E4M3
+with a scale per token row (dsa_sparse_mla_decode_paged), against the oracle's
+paged attention (readings R12/R13 of the oracle: page table to physical rows,
+out-of-range pages absent, fp8 value = decode(code) * scale).
+
+Bars: bf16 pages are bit-equal to dsa_sparse_mla_decode on the same cache laid
+out contiguously (same gather, same arithmetic); both cache types are within
+2e-2 absolute of the oracle (the bf16 output bar), lse within 2e-3 relative.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_decode_amd import synth
+from oracle import dsa_oracle as O
+from tests.helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def ops():
+    from dsa_decode_amd import ops as _ops
+    return _ops
+
+
+def _case(B, T, Hm, Q, W, seed, hole_frac=0.1):
+    rng = np.random.default_rng(seed)
+    kv = torch.from_numpy(rng.standard_normal((B, T, 512)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((Q, Hm, 512)).astype(np.float32)).to(torch.bfloat16)
+    row_seq = (np.arange(Q) % B).astype(np.int32)
+    tok = synth.random_token_ids(Q, W, [T] * B, row_seq.tolist(), seed=seed, hole_frac=hole_frac).numpy()
+    return kv, q, row_seq, tok
+
+
+def _check(q, pg, ps, row_seq, tok, sm_scale, rows=None):
+    out, lse = ops().dsa_sparse_mla_decode_paged(
+        dev(q), dev(pg["kv_pages"]), dev(pg["kv_scale"]) if pg["kv_scale"] is not None else None,
+        dev(pg["block_table"]), ps, dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(tok.astype(np.int32))),
+        sm_scale)
+    rows = list(range(q.shape[0])) if rows is None else rows
+    ref_o, ref_l = O.sparse_mla_decode_paged(q, pg["kv_pages"], pg["kv_scale"], pg["block_table"], ps, row_seq,
+                                             tok, sm_scale, rows=rows)
+    g = out.float().cpu().numpy()[rows]
+    gl = lse.cpu().numpy()[rows]
+    err = np.abs(g - ref_o)
+    assert err.max() <= 2e-2, f"max out err {err.max()}"
+    fin = np.isfinite(ref_l)
+    assert (np.isfinite(gl) == fin).all()
+    assert np.abs(gl[fin] - ref_l[fin]).max(initial=0) <= 2e-3 * max(1.0, np.abs(ref_l[fin]).max(initial=1))
+    return out, lse
+
+
+@pytest.mark.parametrize("Hm,W,ps", [(64, 2048, 64), (16, 60, 16), (128, 300, 128), (32, 1000, 1)])
+def test_paged_bf16_matches_contiguous_bitwise_and_oracle(Hm, W, ps):
+    B, T, Q = 2, 4096, 3
+    kv, q, row_seq, tok = _case(B, T, Hm, Q, W, seed=Hm + W + ps)
+    tok[2, : min(W, 70)] = -1
+    pg = synth.paged_latent(kv, ps, seed=ps)
+    out, lse = _check(q, pg, ps, row_seq, tok, 512 ** -0.5)
+    c_out, c_lse = ops().dsa_sparse_mla_decode(dev(q), dev(kv), dev(torch.from_numpy(row_seq)),
+                                               dev(torch.from_numpy(tok.astype(np.int32))), 512 ** -0.5)
+    assert torch.equal(out.view(torch.int16), c_out.view(torch.int16))
+    assert torch.equal(lse, c_lse)
+
+
+@pytest.mark.parametrize("Hm,W,ps", [(64, 2048, 64), (16, 64, 32), (64, 700, 16)])
+def test_paged_fp8_matches_oracle(Hm, W, ps):
+    B, T, Q = 3, 4096, 4
+    kv, q, row_seq, tok = _case(B, T, Hm, Q, W, seed=3 * Hm + W + ps)
+    tok[1, :] = -1                                   # a row with nothing selected
+    pg = synth.paged_latent(kv, ps, seed=ps + 1, fp8=True)
+    _check(q, pg, ps, row_seq, tok, 512 ** -0.5)
+
+
+def test_paged_out_of_range_pages_and_tokens_are_absent():
+    B, T, Hm, Q, W, ps = 2, 2048, 64, 2, 500, 32
+    kv, q, row_seq, tok = _case(B, T, Hm, Q, W, seed=11, hole_frac=0.0)
+    for fp8 in (False, True):
+        pg = synth.paged_latent(kv, ps, seed=12, fp8=fp8)
+        bt = pg["block_table"].clone()
+        bt[row_seq[0], int(tok[0, 0]) // ps] = pg["num_pages"] + 3   # a table entry past the pages
+        bt[row_seq[1], int(tok[1, 0]) // ps] = -2                      # a negative entry
+        tk = tok.copy()
+        tk[0, 1] = bt.shape[1] * ps + 5                                # a token past the table
+        pg = dict(pg, block_table=bt)
+        _check(q, pg, ps, row_seq, tk, 512 ** -0.5)
+
+
+def test_paged_fp8_long_context_rows():
+    # the long-context decode shape: 4 sequences x 262144 tokens in 64-token fp8
+    # pages, 2048 listed tokens per row, 64 heads
+    wl = synth.workload("long")
+    mi = synth.mla_inputs(wl)
+    rng = np.random.default_rng(262144)
+    tok = np.stack([rng.choice(wl.T_max, wl.W, replace=False) for _ in range(wl.Q)]).astype(np.int32)
+    pg = synth.paged_latent(mi["kv"], 64, seed=64, fp8=True)
+    _check(mi["q_lat"], pg, 64, np.arange(wl.Q, dtype=np.int32), tok, mi["sm_scale"])
