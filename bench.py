@@ -96,6 +96,8 @@ def _parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 64 MiB device copy first (a known-size kernel for counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the extra timing of the sparse MLA over a paged (bf16, fp8) latent cache")
     ap.add_argument("--workload", choices=["long", "prefill"], default="long",
                     help="long: the decode step (the headline line); prefill: the 4096-row prefill chunk's "
                          "scores + top-k + expand, reported against the MFMA roofline")
@@ -284,6 +286,8 @@ def main() -> int:
     achieved = bytes_per_launch / (score_us_mean * 1e-6) / 1e9
     steps_per_s = 1e3 / ms_per_step
 
+    paged = None if args.no_paged else paged_mla_stages(wl, mi, q_lat, row_seq, reps[0]["tok"], stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, ip, mi, comp, args.cpu_seconds)
@@ -308,6 +312,7 @@ def main() -> int:
                    "replicas": REPLICAS},
         "tokens_per_s": round(steps_per_s * Q, 1),
         "stages_us": stages_us,
+        "paged_mla_us": paged,
         "host_issue_us_per_step": round(host_issue_us, 2),
         "roofline": {"bound": "hbm", "kernel": "index_scores_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -317,6 +322,49 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def paged_mla_stages(wl, mi, q_lat, row_seq, tok, stream, calls: int = 64) -> dict:
+    """Event-timed dsa_sparse_mla_decode_paged (main + combine launches) on the
+    step's token ids, over the same latent cache laid out in 64-token pages:
+    bf16 pages (1 KiB gathered per token) and fp8 E4M3 pages with a per-row
+    scale (512 B + 4 B).  Eight shifted copies of the id lists rotate so that
+    the gathered rows do not stay in the last-level cache between calls."""
+    import torch
+    from dsa_decode_amd import ops, synth
+
+    res = {}
+    Q, W = tok.shape
+    toks = [((tok.long() + k * 8192) % wl.T_max).to(torch.int32).contiguous() for k in range(8)]
+    toks = [torch.where(tok >= 0, t, tok) for t in toks]
+    for name, fp8 in (("bf16_pages", False), ("fp8_pages", True)):
+        pg = synth.paged_latent(mi["kv"], 64, seed=64, fp8=fp8)
+        kvp = pg["kv_pages"].cuda()
+        sc = pg["kv_scale"].cuda() if fp8 else None
+        bt = pg["block_table"].cuda()
+        del pg
+        out = torch.empty((Q, wl.Hm, wl.Dl), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((Q, wl.Hm), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, ops.dsa_sparse_mla_paged_workspace_bytes(Q, wl.Hm, wl.Dl, W)), dtype=torch.uint8,
+                         device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            run = lambda k: ops.dsa_sparse_mla_decode_paged(q_lat, kvp, sc, bt, 64, row_seq, toks[k % 8],
+                                                            mi["sm_scale"], out=out, lse=lse, workspace=ws)
+            for k in range(8):
+                run(k)
+            stream.synchronize()
+            ev = TimingEvents(2 * calls)
+            for k in range(calls):
+                ev.record(2 * k, stream.cuda_stream)
+                run(k)
+                ev.record(2 * k + 1, stream.cuda_stream)
+            stream.synchronize()
+        res[name] = round(float(sorted(ev.elapsed_us(2 * k, 2 * k + 1) for k in range(calls))[calls // 2]), 2)
+        ev.close()
+        del kvp, sc, bt
+        torch.cuda.synchronize()
+    return res
 
 
 def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
