@@ -39,6 +39,14 @@ muts = [
  ("w row 0 for all rows", "s = (w[r][None, :]", "s = (w[0][None, :]"),
  ("scores rows seq", "b = int(row_seq[r])\n        if b not in normed", "b = 0\n        if b not in normed"),
  ("empty ids", "ids = token_ids[r][token_ids[r] >= 0]", "ids = np.abs(token_ids[r])"),
+ ("fp8 bias 8", "(1.0 + m / 8.0) * np.ldexp(1.0, e - 7)", "(1.0 + m / 8.0) * np.ldexp(1.0, e - 8)"),
+ ("fp8 no subnormals", "np.where(e == 0, (m / 8.0) * 2.0 ** -6,", "np.where(e == 0, 0.0 * m,"),
+ ("fp8 no nan", "mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)", "pass"),
+ ("fp8 scale ignored", "return vals * f64(kv_scale).reshape(-1, 1)", "return vals"),
+ ("page row from page start", "out[r, c] = pg * page_size + t % page_size", "out[r, c] = pg * page_size"),
+ ("page by token not table", "pg = int(bt[b, t // page_size])", "pg = t // page_size"),
+ ("page table of sequence 0", "pg = int(bt[b, t // page_size])", "pg = int(bt[0, t // page_size])"),
+ ("out-of-range page kept", "if 0 <= pg < num_pages:", "if True:"),
 ]
 
 
