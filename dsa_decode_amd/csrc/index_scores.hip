@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-// Prefill kernel.  A workgroup keeps 4 x 64 pools' keys in registers (wave w:
+// Prefill kernel.  A workgroup of WPB waves keeps WPB x 64 pools' keys in registers (wave w:
 // 4 tiles) and runs a group of rows of one sequence over them, staging the
 // folded operands of RPB rows at a time in LDS.  The LayerNorm statistics of
 // a pool do not depend on the row, so they are formed once per tile when the
@@ -358,8 +358,8 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // epilogue, the MFMAs of tile t+1 issued before the epilogue of tile t.  After
 // the lane-group sum every lane holds a tile's scores: lane (kg, ln) keeps
 // tile kg's, so a row's 64 pools per wave go out in one 256-byte store.
-template <int NH, int RPB, int KT>
-__global__ __launch_bounds__(kIsThreads) void index_scores_rows(
+template <int NH, int RPB, int KT, int WPB>
+__global__ __launch_bounds__(WPB * 64) void index_scores_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   const int diag_addr = 4 * (16 * (ln >> 2) + ln);
   const int r_begin = blockIdx.y * rows_per_group;
   const int r_end = min(Q, r_begin + rows_per_group);
-  const int p_wave = blockIdx.x * (kIsWaves * kTiles * 16) + wave * (kTiles * 16);
+  const int p_wave = blockIdx.x * (WPB * kTiles * 16) + wave * (kTiles * 16);
   // the pools whose scores this lane stores: tile kg + 4 u, pool ln
   int p_mine[NS];
 #pragma unroll
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kIsThreads) void index_scores_rows(
   for (int rb = r_begin; rb < r_end; rb += RPB) {
     const int nr = min(RPB, r_end - rb);
     __syncthreads();  // the previous batch's LDS reads are finished
-    for (int u = tid; u < nr * H * 8; u += kIsThreads) {
+    for (int u = tid; u < nr * H * 8; u += WPB * 64) {
       const int rr = u / (H * 8);
       const RowIn rin = stage_row_load(q + size_t(rb + rr) * H * kIsD, w + size_t(rb + rr) * H, gamma, beta,
                                        u - rr * H * 8);
@@ -558,6 +558,11 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 }
 
 // Launch shapes of the MFMA path.
+// prefill kernel: waves per workgroup (8: 512 pools per workgroup, so each row's
+// folded operands are staged by half as many workgroups as with 4 waves; 2.84
+// -> 2.44 ms on the prefill chunk; 207 registers leave room for one such
+// workgroup per CU)
+constexpr int kRowsWaves = 8;
 constexpr int kRowsTiles = 4;  // prefill kernel: key tiles per wave (256 pools per workgroup; 8 needs 316 registers, one wave per SIMD, and measured 10 % slower)
 // Decode launch shape (tuned on MI355X at 4 x 65536 pools)
 struct IsPlan {
@@ -581,7 +586,7 @@ static IsPlan is_plan(int Q, int P_max) {
   }
   // many rows: groups of rows of one sequence share the keys held in registers
   pl.rows = true;
-  const long chunks = (P_max + kIsWaves * kRowsTiles * 16 - 1) / (kIsWaves * kRowsTiles * 16);
+  const long chunks = (P_max + kRowsWaves * kRowsTiles * 16 - 1) / (kRowsWaves * kRowsTiles * 16);
   int groups = int((2048 + chunks - 1) / chunks);
   if (groups < 1) groups = 1;
   const int per = (Q + groups - 1) / groups;
@@ -628,10 +633,11 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
 #undef DSA_IS_STREAM
       return launch_status();
     }
-    dim3 grid(ceil_div(P_max, kIsWaves * kRowsTiles * 16), ceil_div(Q, pl.rows_per_group));
+    dim3 grid(ceil_div(P_max, kRowsWaves * kRowsTiles * 16), ceil_div(Q, pl.rows_per_group));
     if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
 #define DSA_IS_ROWS(NH)                                                                               \
-  hipLaunchKernelGGL((index_scores_rows<NH, 4, kRowsTiles>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, \
+  hipLaunchKernelGGL((index_scores_rows<NH, 4, kRowsTiles, kRowsWaves>), grid, dim3(kRowsWaves * 64), 0, s,       \
+                     (const uint16_t*)q,                                                                  \
                      w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
                      ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
     if (H == 32) DSA_IS_ROWS(2);
