@@ -172,8 +172,10 @@ def main() -> int:
     mi = synth.mla_inputs(wl)
 
     # pool cache: one compress on the GPU, then replicas
-    comp = ops.dsa_kpool_compress(dev(ti["k"]), dev(ti["gate"]), dev(ti["valid"]), dev(ti["ape"]),
-                                  dev(ti["seq_len"]), wl.kp, P)
+    tok_dev = dict(k=dev(ti["k"]), gate=dev(ti["gate"]), valid=dev(ti["valid"]), ape=dev(ti["ape"]),
+                   seq_len=dev(ti["seq_len"]))
+    comp = ops.dsa_kpool_compress(tok_dev["k"], tok_dev["gate"], tok_dev["valid"], tok_dev["ape"],
+                                  tok_dev["seq_len"], wl.kp, P)
     del ti
     kv0 = dev(mi["kv"])
     reps = []
@@ -287,6 +289,8 @@ def main() -> int:
     steps_per_s = 1e3 / ms_per_step
 
     paged = None if args.no_paged else paged_mla_stages(wl, mi, q_lat, row_seq, reps[0]["tok"], stream)
+    append_us = append_stage_us(wl, tok_dev, comp, stream)
+    del tok_dev
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -313,6 +317,7 @@ def main() -> int:
         "tokens_per_s": round(steps_per_s * Q, 1),
         "stages_us": stages_us,
         "paged_mla_us": paged,
+        "kpool_append_us": append_us,
         "host_issue_us_per_step": round(host_issue_us, 2),
         "roofline": {"bound": "hbm", "kernel": "index_scores_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -322,6 +327,33 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def append_stage_us(wl, tok_dev, comp, stream, calls: int = 64) -> float:
+    """Event-timed dsa_kpool_append for one decode token of every sequence that
+    completes a pool: the state is rewound by one pool per sequence before each
+    call (outside the timed events), so each call forms the newest pool of all
+    4 sequences again, as the step that fills a pool would."""
+    import torch
+    from dsa_decode_amd import ops
+
+    st = {k: comp[k].clone() for k in ("k_pool", "pool_start", "pool_valid", "n_pools", "first_valid")}
+    n_full = st["n_pools"].clone()
+    n_back = (n_full - 1).clamp_min(0)
+    call = ops.bind_kpool_append(tok_dev["k"], tok_dev["gate"], tok_dev["valid"], tok_dev["ape"],
+                                 tok_dev["seq_len"], wl.kp, st, 1)
+    ev = TimingEvents(2 * calls)
+    with torch.cuda.stream(stream):
+        for k in range(calls):
+            st["n_pools"].copy_(n_back)
+            ev.record(2 * k, stream.cuda_stream)
+            call()
+            ev.record(2 * k + 1, stream.cuda_stream)
+        stream.synchronize()
+    assert torch.equal(st["n_pools"], n_full)
+    us = sorted(ev.elapsed_us(2 * k, 2 * k + 1) for k in range(calls))[calls // 2]
+    ev.close()
+    return round(float(us), 2)
 
 
 def paged_mla_stages(wl, mi, q_lat, row_seq, tok, stream, calls: int = 64) -> dict:
