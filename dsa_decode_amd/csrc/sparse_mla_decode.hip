@@ -477,39 +477,38 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // Many-rows path for 64 heads: one workgroup per row holds all 64 heads, so
-// each gathered latent row lands in LDS once for every head of the row.  Per
-// 64-id block:
-//   - every wave holds the block's 64 ids (one per lane; a ballot gives the
-//     validity of all 64) and gathers the rows of ids 16w .. 16w+15 into LDS;
-//     the rows of block i+1 are gathered into the second buffer while block i
-//     is computed;
-//   - wave w forms the logits of heads 16w .. 16w+15 over all 64 tokens (kv
-//     rows from LDS x q^T from registers, four token tiles), so the softmax of
-//     its heads needs no other wave: it keeps the running maximum and sum of
-//     its heads, writes P relative to the new maximum (bf16) and the rescale
-//     factor 2^(M_old - M_new) of each head to LDS;
-//   - wave w then accumulates latent quarter w of O^T for all 64 heads (kv^T
-//     from the transposing LDS reads, each fragment used for the four head
-//     tiles; P^T from LDS), rescaling its accumulators by the heads' factors.
-// The final sums cross waves once through LDS.  LDS: two 64 KiB row buffers
-// + 9 KiB of P; one workgroup per CU (the 128 accumulators per lane and the
-// row's q_lat in registers allow one wave per SIMD).
-struct alignas(16) Mla64Shared {
+// each gathered latent row lands in LDS once for every head of the row.  Eight
+// waves, two per SIMD (240 registers: each wave holds 64 accumulators, not the
+// 128 a latent quarter would need).  Wave w forms the
+// logits of heads 16 (w & 3) .. +15 over token half w >> 2 of each 64-id block
+// (q^T of its 16 heads in registers), and accumulates latent eighth w of O^T
+// for all 64 heads (64 accumulators per lane instead of 128).  The two token
+// halves of a head meet in LDS: each wave writes P relative to its own maximum
+// with that maximum and its sum; every wave then forms, for each of the 64
+// heads, the new running maximum, the rescale 2^(M_old - M_new) of its
+// accumulators and the factors 2^(m_half - M_new) it applies to P as it reads
+// it (all waves form the same values from the same LDS words).  Rows are
+// gathered 8 per wave, the next block into the second buffer while this one
+// is computed.
+struct alignas(16) Mla64x8Shared {
   uint16_t rows[2][kMlaSplit][kMlaDl];  // latent rows, pieces swizzled by mla_swz
-  uint16_t p[64][kMlaSplit + 8];        // P[head][token], rows padded to 144 B
-  float alpha[64];                      // per head: rescale of the running sums in this block
-  float l[64];                          // per head: final sum of P
+  uint16_t p[64][kMlaSplit + 8];        // P[head][token] relative to its half's maximum
+  float m[64][2];                       // per head and token half: maximum (log2 domain, 0 if none)
+  float l[64][2];                       // per head and token half: sum of P
 };
 
-__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))) void mla_rows64_mfma(
+constexpr int kMla8Threads = 512;
+
+__global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2))) void mla_rows64w8_mfma(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Q, int B, int T_max,
     int W, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int Hm = 64;
-  __shared__ Mla64Shared sh;
+  __shared__ Mla64x8Shared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
+  const int hgw = w & 3, th = w >> 2;
   const int r = blockIdx.x;
   const int b = row_seq[r];
   const bool bok = b >= 0 && b < B;
@@ -517,22 +516,21 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
   const int32_t* ids_row = token_ids + size_t(r) * W;
   const int nblk = (W + kMlaSplit - 1) / kMlaSplit;
 
-  // raw id of token `lane` of block blk (-1 past the list) and its check
-  // (-1 when absent or out of range), kept apart so that the next block's id
-  // load is not waited for right after the gather it would otherwise follow
   auto load_raw = [&](int blk) {
     const int c = blk * kMlaSplit + lane;
     return (blk < nblk && c < W) ? ids_row[c] : -1;
   };
   auto check_id = [&](int v) { return (bok && v >= 0 && v < T_max) ? v : -1; };
-  // rows 16w .. 16w+15 of the block whose ids `ids` holds, into buffer `buf`
+  // rows 8w .. 8w+7 of the block whose ids `ids` holds, into buffer `buf`
   auto gather = [&](int ids, int buf) {
+    int lg = lane;
+    asm volatile("" : "+v"(lg));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * w + i;
+    for (int i = 0; i < 8; ++i) {
+      const int t = 8 * w + i;
       const int id = __builtin_amdgcn_readlane(ids, t);
       if (id >= 0) {
-        const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
+        const uint16_t* src = kv + (seq_base + size_t(id)) * kMlaDl + 8 * (lg ^ mla_swz(t));
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[buf][t][0]), 16,
                                          0, 0);
       } else {
@@ -541,9 +539,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
     }
   };
   int cur_id = check_id(load_raw(0));
-  // q_lat of heads 16w .. 16w+15 in registers (lane (kg, ln): head 16w + ln,
-  // 16-byte piece 4j + kg of the latent for k-step j)
-  const int hq = 16 * w + ln;
+  const int hq = 16 * hgw + ln;  // the head whose logits this lane forms
   u32x4 qv[16];
   {
     const uint16_t* qrow = q_lat + (size_t(r) * Hm + hq) * kMlaDl + 8 * kg;
@@ -552,14 +548,15 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
   }
   gather(cur_id, 0);
   int nxt_raw = load_raw(1);
-  float M_run = -INFINITY, l_run = 0.f;  // head hq
-  f32x4 o[4][8];                         // [head tile][16-wide latent block of quarter w]
+  float M_run[4], l_run[4];  // heads 16 ht + ln
+  f32x4 o[4][4];             // [head tile][16-wide latent block of eighth w]
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
+  for (int ht = 0; ht < 4; ++ht) {
+    M_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[ht][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // logits reads: token row 16t + ln has swizzle mla_swz(ln), so the piece of
-  // k-step k is 4 * (k ^ s2) + (kg ^ s1): four lane bases, the rest constant
+    for (int k = 0; k < 4; ++k) o[ht][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const int swl = mla_swz(ln);
   int lbase[4];
 #pragma unroll
@@ -577,82 +574,98 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
     }
     const uint16_t* rows = &sh.rows[cur][0][0];
 
-    // logits of tokens 16t + 4kg + j (t < 4, j < 4) for head hq
-    f32x4 acc[4];
+    // logits of tokens 32 th + 16 t + 4 kg + j (t < 2, j < 4) for head hq
+    f32x4 acc[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      bf16x8 a[4];
+      bf16x8 a[2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[k & 3] + 16 * t * kMlaDl + (k >> 2) * 128));
+      for (int t = 0; t < 2; ++t)
+        a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[k & 3] + (32 * th + 16 * t) * kMlaDl +
+                                                         (k >> 2) * 128));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[k]), acc[t]);
+      for (int t = 0; t < 2; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[k]), acc[t]);
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tok = 16 * t + 4 * kg + j;
+        const int tok = 32 * th + 16 * t + 4 * kg + j;
         acc[t][j] = (vmask >> tok) & 1ull ? acc[t][j] * scale_log2 : -INFINITY;
         m = fmaxf(m, acc[t][j]);
       }
     m = fmaxf(m, __shfl_xor(m, 16, kWave));
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const float M_new = fmaxf(M_run, m);
-    const float M_use = M_new == -INFINITY ? 0.f : M_new;
-    const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
-    float lb = 0.f;
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float lh = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(acc[t][j] - M_use);
-        lb += p[j];
+        p[j] = __builtin_amdgcn_exp2f(acc[t][j] - m_use);
+        lh += p[j];
       }
-      *reinterpret_cast<u32x2*>(&sh.p[hq][16 * t + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+      *reinterpret_cast<u32x2*>(&sh.p[hq][32 * th + 16 * t + 4 * kg]) =
+          u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
     }
-    lb += __shfl_xor(lb, 16, kWave);
-    lb += __shfl_xor(lb, 32, kWave);
-    l_run = fmaf(l_run, alpha, lb);
-    M_run = M_new;
-    if (kg == 0) sh.alpha[hq] = alpha;
-    // P and the rescale factors of all 64 heads published: LDS writes done,
-    // then the barrier alone (a full __syncthreads would also wait for the
-    // next block's gather, which must stay in flight)
+    lh += __shfl_xor(lh, 16, kWave);
+    lh += __shfl_xor(lh, 32, kWave);
+    if (kg == 0) {
+      sh.m[hq][th] = m_use;
+      sh.l[hq][th] = lh;
+    }
+    // P and the halves' maxima and sums of all 64 heads published: LDS writes
+    // done, then the barrier alone (the next block's gather stays in flight)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // O^T over latent quarter w for the four head tiles: A = kv^T (16 dl x 32
-    // tokens, two transposing reads), B = P^T (32 tokens x 16 heads)
+    // merge the two halves into each head's running sums (the factors of the
+    // halves are applied to P^T as it is read, one token half at a time)
+    float fh[4][2];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-      const float av = sh.alpha[16 * ht + ln];
+      const int h = 16 * ht + ln;
+      const f32x2 mh = *reinterpret_cast<const f32x2*>(&sh.m[h][0]);
+      const f32x2 lhv = *reinterpret_cast<const f32x2*>(&sh.l[h][0]);
+      const float Mb = fmaxf(lhv[0] > 0.f ? mh[0] : -INFINITY, lhv[1] > 0.f ? mh[1] : -INFINITY);
+      const float M_new = fmaxf(M_run[ht], Mb);
+      const float M_use = M_new == -INFINITY ? 0.f : M_new;
+      const float alpha = M_run[ht] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run[ht] - M_use);
+      fh[ht][0] = lhv[0] > 0.f ? __builtin_amdgcn_exp2f(mh[0] - M_use) : 0.f;
+      fh[ht][1] = lhv[1] > 0.f ? __builtin_amdgcn_exp2f(mh[1] - M_use) : 0.f;
+      l_run[ht] = fmaf(l_run[ht], alpha, fmaf(fh[ht][0], lhv[0], fh[ht][1] * lhv[1]));
+      M_run[ht] = M_new;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[ht][k] *= av;
+      for (int kk = 0; kk < 4; ++kk) o[ht][kk] *= alpha;
     }
-    // the piece of column block blk in token rows t0 (t1 = t0 + 4) is
-    // 16w + 2 (blk ^ s3) + e (e ^ 1 for t1); s3 is recomputed per block so
-    // that the 32 addresses are not held across the loop
-    int s3 = (ln >> 2) + 4 * (kg & 1);
-    asm volatile("" : "+v"(s3));
-    const int e = (ln & 3) >> 1, off = 4 * (ln & 1);
+    // O^T over latent eighth w: A = kv^T (16 dl x 32 tokens, two transposing
+    // reads), B = P^T (32 tokens x 16 heads); addresses recomputed per block
+    int lv = lane;
+    asm volatile("" : "+v"(lv));
+    const int kgv = lv >> 4, lnv = lv & 15;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pb[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-        pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][32 * ks + 8 * kg]));
-      const int t0 = 32 * ks + 8 * kg + (ln >> 2);
-      const uint16_t* r0 = rows + t0 * kMlaDl + off;
-      const uint16_t* r1 = r0 + 4 * kMlaDl;
+      for (int ht = 0; ht < 4; ++ht) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][32 * ks + 8 * kg]);
+        const float f = fh[ht][ks];
+        u32x4 sc;
 #pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        const int pc = 16 * w + 2 * (blk ^ s3);
-        const u32x2 lo = lds_read_tr16(r0 + (pc + e) * 8);
-        const u32x2 hi = lds_read_tr16(r1 + (pc + (e ^ 1)) * 8);
+        for (int e = 0; e < 4; ++e)
+          sc[e] = pack2bf(__uint_as_float(raw[e] << 16) * f, __uint_as_float(raw[e] & 0xffff0000u) * f);
+        pb[ht] = as_bf16x8(sc);
+      }
+      const int t0 = 32 * ks + 8 * kgv + (lnv >> 2), t1 = t0 + 4;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int col = 64 * w + 16 * blk + 4 * (lnv & 3);
+        const int pc = col >> 3, off = col & 7;
+        const u32x2 lo = lds_read_tr16(rows + t0 * kMlaDl + ((pc ^ mla_swz(t0)) << 3) + off);
+        const u32x2 hi = lds_read_tr16(rows + t1 * kMlaDl + ((pc ^ mla_swz(t1)) << 3) + off);
         const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) o[ht][blk] = mfma16x16x32(av, pb[ht], o[ht][blk]);
@@ -660,23 +673,21 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1))
     }
   }
 
-  if (kg == 0) sh.l[hq] = l_run;
-  if (kg == 0 && lse)
-    lse[size_t(r) * Hm + hq] = l_run > 0.f ? (M_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
-  __syncthreads();
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int h = 16 * ht + ln;
-    const float lh = sh.l[h];
-    const float inv = lh > 0.f ? 1.0f / lh : 0.f;
-    uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
+    const float inv = l_run[ht] > 0.f ? 1.0f / l_run[ht] : 0.f;
+    uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 64 + 4 * kg;
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
+    for (int blk = 0; blk < 4; ++blk) {
       u32x2 pkd;
       pkd[0] = pack2bf(o[ht][blk][0] * inv, o[ht][blk][1] * inv);
       pkd[1] = pack2bf(o[ht][blk][2] * inv, o[ht][blk][3] * inv);
       *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
     }
+    if (w == 0 && kg == 0 && lse)
+      lse[size_t(r) * Hm + h] =
+          l_run[ht] > 0.f ? (M_run[ht] + __builtin_amdgcn_logf(l_run[ht])) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -864,7 +875,7 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   if (pl.rows && Hm == 64) {
-    hipLaunchKernelGGL(mla_rows64_mfma, dim3(Q), dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
+    hipLaunchKernelGGL(mla_rows64w8_mfma, dim3(Q), dim3(kMla8Threads), 0, s, (const uint16_t*)q_lat,
                        (const uint16_t*)kv, row_seq, token_ids, Q, B, T_max, W, scale_log2, (uint16_t*)out,
                        lse);
     return launch_status();
