@@ -137,6 +137,16 @@ def measured_traffic():
         return None
 
 
+def step_algorithmic_bytes(Q: int, P: int, K: int, W: int, Hm: int, Dl: int, score_bytes: int) -> int:
+    """Bytes one decode step must move at least: the score launch's bytes, the
+    top-k reading the scores and writing pool ids and token ids, the sparse MLA
+    reading each listed latent row once plus q_lat and writing out and lse
+    (bf16 activations, 4-byte scores, ids and lse)."""
+    topk = Q * P * 4 + Q * K * 4 + Q * W * 4
+    mla = Q * W * Dl * 2 + Q * Hm * Dl * 2 + Q * Hm * Dl * 2 + Q * Hm * 4 + Q * W * 4
+    return score_bytes + topk + mla
+
+
 def score_bytes_per_pool() -> int:
     # key row (128 bf16) + pool_valid (u8) + pool_start (i32) read, score (fp32) written
     return 128 * 2 + 1 + 4 + 4
@@ -287,6 +297,7 @@ def main() -> int:
     bytes_per_launch = score_bytes_per_pool() * Q * P + q.numel() * 2 + w.numel() * 4 + 2 * 128 * 4
     achieved = bytes_per_launch / (score_us_mean * 1e-6) / 1e9
     steps_per_s = 1e3 / ms_per_step
+    step_bytes = step_algorithmic_bytes(Q, P, K, W, wl.Hm, wl.Dl, bytes_per_launch)
 
     paged = None if args.no_paged else paged_mla_stages(wl, mi, q_lat, row_seq, reps[0]["tok"], stream)
     append_us = append_stage_us(wl, tok_dev, comp, stream)
@@ -315,6 +326,9 @@ def main() -> int:
                    "batch": Q, "context": wl.T_max, "kpool": wl.kp, "select_k": K, "mode": args.mode,
                    "replicas": REPLICAS},
         "tokens_per_s": round(steps_per_s * Q, 1),
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "stages_us": stages_us,
         "paged_mla_us": paged,
         "kpool_append_us": append_us,

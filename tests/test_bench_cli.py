@@ -50,3 +50,14 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.measured_traffic() is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
     assert bench.measured_traffic() is None
+
+
+def test_step_algorithmic_bytes():
+    # the long-context decode step: 4 rows x 65536 pools, K 512, W 2048, 64 x 512 latent
+    import bench
+    score = bench.score_bytes_per_pool() * 4 * 65536 + 4 * 32 * 128 * 2 + 4 * 32 * 4 + 2 * 128 * 4
+    total = bench.step_algorithmic_bytes(4, 65536, 512, 2048, 64, 512, score)
+    gathered = 4 * 2048 * 1024                       # each listed latent row once
+    assert total == score + 4 * 65536 * 4 + 4 * 512 * 4 + 4 * 2048 * 4 + gathered + 2 * 4 * 64 * 512 * 2 \
+        + 4 * 64 * 4 + 4 * 2048 * 4
+    assert 78e6 < total < 80e6                       # ~78.5 MB: 9.8 us at 8 TB/s
