@@ -37,13 +37,18 @@ design notes of the repository):
       argument.
   R11 Pools p >= n_pools (and every pool of a sequence with no valid token) are
       written as k_pool = 0, pool_start = -1, pool_valid = 0.
-  R12 Paged latent cache (the page names a paged decode and an fp8 variant of
+  R12 A sequence with no valid token has no pools; its first_valid is reported
+      as its length.
+  R13 (workload, not arithmetic) The prefill chunk is the last 4096 tokens of
+      its sequence, and exact score ties come from pooled keys drawn on the 1/8
+      grid from a small codebook with q on the same grid.
+  R14 Paged latent cache (the page names a paged decode and an fp8 variant of
       it only by file name): physical pages [num_pages, page_size, Dl]; a page
       table [B, max_pages] maps page j of sequence b to a physical page, so
       token t of sequence b is row t % page_size of page
       block_table[b, t // page_size].  A token whose page index or table entry
       is out of range counts as absent (like -1).
-  R13 fp8 latent cache: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias
+  R15 fp8 latent cache: OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias
       7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN) and one
       fp32 scale per token row; the latent value is decode(code) * scale.
 """
@@ -282,7 +287,7 @@ def sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, rows=None)
 
 
 # --------------------------------------------------------------------------
-# paged and fp8 latent cache (readings R12, R13): the attention above over a
+# paged and fp8 latent cache (readings R14, R15): the attention above over a
 # latent cache stored in pages, optionally as fp8 E4M3 codes with a scale per
 # token row.  [DSA] module list: "attend", the launcher of the selected-index
 # NoPE MLA *paged* decode; "Constants": mla_paged_decode{,_fp8}.
@@ -312,7 +317,7 @@ def paged_latent_rows(kv_pages, kv_scale=None) -> np.ndarray:
 
 
 def paged_token_rows(token_ids, row_seq, block_table, page_size: int, num_pages: int) -> np.ndarray:
-    """Physical row of each listed token (R12): -1 for -1 entries and for tokens
+    """Physical row of each listed token (R14): -1 for -1 entries and for tokens
     whose page index or page-table entry is out of range."""
     tok = _i(token_ids); row_seq = _i(row_seq); bt = _i(block_table)
     max_pages = bt.shape[1]
@@ -332,7 +337,7 @@ def paged_token_rows(token_ids, row_seq, block_table, page_size: int, num_pages:
 def sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_size: int, row_seq, token_ids,
                             sm_scale: float, rows=None):
     """sparse_mla_decode over a paged (optionally fp8) latent cache: each listed
-    token is resolved to its physical row (R12), the rows are dequantized (R13),
+    token is resolved to its physical row (R14), the rows are dequantized (R15),
     and the same softmax attention is taken over them."""
     num_pages = int(np.asarray(kv_pages.shape)[0])
     phys = paged_token_rows(token_ids, row_seq, block_table, page_size, num_pages)

@@ -407,7 +407,7 @@ def test_expand_id_naming_no_pool_gives_sentinel():
     assert tok.tolist() == [[6, 7, 8, 9] + [-1] * 10]
 
 
-# ------------------------------------------------------------------ paged / fp8 latent (R12, R13)
+# ------------------------------------------------------------------ paged / fp8 latent (R14, R15)
 def test_fp8_e4m3_decode_matches_torch_and_closed_forms():
     codes = np.arange(256, dtype=np.uint8)
     got = O.fp8_e4m3_decode(codes)

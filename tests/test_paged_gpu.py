@@ -1,6 +1,6 @@
 """GPU parity of the sparse MLA over a paged latent cache, bf16 or fp8 E4M3
 with a scale per token row (dsa_sparse_mla_decode_paged), against the oracle's
-paged attention (readings R12/R13 of the oracle: page table to physical rows,
+paged attention (readings R14/R15 of the oracle: page table to physical rows,
 out-of-range pages absent, fp8 value = decode(code) * scale).
 
 Bars: bf16 pages are bit-equal to dsa_sparse_mla_decode on the same cache laid
