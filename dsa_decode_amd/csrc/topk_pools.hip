@@ -17,7 +17,7 @@
 //    bin on average; the map is monotone, so the bins keep the key order and
 //    tied scores share a bin); one wave scans the histogram with DPP prefix
 //    sums and finds the bin of the K-th key;
-//  * when every bin from that one up holds at most 64 keys, those keys are
+//  * when every bin from that one up holds at most 256 keys, those keys are
 //    scattered bin by bin into LDS and each is placed directly: output
 //    position = keys in higher bins + its rank among its bin mates;
 //  * otherwise (a large tie, or scores spread too widely for equal bins) a
@@ -57,7 +57,7 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 
 constexpr int kDig = 11;              // radix digit width
 constexpr int kBins = 1 << kDig;      // 2048 bins, 32 per lane of the scanning wave
-constexpr int kRankCap = 64;          // largest bin that is ordered by pairwise ranks
+constexpr int kRankCap = 256;         // largest bin that is ordered by pairwise ranks
 
 // Bins of the first (linear) pass for n keys: about 4 keys per bin on average,
 // between 512 and kBins (the single-wave scan of the histogram is on the
