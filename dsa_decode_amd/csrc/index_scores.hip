@@ -563,6 +563,10 @@ __global__ __launch_bounds__(256) void index_scores_generic(
 // -> 2.44 ms on the prefill chunk; 207 registers leave room for one such
 // workgroup per CU)
 constexpr int kRowsWaves = 8;
+// prefill kernel: rows whose folded operands are staged in LDS per batch (8:
+// 139 KiB of LDS, still one workgroup per CU, half the barriers per row of 4;
+// 2.44 -> 2.35 ms on the prefill chunk)
+constexpr int kRowsBatch = 8;
 constexpr int kRowsTiles = 4;  // prefill kernel: key tiles per wave (256 pools per workgroup; 8 needs 316 registers, one wave per SIMD, and measured 10 % slower)
 // Decode launch shape (tuned on MI355X at 4 x 65536 pools)
 struct IsPlan {
@@ -636,7 +640,7 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
     dim3 grid(ceil_div(P_max, kRowsWaves * kRowsTiles * 16), ceil_div(Q, pl.rows_per_group));
     if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
 #define DSA_IS_ROWS(NH)                                                                               \
-  hipLaunchKernelGGL((index_scores_rows<NH, 4, kRowsTiles, kRowsWaves>), grid, dim3(kRowsWaves * 64), 0, s,       \
+  hipLaunchKernelGGL((index_scores_rows<NH, kRowsBatch, kRowsTiles, kRowsWaves>), grid, dim3(kRowsWaves * 64), 0, s,       \
                      (const uint16_t*)q,                                                                  \
                      w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
                      ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
