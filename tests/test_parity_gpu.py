@@ -456,7 +456,8 @@ def _distinct_ids_below(rng, Q, W, limits, hole_frac=0.0):
     return out
 
 
-@pytest.mark.parametrize("Q,Hm,W", [(256, 64, 1000), (1024, 16, 130), (300, 64, 2048)])
+@pytest.mark.parametrize("Q,Hm,W", [(256, 64, 1000), (1024, 16, 130), (300, 64, 2048), (1030, 16, 200),
+                                    (600, 32, 333)])
 def test_mla_many_rows_path(Q, Hm, W):
     # enough (row, head group) pairs that each workgroup runs over all of its
     # row's ids with the online softmax (no split partials): ragged last
