@@ -582,3 +582,48 @@ def test_end_to_end_decode_pipeline_on_gpu():
     assert set(clearly_in.tolist()) <= set(sel.tolist())
     if set(sel.tolist()) == set(ref_ids[0].tolist()):
         assert np.abs(out.float().cpu().numpy() - ref_o).max() <= 2e-2
+
+
+def test_end_to_end_batched_pipeline_on_gpu():
+    """The batched decode workload (32 sequences of ragged lengths with left
+    padding) through the whole GPU pipeline (compress -> scores -> top-k +
+    expand -> sparse MLA), against the oracle's own pipeline on the same token
+    inputs, row by row: every pool the oracle ranks clearly inside the cut is
+    selected, every GPU pick scores no lower than the oracle's K-th score minus
+    the tolerance, every token id lies in [first valid, length) of its own
+    sequence, and rows whose selection equals the oracle's agree in attention."""
+    d = wl_data("batched")
+    wl, ip = d["wl"], d["ip"]
+    comp = run_compress(d)
+    scores = ops().dsa_index_scores(dev(ip["q"]), dev(ip["w"]), ip["scale"], comp["k_pool"], comp["pool_start"],
+                                    comp["pool_valid"], dev(ip["gamma"]), dev(ip["beta"]), ip["eps"],
+                                    dev(ip["row_seq"]), dev(ip["row_pos"]), wl.kp)
+    ids, tok = ops().dsa_topk_pools_expand(scores, wl.K, dev(ip["row_seq"]), comp["pool_start"], wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    out, _ = ops().dsa_sparse_mla_decode(dev(mi["q_lat"]), dev(mi["kv"]), dev(ip["row_seq"]), tok, mi["sm_scale"])
+    torch.cuda.synchronize()
+    ids, tok, out = ids.cpu().numpy(), tok.cpu().numpy(), out.float().cpu().numpy()
+    rows = [0, 7, 13, 31]
+    pc = pool_cache_from_oracle(d["comp"], wl.torch_dtype)
+    ref = oracle_scores(d, pc, rows)
+    first = d["comp"]["first_valid"]
+    same = []
+    for i, r in enumerate(rows):
+        s = ref[i]
+        fin = np.sort(s[np.isfinite(s)])[::-1]
+        kth = fin[wl.K - 1]
+        tol = 1e-3 * abs(kth) + 1e-4
+        sel = ids[r]
+        assert (sel >= 0).all() and len(set(sel.tolist())) == wl.K
+        assert (s[sel] >= kth - tol).all()
+        assert set(np.flatnonzero(s > kth + tol).tolist()) <= set(sel.tolist())
+        b = int(ip["row_seq"][r])
+        t = tok[r]
+        assert (t >= first[b]).all() and (t < wl.seq_len[b]).all() and len(set(t.tolist())) == wl.W
+        if set(sel.tolist()) == set(O.topk_pools(s[None], wl.K)[0].tolist()):
+            same.append((i, r))
+    assert same, "no row selected the oracle's set"
+    ref_tok = np.stack([tok[r] for _, r in same])
+    ro, _ = O.sparse_mla_decode(mi["q_lat"][[r for _, r in same]], mi["kv"], ip["row_seq"][[r for _, r in same]],
+                                ref_tok, mi["sm_scale"])
+    assert np.abs(out[[r for _, r in same]] - ro).max() <= 2e-2
