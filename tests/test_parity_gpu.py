@@ -627,3 +627,40 @@ def test_end_to_end_batched_pipeline_on_gpu():
     ro, _ = O.sparse_mla_decode(mi["q_lat"][[r for _, r in same]], mi["kv"], ip["row_seq"][[r for _, r in same]],
                                 ref_tok, mi["sm_scale"])
     assert np.abs(out[[r for _, r in same]] - ro).max() <= 2e-2
+
+
+def test_end_to_end_prefill_chunk_on_gpu():
+    """The prefill chunk chained on the GPU (scores over the forced-ties pool
+    cache -> top-k + expand -> sparse MLA over the selected tokens), checked on
+    sampled rows against the oracle: the selection is valid for the oracle's
+    scores (clearly-in pools selected, no pick below the K-th score minus the
+    tolerance; ties at the cut may resolve either way within tolerance), token
+    ids are causal and distinct, and the attention over the GPU's own token ids
+    matches the oracle's attention over the same ids."""
+    d = wl_data_prefill()
+    wl, ip = d["wl"], d["ip"]
+    pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl))
+    scores = run_scores(d, pc)
+    ids, tok = ops().dsa_topk_pools_expand(scores, wl.K, dev(ip["row_seq"]), dev(pc["pool_start"]), wl.kp, wl.W)
+    mi = synth.mla_inputs(wl)
+    out, lse = ops().dsa_sparse_mla_decode(dev(mi["q_lat"]), dev(mi["kv"]), dev(ip["row_seq"]), tok,
+                                           mi["sm_scale"])
+    torch.cuda.synchronize()
+    ids, tok = ids.cpu().numpy(), tok.cpu().numpy()
+    rows = [0, 1234, 4095]
+    ref = oracle_scores(d, pc, rows)
+    A = score_scale(ip["q"], ip["w"], ip["scale"], pc["k_pool"], ip["gamma"], ip["beta"], ip["eps"],
+                    ip["row_seq"], rows)
+    for i, r in enumerate(rows):
+        s = ref[i]
+        kth = np.sort(s[np.isfinite(s)])[::-1][wl.K - 1]
+        tol = 1e-3 * abs(kth) + 1e-5 * A[i][np.isfinite(s)].max()
+        sel = ids[r]
+        assert (sel >= 0).all() and len(set(sel.tolist())) == wl.K
+        assert (s[sel] >= kth - tol).all()
+        assert set(np.flatnonzero(s > kth + tol).tolist()) <= set(sel.tolist())
+        t = tok[r]
+        assert (t >= 0).all() and (t <= int(ip["row_pos"][r])).all() and len(set(t.tolist())) == wl.W
+    ro, rl = O.sparse_mla_decode(mi["q_lat"], mi["kv"], ip["row_seq"], tok, mi["sm_scale"], rows=rows)
+    assert np.abs(out.float().cpu().numpy()[rows] - ro).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy()[rows] - rl).max() <= 2e-3 * max(1.0, np.abs(rl).max())
