@@ -551,6 +551,25 @@ def bench_prefill(args) -> int:
             tev.record(4 * i + 3, sh)
         stream.synchronize()
         t1 = time.perf_counter()
+    # the same scores + top-k + expand streamed over row blocks (at most 64 MiB of
+    # scores at a time), timed separately on the same stream
+    st_ws = torch.zeros(ops.dsa_index_topk_workspace_bytes(Q, P, K), dtype=torch.uint8, device="cuda")
+    st_ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
+    st_tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        stc = ops.bind_index_topk_pools_expand(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"],
+                                               gamma, beta, ip["eps"], row_seq, row_pos, wl.kp, K, st_ids, st_tok,
+                                               st_ws)
+        stc()
+        stream.synchronize()
+        sev = TimingEvents(2 * args.steps)
+        for i in range(args.steps):
+            sev.record(2 * i, stream.cuda_stream)
+            stc()
+            sev.record(2 * i + 1, stream.cuda_stream)
+        stream.synchronize()
+    streamed_us = float(np.mean([sev.elapsed_us(2 * i, 2 * i + 1) for i in range(args.steps)]))
+    sev.close()
     score_us = float(np.mean([tev.elapsed_us(4 * i, 4 * i + 1) for i in range(args.steps)]))
     topk_us = float(np.mean([tev.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
     mla_us = float(np.mean([tev.elapsed_us(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
@@ -581,6 +600,7 @@ def bench_prefill(args) -> int:
                    "rows": Q, "pools": P, "select_k": K},
         "stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2),
                       "sparse_mla_decode": round(mla_us, 2)},
+        "streamed_index_topk_us": round(streamed_us, 2),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
                      "traffic": None, "launch_us": kernels[dom]["launch_us"],

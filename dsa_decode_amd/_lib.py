@@ -38,6 +38,11 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "dsa_index_topk_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "dsa_index_topk_pools_expand": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                            c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                            c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "dsa_sparse_mla_paged_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "dsa_sparse_mla_decode_paged": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                             c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_float,

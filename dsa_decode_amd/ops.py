@@ -151,6 +151,36 @@ def dsa_topk_pools_expand(scores, K: int, row_seq, pool_start, kpool: int, W: in
     return pool_ids, token_ids
 
 
+def dsa_index_topk_workspace_bytes(Q: int, P_max: int, K: int) -> int:
+    return int(_lib.load().dsa_index_topk_workspace_bytes(Q, P_max, K))
+
+
+def dsa_index_topk_pools_expand(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamma, ln_beta,
+                                ln_eps: float, row_seq, row_pos, kpool: int, K: int, W: int, pool_ids=None,
+                                token_ids=None, workspace=None):
+    """dsa_index_scores then dsa_topk_pools_expand over row blocks whose scores
+    fit 64 MiB -> (pool_ids [Q, K], token_ids [Q, W]), bit-identical to the two
+    calls.  A workspace passed in must start zeroed (the top-k counters)."""
+    Q, H, D = q.shape
+    B, P_max = pool_start.shape
+    _check_pool_cache(k_pool, B, P_max, D)
+    if pool_ids is None:
+        pool_ids = torch.empty((Q, K), dtype=torch.int32, device=q.device)
+    if token_ids is None:
+        token_ids = torch.empty((Q, W), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(dsa_index_topk_workspace_bytes(Q, P_max, K), dtype=torch.uint8, device=q.device)
+    st = _lib.load().dsa_index_topk_pools_expand(
+        _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
+        _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
+        _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps),
+        _dev(row_seq, "row_seq", torch.int32), _dev(row_pos, "row_pos", torch.int32), Q, H, D, B, P_max, kpool,
+        _act_code(k_pool), K, _dev(pool_ids, "pool_ids", torch.int32), _dev(token_ids, "token_ids", torch.int32),
+        W, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream())
+    check("dsa_index_topk_pools_expand", st)
+    return pool_ids, token_ids
+
+
 def dsa_expand_selection(pool_ids, row_seq, pool_start, kpool: int, W: int, token_ids=None):
     """-> token_ids [Q, W] int32 (-1 = invalid, every column written)."""
     Q, K = pool_ids.shape
@@ -316,3 +346,17 @@ def bind_kpool_append(k, gate, valid, ape, seq_len, kpool, state, max_new_pools=
         _dev(state["k_pool"], "k_pool", k.dtype), _dev(state["pool_start"], "pool_start", torch.int32),
         _dev(state["pool_valid"], "pool_valid", torch.uint8), _dev(state["n_pools"], "n_pools", torch.int32),
         _dev(state["first_valid"], "first_valid", torch.int32), _stream()))
+
+
+def bind_index_topk_pools_expand(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,
+                                 row_pos, kpool, K, pool_ids, token_ids, workspace) -> BoundCall:
+    Q, H, D = q.shape
+    B, P_max = pool_start.shape
+    _check_pool_cache(k_pool, B, P_max, D)
+    return BoundCall("dsa_index_topk_pools_expand", (
+        _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
+        _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
+        _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps),
+        _dev(row_seq, "row_seq", torch.int32), _dev(row_pos, "row_pos", torch.int32), Q, H, D, B, P_max, kpool,
+        _act_code(k_pool), K, _dev(pool_ids, "pool_ids", torch.int32), _dev(token_ids, "token_ids", torch.int32),
+        token_ids.shape[1], _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))

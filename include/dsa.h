@@ -274,6 +274,30 @@ int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_index_topk_pools_expand -- dsa_index_scores, then dsa_topk_pools_expand,
+ * for many rows (a prefill chunk) without the [Q, P_max] score tensor.  Same
+ * operations as those two calls ("Module glm5next_dsa", "Shape of the
+ * pipeline": index_scores -> topk_pools -> expand_selection; see them for the
+ * arguments): the rows are taken in blocks whose fp32 scores fit 64 MiB, each
+ * block's scores written into the workspace and consumed by its top-k before
+ * the next block, so pool_ids [Q, K] and token_ids [Q, W] are bit-identical to
+ * the two calls while at most 64 MiB of scores exist at a time.
+ *   workspace  dsa_index_topk_workspace_bytes(Q, P_max, K) bytes.  When rows
+ *              are few enough for the top-k to split them, the workspace
+ *              starts with the top-k counter block: its first
+ *              DSA_TOPK_COUNTER_BYTES must be zero before the first use, and
+ *              every call leaves them zero (as for dsa_topk_pools).
+ * Every argument check of both stages is made before any launch.
+ */
+size_t dsa_index_topk_workspace_bytes(int Q, int P_max, int K);
+int dsa_index_topk_pools_expand(const void* q, const float* w, float scale, const void* k_pool,
+                                const int32_t* pool_start, const uint8_t* pool_valid, const float* ln_gamma,
+                                const float* ln_beta, float ln_eps, const int32_t* row_seq, const int32_t* row_pos,
+                                int Q, int H, int D, int B, int P_max, int kpool, int dtype, int K,
+                                int32_t* pool_ids, int32_t* token_ids, int W, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * dsa_sparse_mla_decode_paged -- dsa_sparse_mla_decode over a paged latent
  * cache, optionally stored as fp8.  "Module glm5next_dsa", module list
  * ("attend": the launcher of the selected-index NoPE MLA *paged* decode) and

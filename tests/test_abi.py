@@ -189,3 +189,28 @@ def test_paged_mla_refuses_bad_arguments_and_sizes_workspace(lib):
     assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 64) == 0   # one id slice
     # the paged entry splits the ids for any row count (no many-rows path)
     assert lib.dsa_sparse_mla_paged_workspace_bytes(4096, 64, 512, 2048) > 0
+
+
+def _streamed(lib, **kw):
+    a = dict(q=FAKE, w=FAKE, scale=0.1, k_pool=FAKE, ps=FAKE, pv=FAKE, g=FAKE, b=FAKE, eps=1e-5, rs=FAKE, rp=FAKE,
+             Q=4096, H=32, D=128, B=1, P_max=32768, kpool=4, dtype=1, K=512, ids=FAKE, tok=FAKE, W=2048, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.dsa_index_topk_pools_expand(*a.values())
+
+
+def test_streamed_index_topk_refuses_bad_arguments_and_sizes_workspace(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE
+    assert _streamed(lib, tok=None) == DSA_ERR_NULL
+    assert _streamed(lib, W=2047) == DSA_ERR_SHAPE          # W < K * kpool
+    assert _streamed(lib, K=0) == DSA_ERR_SHAPE
+    assert _streamed(lib, K=4096, W=4 * 4096) == DSA_ERR_UNSUPPORTED
+    assert _streamed(lib, D=96) == DSA_ERR_UNSUPPORTED
+    assert _streamed(lib, kpool=9, W=9 * 512) == DSA_ERR_UNSUPPORTED
+    assert _streamed(lib, ws=None) == DSA_ERR_WORKSPACE
+    assert _streamed(lib, ws_bytes=1 << 20) == DSA_ERR_WORKSPACE
+    # the prefill chunk: blocks of 512 rows, 64 MiB of scores, no top-k split
+    assert lib.dsa_index_topk_workspace_bytes(4096, 32768, 512) == 512 * 32768 * 4
+    # few rows: one block, the split top-k's workspace (counter block first) plus the scores
+    n = lib.dsa_index_topk_workspace_bytes(4, 65536, 512)
+    assert n >= lib.dsa_topk_workspace_bytes(4, 65536, 512) + 4 * 65536 * 4

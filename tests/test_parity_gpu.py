@@ -664,3 +664,39 @@ def test_end_to_end_prefill_chunk_on_gpu():
     ro, rl = O.sparse_mla_decode(mi["q_lat"], mi["kv"], ip["row_seq"], tok, mi["sm_scale"], rows=rows)
     assert np.abs(out.float().cpu().numpy()[rows] - ro).max() <= 2e-2
     assert np.abs(lse.cpu().numpy()[rows] - rl).max() <= 2e-3 * max(1.0, np.abs(rl).max())
+
+
+@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3)])
+def test_streamed_index_topk_bit_identical(Q, P, B):
+    # dsa_index_topk_pools_expand over row blocks of at most 64 MiB of scores
+    # gives the bits of dsa_index_scores + dsa_topk_pools_expand: 2 blocks with
+    # a ragged last block that takes the split top-k (1000 x 20000), one block
+    # with the split top-k (decode rows), and a small case
+    rng = np.random.default_rng(Q + P)
+    H, D, kp, K = 32, 128, 4, 512
+    W = K * kp + 3
+    k_pool = torch.from_numpy(rng.standard_normal((B, P, D)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((Q, H, D)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.random((Q, H)) / H).astype(np.float32))
+    gamma = torch.from_numpy((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+    beta = torch.from_numpy((0.02 * rng.standard_normal(D)).astype(np.float32))
+    n = [P - 5 * b for b in range(B)]
+    ps = np.full((B, P), -1, np.int32)
+    pv = np.zeros((B, P), np.uint8)
+    for b in range(B):
+        ps[b, :n[b]] = 7 + kp * np.arange(n[b])
+        pv[b, :n[b]] = rng.random(n[b]) > 0.02
+    row_seq = np.sort(rng.integers(0, B, Q)).astype(np.int32)
+    row_pos = (7 + kp * np.asarray(n)[row_seq] - rng.integers(0, 40, Q)).astype(np.int32)
+    args = (dev(q), dev(w), D ** -0.5, dev(tile_pool_cache(k_pool)), dev(torch.from_numpy(ps)),
+            dev(torch.from_numpy(pv)), dev(gamma), dev(beta), 1e-5, dev(torch.from_numpy(row_seq)),
+            dev(torch.from_numpy(row_pos)), kp)
+    scores = ops().dsa_index_scores(*args)
+    ids_a, tok_a = ops().dsa_topk_pools_expand(scores, K, args[9], args[4], kp, W)
+    ws = torch.zeros(ops().dsa_index_topk_workspace_bytes(Q, P, K), dtype=torch.uint8, device="cuda")
+    for _ in range(2):   # twice on one workspace: the top-k counters are left zero
+        ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, K, W, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids_a, ids_b)
+        assert torch.equal(tok_a, tok_b)
+    assert_topk_property(scores.cpu().numpy()[:3], ids_b.cpu().numpy()[:3], K)
