@@ -700,3 +700,22 @@ def test_streamed_index_topk_bit_identical(Q, P, B):
         assert torch.equal(ids_a, ids_b)
         assert torch.equal(tok_a, tok_b)
     assert_topk_property(scores.cpu().numpy()[:3], ids_b.cpu().numpy()[:3], K)
+
+
+def test_streamed_index_topk_prefill_chunk_full_size():
+    # the prefill chunk (4096 rows x 32768 pools, forced ties at the cut): 8 row
+    # blocks of 512, bit-identical to the unfused calls
+    d = wl_data_prefill()
+    wl, ip = d["wl"], d["ip"]
+    pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl))
+    args = (dev(ip["q"]), dev(ip["w"]), ip["scale"], dev(tile_pool_cache(pc["k_pool"])), dev(pc["pool_start"]),
+            dev(pc["pool_valid"]), dev(ip["gamma"]), dev(ip["beta"]), ip["eps"], dev(ip["row_seq"]),
+            dev(ip["row_pos"]), wl.kp)
+    scores = ops().dsa_index_scores(*args)
+    ids_a, tok_a = ops().dsa_topk_pools_expand(scores, wl.K, args[9], args[4], wl.kp, wl.W)
+    del scores
+    assert ops().dsa_index_topk_workspace_bytes(wl.Q, wl.P_max, wl.K) == 512 * wl.P_max * 4
+    ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, wl.K, wl.W)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_a, ids_b)
+    assert torch.equal(tok_a, tok_b)
