@@ -330,7 +330,6 @@ extern "C" int dsa_kpool_append(const void* k, const void* gate, const uint8_t* 
   if (kpool > DSA_MAX_KPOOL) return DSA_ERR_UNSUPPORTED;
   if (D % 8 != 0 || D > 1024) return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
-  if (long(B) > 2147483647L) return DSA_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (dtype == DSA_BF16)
     launch_append<uint16_t>(kpool, B, s, k, gate, valid, ape, seq_len, T_max, D, P_max, max_new_pools,
