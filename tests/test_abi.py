@@ -214,3 +214,17 @@ def test_streamed_index_topk_refuses_bad_arguments_and_sizes_workspace(lib):
     # few rows: one block, the split top-k's workspace (counter block first) plus the scores
     n = lib.dsa_index_topk_workspace_bytes(4, 65536, 512)
     assert n >= lib.dsa_topk_workspace_bytes(4, 65536, 512) + 4 * 65536 * 4
+
+
+def test_streamed_workspace_covers_a_ragged_last_block(lib):
+    # 1000 rows x 20000 pools: blocks of 832 rows (64 MiB / 80000 B, a multiple of 8)
+    # and a last block of 168 rows, whose top-k splits the rows and needs the
+    # counter block; the workspace holds the larger of the two top-k needs
+    # (aligned to 256 B) and one block of scores
+    R, rem, P, K = 832, 168, 20000, 512
+    tk = max(lib.dsa_topk_workspace_bytes(R, P, K), lib.dsa_topk_workspace_bytes(rem, P, K))
+    assert lib.dsa_topk_workspace_bytes(rem, P, K) > 0
+    assert lib.dsa_index_topk_workspace_bytes(1000, P, K) == ((tk + 255) // 256) * 256 + R * P * 4
+    # rows that fit one block: all of them at once
+    assert lib.dsa_index_topk_workspace_bytes(100, P, K) == \
+        ((lib.dsa_topk_workspace_bytes(100, P, K) + 255) // 256) * 256 + 100 * P * 4
