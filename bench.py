@@ -30,12 +30,15 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode steps/s (indexer+top-k+sparse MLA) @262K ctx; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 REPLICAS = 8
+RUNS = 5  # timed runs per mode; the reported figure is their median
 
 
 class TimingEvents:
@@ -148,8 +151,8 @@ def step_algorithmic_bytes(Q: int, P: int, K: int, W: int, Hm: int, Dl: int, sco
 
 
 def score_bytes_per_pool() -> int:
-    # key row (128 bf16) + pool_valid (u8) + pool_start (i32) read, score (fp32) written
-    return 128 * 2 + 1 + 4 + 4
+    # key row (128 bf16) + pool_valid (u8) read, score (fp32) written
+    return 128 * 2 + 1 + 4
 
 
 def main() -> int:
@@ -200,7 +203,7 @@ def main() -> int:
     q, w, gamma, beta = dev(ip["q"]), dev(ip["w"]), dev(ip["gamma"]), dev(ip["beta"])
     row_seq, row_pos = dev(ip["row_seq"]), dev(ip["row_pos"])
     q_lat = dev(mi["q_lat"])
-    tk_ws = torch.zeros(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    tk_ws = ops.topk_workspace(ops.dsa_topk_workspace_bytes(Q, P, K))
     mla_ws = torch.empty(max(1, ops.dsa_sparse_mla_workspace_bytes(Q, wl.Hm, wl.Dl, W, ops.DSA_BF16)),
                          dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -229,52 +232,63 @@ def main() -> int:
             c()
 
     torch.cuda.synchronize()
-    if args.mode == "graph":
-        g_scores, g_rest = [], []
+
+    def timed_runs(run_step, with_events: bool):
+        """RUNS timed runs of args.steps steps each (after the warm-up), each
+        bracketed by a device synchronisation; -> (ms per step of every run,
+        event-timed score-kernel launches in us or [])."""
         with torch.cuda.stream(stream):
-            for i in range(REPLICAS):  # one eager pass on the capture stream first
-                scores_stage(i)
-                rest_stages(i)
+            for i in range(args.warmup):
+                run_step(i % REPLICAS, None)
+            stream.synchronize()
+            torch.cuda.synchronize()
+            ms, score_us = [], []
+            for _ in range(RUNS):
+                tev = TimingEvents(2 * args.steps) if with_events else None
+                t0 = time.perf_counter()
+                for i in range(args.steps):
+                    run_step(i % REPLICAS, (tev, i) if with_events else None)
+                stream.synchronize()
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                ms.append((t1 - t0) * 1e3 / args.steps)
+                if with_events:
+                    score_us += [tev.elapsed_us(2 * i, 2 * i + 1) for i in range(args.steps)]
+                    tev.close()
+        return ms, score_us
+
+    sh = stream.cuda_stream
+
+    def eager_step(j, ev):
+        if ev is not None:
+            ev[0].record(2 * ev[1], sh)
+        scores_stage(j)
+        if ev is not None:
+            ev[0].record(2 * ev[1] + 1, sh)
+        rest_stages(j)
+
+    # eager launches (the headline): score-kernel launches event-timed for the roofline
+    eager_ms, score_us = timed_runs(eager_step, True)
+
+    # the same step replayed from HIP graphs (one graph per replica: all launches of the step)
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(REPLICAS):
+            scores_stage(i)
+            rest_stages(i)
         stream.synchronize()
         for i in range(REPLICAS):
-            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(ga, stream=stream):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
                 scores_stage(i)
-            with torch.cuda.graph(gb, stream=stream):
                 rest_stages(i)
-            g_scores.append(ga)
-            g_rest.append(gb)
-        run_scores = lambda i: g_scores[i].replay()
-        run_rest = lambda i: g_rest[i].replay()
-    else:
-        run_scores = scores_stage
-        run_rest = rest_stages
+            graphs.append(g)
+    graph_ms, _ = timed_runs(lambda j, ev: graphs[j].replay(), False)
+    del graphs
 
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            run_scores(i % REPLICAS)
-            run_rest(i % REPLICAS)
-        stream.synchronize()
-        torch.cuda.synchronize()
-        tev = TimingEvents(2 * args.steps)
-        sh = stream.cuda_stream
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            j = i % REPLICAS
-            tev.record(2 * i, sh)
-            run_scores(j)
-            tev.record(2 * i + 1, sh)
-            run_rest(j)
-        t_issued = time.perf_counter()
-        stream.synchronize()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    host_issue_us = (t_issued - t0) * 1e6 / args.steps  # host time to enqueue one step
-    score_us = [tev.elapsed_us(2 * i, 2 * i + 1) for i in range(args.steps)]
-    tev.close()
+    ms_runs = graph_ms if args.mode == "graph" else eager_ms
+    ms_per_step = float(np.median(ms_runs))
     score_us_mean = float(np.mean(score_us))
-
     # per-stage breakdown (separate instrumented pass, eager launches, events around each stage)
     stage_names = (["index_scores", "topk_pools", "expand_selection", "sparse_mla_decode"] if args.split_topk_expand
                    else ["index_scores", "topk_pools_expand", "sparse_mla_decode"])
@@ -295,12 +309,14 @@ def main() -> int:
     stages_us = {n: round(float(np.median(v)), 2) for n, v in stage_t.items()}
 
     bytes_per_launch = score_bytes_per_pool() * Q * P + q.numel() * 2 + w.numel() * 4 + 2 * 128 * 4
+    ceiling = read_stream_ceiling(reps, stream)
     achieved = bytes_per_launch / (score_us_mean * 1e-6) / 1e9
     steps_per_s = 1e3 / ms_per_step
     step_bytes = step_algorithmic_bytes(Q, P, K, W, wl.Hm, wl.Dl, bytes_per_launch)
 
     paged = None if args.no_paged else paged_mla_stages(wl, mi, q_lat, row_seq, reps[0]["tok"], stream)
     append_us = append_stage_us(wl, tok_dev, comp, stream)
+    with_append = step_with_append_us(wl, tok_dev, comp, bound, scores_stage, rest_stages, stream, args.steps)
     del tok_dev
 
     cpu = None
@@ -315,6 +331,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "runs": {"count": RUNS, "steps_per_s": [round(1e3 / m, 1) for m in ms_runs],
+                 "statistic": "median of the runs' steps/s"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -329,18 +347,93 @@ def main() -> int:
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "graph_steps_per_s": round(1e3 / float(np.median(graph_ms)), 1),
+        "eager_steps_per_s": round(1e3 / float(np.median(eager_ms)), 1),
+        "step_with_append": with_append,
         "stages_us": stages_us,
         "paged_mla_us": paged,
         "kpool_append_us": append_us,
-        "host_issue_us_per_step": round(host_issue_us, 2),
         "roofline": {"bound": "hbm", "kernel": "index_scores_stream", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "launch_us": round(score_us_mean, 3),
-                     "algorithmic_bytes": bytes_per_launch},
+                     "algorithmic_bytes": bytes_per_launch, "bytes_per_pool": score_bytes_per_pool(),
+                     "stream_ceiling": ceiling},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def read_stream_ceiling(reps, stream, calls: int = 64) -> dict:
+    """The plain read-stream reference kernel (libdsa_probe.so) over the same
+    64 MiB pool-cache buffers the score kernel reads, rotating through the
+    replicas, each wave reading 32 KiB: the HBM bandwidth this machine delivers to
+    a pure streaming read of that size, event-timed per launch."""
+    import ctypes
+    import torch
+    from dsa_decode_amd import build_lib
+
+    lib = ctypes.CDLL(build_lib.PROBE_LIB)
+    lib.dsa_probe_read_stream.restype = ctypes.c_int
+    lib.dsa_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_long, ctypes.c_void_p]
+    bufs = [r["k_pool"] for r in reps]
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    ev = TimingEvents(2 * calls)
+    with torch.cuda.stream(stream):
+        for k in range(2 * len(bufs)):
+            assert lib.dsa_probe_read_stream(bufs[k % len(bufs)].data_ptr(), nbytes, 32768, stream.cuda_stream) == 0
+        stream.synchronize()
+        for k in range(calls):
+            ev.record(2 * k, stream.cuda_stream)
+            lib.dsa_probe_read_stream(bufs[k % len(bufs)].data_ptr(), nbytes, 32768, stream.cuda_stream)
+            ev.record(2 * k + 1, stream.cuda_stream)
+        stream.synchronize()
+    us = float(np.mean([ev.elapsed_us(2 * k, 2 * k + 1) for k in range(calls)]))
+    ev.close()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "read_stream (plain 16-byte non-temporal loads, 32 KiB per wave)", "bytes": nbytes,
+            "launch_us": round(us, 3), "achieved": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def step_with_append_us(wl, tok_dev, comp, bound, scores_stage, rest_stages, stream, steps: int) -> dict:
+    """The decode step with the indexer-state update in front of it
+    (dsa_kpool_append -> scores -> top-k + expand -> sparse MLA), event-timed
+    per step.  With kpool 4, three decode tokens in four complete no pool (the
+    append only reads the state) and the fourth completes one pool in every
+    sequence; both kinds are timed (the state is rewound by one pool, outside
+    the events, before each pool-forming step) and weighted 3:1."""
+    import torch
+    from dsa_decode_amd import ops
+
+    st = {k: comp[k].clone() for k in ("k_pool", "pool_start", "pool_valid", "n_pools", "first_valid")}
+    n_full = st["n_pools"].clone()
+    n_back = (n_full - 1).clamp_min(0)
+    res = {}
+    with torch.cuda.stream(stream):
+        # bound inside the stream context: a bound call launches on the stream current at bind time
+        app = ops.bind_kpool_append(tok_dev["k"], tok_dev["gate"], tok_dev["valid"], tok_dev["ape"],
+                                    tok_dev["seq_len"], wl.kp, st, 1)
+        for name, rewind in (("no_new_pool_us", False), ("new_pool_us", True)):
+            ev = TimingEvents(2 * steps)
+            for i in range(steps):
+                j = i % REPLICAS
+                if rewind:
+                    st["n_pools"].copy_(n_back)
+                ev.record(2 * i, stream.cuda_stream)
+                app()
+                scores_stage(j)
+                rest_stages(j)
+                ev.record(2 * i + 1, stream.cuda_stream)
+            stream.synchronize()
+            res[name] = round(float(np.median([ev.elapsed_us(2 * i, 2 * i + 1) for i in range(steps)])), 2)
+            ev.close()
+    assert torch.equal(st["n_pools"], n_full)
+    per_token = (3 * res["no_new_pool_us"] + res["new_pool_us"]) / 4
+    res["mean_us_per_step"] = round(per_token, 2)
+    res["steps_per_s"] = round(1e6 / per_token, 1)
+    res["note"] = ("event-timed per step (median of each kind), weighted 3:1; the append updates its own copy "
+                   "of the indexer state in front of the step's launches on the same stream")
+    return res
 
 
 def append_stage_us(wl, tok_dev, comp, stream, calls: int = 64) -> float:
@@ -354,10 +447,11 @@ def append_stage_us(wl, tok_dev, comp, stream, calls: int = 64) -> float:
     st = {k: comp[k].clone() for k in ("k_pool", "pool_start", "pool_valid", "n_pools", "first_valid")}
     n_full = st["n_pools"].clone()
     n_back = (n_full - 1).clamp_min(0)
-    call = ops.bind_kpool_append(tok_dev["k"], tok_dev["gate"], tok_dev["valid"], tok_dev["ape"],
-                                 tok_dev["seq_len"], wl.kp, st, 1)
     ev = TimingEvents(2 * calls)
     with torch.cuda.stream(stream):
+        # bound inside the stream context: a bound call launches on the stream current at bind time
+        call = ops.bind_kpool_append(tok_dev["k"], tok_dev["gate"], tok_dev["valid"], tok_dev["ape"],
+                                     tok_dev["seq_len"], wl.kp, st, 1)
         for k in range(calls):
             st["n_pools"].copy_(n_back)
             ev.record(2 * k, stream.cuda_stream)
@@ -413,72 +507,99 @@ def paged_mla_stages(wl, mi, q_lat, row_seq, tok, stream, calls: int = 64) -> di
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _timed_oracle(step_row, n_rows_per_unit: int, budget_s: float, threads: int | None):
+    """Rows through step_row until about budget_s of CPU work -> (units/s,
+    rows, seconds); threads limits the BLAS pool (None: as configured)."""
+    from contextlib import nullcontext
+    ctx = nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=threads)
+    rows_done = 0
+    with ctx:
+        t0 = time.perf_counter()
+        while True:
+            step_row(rows_done)
+            rows_done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+    return rows_done / n_rows_per_unit / el, rows_done, el
+
+
 def cpu_baseline(wl, ip, mi, comp, budget_s: float) -> dict:
     """The oracle (as it is) on a bounded sample of the same step: decode rows of
     the same workload, each through scores -> top-k -> expand -> sparse MLA,
-    repeated until about budget_s of CPU work; scaled to steps/s (4 rows/step)."""
-    import numpy as np
-    import torch
+    repeated until about budget_s of CPU work; scaled to steps/s (4 rows/step).
+    Timed on all the BLAS threads, then on one thread for a third of the budget."""
     from oracle import dsa_oracle as O
-
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     from dsa_decode_amd.layout import untile_pool_cache
+
+    cores = _oracle_threads()
     pc = dict(k_pool=untile_pool_cache(comp["k_pool"].cpu(), wl.P_max), pool_start=comp["pool_start"].cpu(),
               pool_valid=comp["pool_valid"].cpu())
-    rows_done = 0
-    t0 = time.perf_counter()
-    while True:
-        r = rows_done % wl.Q
+
+    def step_row(i):
+        r = i % wl.Q
         s = O.index_scores(ip["q"], ip["w"], ip["scale"], pc["k_pool"], pc["pool_start"], pc["pool_valid"],
                            ip["gamma"], ip["beta"], ip["eps"], ip["row_seq"], ip["row_pos"], wl.kp, rows=[r])
         ids = O.topk_pools(s, wl.K)
         tok = O.expand_selection(ids, ip["row_seq"].numpy()[[r]], pc["pool_start"].numpy(), wl.kp, wl.W)
         O.sparse_mla_decode(mi["q_lat"][[r]], mi["kv"], ip["row_seq"][[r]], tok, mi["sm_scale"])
-        rows_done += 1
-        if time.perf_counter() - t0 >= budget_s and rows_done >= 1:
-            break
-    el = time.perf_counter() - t0
-    steps = rows_done / wl.Q
-    return {"value": round(steps / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows_done} decode rows of the same workload (scores over 65536 pools, top-k, "
-                      f"expand, sparse MLA per row) in {el:.1f} s; 4 rows = 1 step"}
+
+    v, rows, el = _timed_oracle(step_row, wl.Q, budget_s, None)
+    v1, rows1, el1 = _timed_oracle(step_row, wl.Q, budget_s / 3, 1)
+    return {"value": round(v, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1_thread": round(v1, 4),
+            "sample": f"{rows} decode rows of the same workload (scores over 65536 pools, top-k, expand, sparse "
+                      f"MLA per row) in {el:.1f} s on {cores} threads, {rows1} rows in {el1:.1f} s on 1 thread; "
+                      f"4 rows = 1 step"}
 
 
 def cpu_baseline_prefill(wl, ip, mi, comp, k_pool, budget_s: float) -> dict:
     """The oracle (as it is) on a bounded sample of the prefill chunk: rows of the
     chunk, each through scores over the 32768 pools -> top-k -> expand -> sparse
     MLA, until about budget_s of CPU work; scaled to chunks/s (4096 rows/chunk)."""
-    import numpy as np
     from oracle import dsa_oracle as O
     from dsa_decode_amd.layout import untile_pool_cache
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = _oracle_threads()
     kp_host = untile_pool_cache(k_pool.cpu(), wl.P_max)
     ps, pv = comp["pool_start"].cpu(), comp["pool_valid"].cpu()
-    rows_done = 0
-    t0 = time.perf_counter()
-    while True:
-        r = (rows_done * 997) % wl.Q
+
+    def step_row(i):
+        r = (i * 997) % wl.Q
         s = O.index_scores(ip["q"], ip["w"], ip["scale"], kp_host, ps, pv, ip["gamma"], ip["beta"], ip["eps"],
                            ip["row_seq"], ip["row_pos"], wl.kp, rows=[r])
         ids = O.topk_pools(s, wl.K)
         tok = O.expand_selection(ids, ip["row_seq"].numpy()[[r]], ps.numpy(), wl.kp, wl.W)
         O.sparse_mla_decode(mi["q_lat"][[r]], mi["kv"], ip["row_seq"][[r]], tok, mi["sm_scale"])
-        rows_done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(rows_done / wl.Q / el, 6), "unit": "chunks/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows_done} rows of the prefill chunk (scores over 32768 pools, top-k, expand, sparse "
-                      f"MLA per row) in {el:.1f} s; 4096 rows = 1 chunk"}
+
+    v, rows, el = _timed_oracle(step_row, wl.Q, budget_s, None)
+    v1, rows1, el1 = _timed_oracle(step_row, wl.Q, budget_s / 3, 1)
+    return {"value": round(v, 6), "unit": "chunks/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1_thread": round(v1, 6),
+            "sample": f"{rows} rows of the prefill chunk (scores over 32768 pools, top-k, expand, sparse MLA per "
+                      f"row) in {el:.1f} s on {cores} threads, {rows1} rows in {el1:.1f} s on 1 thread; "
+                      f"4096 rows = 1 chunk"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
@@ -513,7 +634,7 @@ def bench_prefill(args) -> int:
     scores = torch.empty((Q, P), dtype=torch.float32, device="cuda")
     ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
     tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
-    tk_ws = torch.zeros(max(1, ops.dsa_topk_workspace_bytes(Q, P, K)), dtype=torch.uint8, device="cuda")
+    tk_ws = ops.topk_workspace(ops.dsa_topk_workspace_bytes(Q, P, K))
     mi = synth.mla_inputs(wl)
     q_lat, kv = dev(mi["q_lat"]), dev(mi["kv"])
     out = torch.empty((Q, wl.Hm, wl.Dl), dtype=torch.bfloat16, device="cuda")
@@ -553,7 +674,7 @@ def bench_prefill(args) -> int:
         t1 = time.perf_counter()
     # the same scores + top-k + expand streamed over row blocks (at most 64 MiB of
     # scores at a time), timed separately on the same stream
-    st_ws = torch.zeros(ops.dsa_index_topk_workspace_bytes(Q, P, K), dtype=torch.uint8, device="cuda")
+    st_ws = ops.topk_workspace(ops.dsa_index_topk_workspace_bytes(Q, P, K))
     st_ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
     st_tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
     with torch.cuda.stream(stream):

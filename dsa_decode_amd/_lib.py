@@ -28,6 +28,7 @@ SIGNATURES = {
                                  c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                  c_void_p, c_void_p]),
     "dsa_topk_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "dsa_topk_workspace_init": (c_int, [c_void_p, c_size_t, c_void_p]),
     "dsa_topk_pools": (c_int, [c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_size_t,
                                c_void_p]),
     "dsa_expand_selection": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_int, c_int,

@@ -18,14 +18,26 @@ HIPCC_FLAGS = [
 ]
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "read_stream.hip")
+PROBE_LIB = os.path.join(PKG, "libdsa_probe.so")
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def build(verbose: bool = False) -> str:
+    """Build libdsa.so (the library) and libdsa_probe.so (the read-stream
+    reference kernel that the benchmark quotes the score kernel against)."""
+    _hipcc(sources(), LIB, verbose)
+    _hipcc([PROBE_SRC], PROBE_LIB, verbose)
+    return LIB
+
+
+def _hipcc(srcs: list[str], lib: str, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *sources(), "-o", tmp]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,8 +47,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode})")
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

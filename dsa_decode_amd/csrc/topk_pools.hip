@@ -872,6 +872,21 @@ static void launch_tk_nt(int nt, int kpt, dim3 grid, hipStream_t s, const float*
 
 using namespace dsa;
 
+// zero-fills the counter block of a top-k workspace (a plain fill kernel, so
+// that the call can sit in a captured HIP graph)
+__global__ __launch_bounds__(256) void topk_counter_fill(uint32_t* __restrict__ counters, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counters[i] = 0u;
+}
+
+extern "C" int dsa_topk_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return DSA_ERR_NULL;
+  const size_t n = (workspace_bytes < DSA_TOPK_COUNTER_BYTES ? workspace_bytes : DSA_TOPK_COUNTER_BYTES) / 4;
+  if (n == 0) return DSA_OK;
+  hipLaunchKernelGGL(topk_counter_fill, dim3(64), dim3(256), 0, as_stream(stream), static_cast<uint32_t*>(workspace),
+                     int(n));
+  return launch_status();
+}
+
 extern "C" size_t dsa_topk_workspace_bytes(int Q, int P, int K) {
   if (Q <= 0 || P <= 0 || K <= 0) return 0;
   const TkPlan pl = tk_plan(Q, P, K);

@@ -111,15 +111,40 @@ def dsa_topk_workspace_bytes(Q: int, P: int, K: int) -> int:
     return int(_lib.load().dsa_topk_workspace_bytes(Q, P, K))
 
 
+def dsa_topk_workspace_init(workspace) -> None:
+    """Zero the counter block of a top-k workspace on the current stream (a
+    fill kernel); marks the tensor as a top-k workspace for the calls below."""
+    st = _lib.load().dsa_topk_workspace_init(_dev(workspace, "workspace"),
+                                             workspace.numel() * workspace.element_size(), _stream())
+    check("dsa_topk_workspace_init", st)
+    workspace._dsa_topk_ready = True
+
+
+def topk_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A top-k workspace of nbytes (at least 1) with its counter block zeroed."""
+    ws = torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+    dsa_topk_workspace_init(ws)
+    return ws
+
+
+def _topk_ws(workspace, need: int, device):
+    """The workspace for a top-k call: a new zeroed one when none is given;
+    one passed in must come from topk_workspace / dsa_topk_workspace_init
+    (its counter block starts at zero) and be large enough."""
+    if workspace is None:
+        return topk_workspace(need, device) if need else None
+    if not getattr(workspace, "_dsa_topk_ready", False):
+        raise ValueError("a top-k workspace must be made by ops.topk_workspace or passed through "
+                         "ops.dsa_topk_workspace_init first (its counter block must start at zero)")
+    return workspace
+
+
 def dsa_topk_pools(scores, K: int, pool_ids=None, workspace=None):
     """-> pool_ids [Q, K] int32, (score desc, index asc), -1 padded."""
     Q, P = scores.shape
     if pool_ids is None:
         pool_ids = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
-    need = dsa_topk_workspace_bytes(Q, P, K)
-    if workspace is None and need:
-        # zero-filled: the workspace starts with per-row counters that every call returns to zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    workspace = _topk_ws(workspace, dsa_topk_workspace_bytes(Q, P, K), scores.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.load().dsa_topk_pools(_dev(scores, "scores", torch.float32), Q, P, K,
@@ -138,9 +163,7 @@ def dsa_topk_pools_expand(scores, K: int, row_seq, pool_start, kpool: int, W: in
         pool_ids = torch.empty((Q, K), dtype=torch.int32, device=scores.device)
     if token_ids is None:
         token_ids = torch.empty((Q, W), dtype=torch.int32, device=scores.device)
-    need = dsa_topk_workspace_bytes(Q, P, K)
-    if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    workspace = _topk_ws(workspace, dsa_topk_workspace_bytes(Q, P, K), scores.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.load().dsa_topk_pools_expand(
@@ -160,7 +183,8 @@ def dsa_index_topk_pools_expand(q, w, scale: float, k_pool, pool_start, pool_val
                                 token_ids=None, workspace=None):
     """dsa_index_scores then dsa_topk_pools_expand over row blocks whose scores
     fit 64 MiB -> (pool_ids [Q, K], token_ids [Q, W]), bit-identical to the two
-    calls.  A workspace passed in must start zeroed (the top-k counters)."""
+    calls.  A workspace passed in must come from topk_workspace (the top-k
+    counters at its start must be zero)."""
     Q, H, D = q.shape
     B, P_max = pool_start.shape
     _check_pool_cache(k_pool, B, P_max, D)
@@ -168,8 +192,7 @@ def dsa_index_topk_pools_expand(q, w, scale: float, k_pool, pool_start, pool_val
         pool_ids = torch.empty((Q, K), dtype=torch.int32, device=q.device)
     if token_ids is None:
         token_ids = torch.empty((Q, W), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        workspace = torch.zeros(dsa_index_topk_workspace_bytes(Q, P_max, K), dtype=torch.uint8, device=q.device)
+    workspace = _topk_ws(workspace, dsa_index_topk_workspace_bytes(Q, P_max, K), q.device)
     st = _lib.load().dsa_index_topk_pools_expand(
         _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
         _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
@@ -301,6 +324,7 @@ def bind_index_scores(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_
 
 def bind_topk_pools(scores, K, pool_ids, workspace) -> BoundCall:
     Q, P = scores.shape
+    workspace = _topk_ws(workspace, 1, scores.device)
     return BoundCall("dsa_topk_pools", (
         _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
@@ -308,6 +332,7 @@ def bind_topk_pools(scores, K, pool_ids, workspace) -> BoundCall:
 
 def bind_topk_pools_expand(scores, K, pool_ids, row_seq, pool_start, kpool, token_ids, workspace) -> BoundCall:
     Q, P = scores.shape
+    workspace = _topk_ws(workspace, 1, scores.device)
     B, P_max = pool_start.shape
     return BoundCall("dsa_topk_pools_expand", (
         _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
@@ -353,6 +378,7 @@ def bind_index_topk_pools_expand(q, w, scale, k_pool, pool_start, pool_valid, ln
     Q, H, D = q.shape
     B, P_max = pool_start.shape
     _check_pool_cache(k_pool, B, P_max, D)
+    workspace = _topk_ws(workspace, 1, q.device)
     return BoundCall("dsa_index_topk_pools_expand", (
         _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
         _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),

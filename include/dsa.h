@@ -14,14 +14,19 @@
  *
  * Conventions shared by every call
  *   - Every tensor pointer is a caller-owned DEVICE pointer to a dense,
- *     row-major array (innermost index last, no padding).  Scalars are by value.
+ *     row-major array (innermost index last, no padding), with one exception:
+ *     the pool cache k_pool is tile-interleaved and padded to whole 16-pool
+ *     tiles (layout below, DSA_POOL_CACHE_POOLS).  Scalars are by value.
  *   - The library allocates nothing and keeps no pointer after it returns.
  *     Calls that need scratch take a caller-sized workspace (device memory);
  *     its size comes from the matching *_workspace_bytes function, which is a
  *     pure host computation.
  *   - Work is queued on `stream` (a hipStream_t; NULL = the default stream) and
- *     the call returns without synchronising the host.  Calls keep no state and
- *     may run concurrently on different streams with disjoint outputs.
+ *     the call returns without synchronising the host.  Calls keep no state
+ *     and may run concurrently on different streams with disjoint outputs and
+ *     workspaces, with one exception: the counter block of a top-k workspace
+ *     (see dsa_topk_pools) carries state from call to call, so calls that
+ *     share one top-k workspace must not overlap.
  *   - Geometry is never defaulted: every dimension is an argument.
  *   - Every call checks its arguments on the host first.  On a negative status
  *     nothing was launched and no output was touched.
@@ -90,7 +95,7 @@ const char* dsa_status_string(int status);
 
 /* ABI version of this header (bumped on any signature change). */
 int dsa_abi_version(void);
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 /*
  * dsa_kpool_compress -- pooled index keys.
@@ -173,10 +178,19 @@ int dsa_kpool_append(const void* k, const void* gate, const uint8_t* valid, cons
  *
  *   q [Q, H, D] act     w [Q, H] fp32     gamma, beta [D] fp32
  *   k_pool: pool cache, B * DSA_POOL_CACHE_POOLS(P_max) * D act
- *   pool_start [B, P_max] int32
+ *   pool_start [B, P_max] int32 as dsa_kpool_compress / dsa_kpool_append
+ *              write it: a valid pool p starts at pool_start[b,0] + p*kpool
+ *              (pool p begins kpool*p tokens after the anchor); the decode
+ *              kernel relies on this and reads pool_start[b,0] only
  *   pool_valid [B, P_max] uint8           row_seq, row_pos [Q] int32
  *   scores [Q, P_max] fp32 (out)
  * Requires D in {32, 64, 128} and 1 <= H <= 64.
+ * Accuracy: |score - exact| <= 1e-3 |exact| + 1e-5 sum_h |w| |scale|
+ * sum_c |q kn|.  The bf16 matrix-core path (D = 128, H in {16, 32}) forms
+ * the LayerNorm mean and variance from sum_c x and sum_c x^2 in fp32, which
+ * holds that bound for pooled keys whose mean over the D channels is at most
+ * 100 standard deviations from zero (|mean| <= 100 sigma); keys further off
+ * centre lose accuracy in the variance (about 3e-3 relative at 300 sigma).
  */
 int dsa_index_scores(const void* q, const float* w, float scale, const void* k_pool,
                      const int32_t* pool_start, const uint8_t* pool_valid, const float* ln_gamma,
@@ -199,14 +213,30 @@ int dsa_index_scores(const void* q, const float* w, float scale, const void* k_p
  *   scores [Q, P] fp32     pool_ids [Q, K] int32 (out)
  *   workspace: device buffer of dsa_topk_workspace_bytes(Q, P, K) bytes
  *              (may be NULL when that is 0).  Its first
- *              DSA_TOPK_COUNTER_BYTES bytes are merge counters: zero-fill
- *              them before the first use; every call leaves them at zero, so
- *              the buffer then serves calls of any shape that fit it (the
- *              rest is scratch).  Calls that share a workspace must not
- *              overlap.
+ *              DSA_TOPK_COUNTER_BYTES bytes are per-row merge counters, the
+ *              one piece of state a call carries: the chunk workgroups of a
+ *              split row count themselves in, and the last to arrive merges
+ *              the row and sets its counter back to zero.  So:
+ *                - before the first use, zero the counter block with
+ *                  dsa_topk_workspace_init (or any zero fill);
+ *                - every call that runs to completion leaves the counters
+ *                  at zero, so one buffer then serves calls of any shape
+ *                  that fit it (the rest of it is scratch);
+ *                - calls that share a workspace must not overlap (they
+ *                  would count into the same counters);
+ *                - a call that did not run to completion (its stream failed
+ *                  or the process was stopped while it ran) may leave
+ *                  counters non-zero, after which the next call on that
+ *                  workspace would merge too early or never: zero the
+ *                  counter block again before reusing the workspace.
  * Requires 1 <= K <= DSA_MAX_SELECT_K and P <= 524288.
  */
 size_t dsa_topk_workspace_bytes(int Q, int P, int K);
+/* Zero the counter block (the first min(workspace_bytes,
+ * DSA_TOPK_COUNTER_BYTES) bytes) of a top-k workspace with a fill kernel
+ * queued on `stream` (no memset node, so it may be captured in a HIP graph).
+ * For a new workspace, and after a call on it did not complete. */
+int dsa_topk_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 int dsa_topk_pools(const float* scores, int Q, int P, int K, int32_t* pool_ids, void* workspace,
                    size_t workspace_bytes, void* stream);
 

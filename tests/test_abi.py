@@ -32,10 +32,16 @@ def test_binding_signatures_cover_header(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dsa_abi_version() == 1
-    for code in range(0, -6, -1):
-        assert lib.dsa_status_string(code)
+    assert lib.dsa_abi_version() == 2
+    texts = [lib.dsa_status_string(code) for code in range(0, -6, -1)]
+    assert all(texts) and len(set(texts)) == len(texts)
     assert lib.dsa_status_string(0) == b"ok"
+
+
+def test_topk_workspace_init_checks(lib):
+    from dsa_decode_amd._lib import DSA_ERR_NULL, DSA_OK
+    assert lib.dsa_topk_workspace_init(None, 1024, None) == DSA_ERR_NULL
+    assert lib.dsa_topk_workspace_init(FAKE, 0, None) == DSA_OK      # nothing to clear: no launch
 
 
 def test_binding_constants_match_header():

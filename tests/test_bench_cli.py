@@ -20,11 +20,12 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_decode_algorithmic_bytes():
-    # per pool: 128 bf16 key channels + 1 valid byte + 4 start bytes read, 4 score bytes written
-    assert bench.score_bytes_per_pool() == 256 + 1 + 4 + 4
+    # per pool: 128 bf16 key channels + 1 valid byte read, 4 score bytes written (a pool's
+    # start is first_valid + p * kpool: one value per sequence, not a per-pool read)
+    assert bench.score_bytes_per_pool() == 256 + 1 + 4
     Q, P, H, D = 4, 65536, 32, 128
     total = bench.score_bytes_per_pool() * Q * P + Q * H * D * 2 + Q * H * 4 + 2 * D * 4
-    assert total == 69502464
+    assert total == 68453888                          # 68.45 MB per launch
 
 
 def test_prefill_candidate_pairs_closed_form():

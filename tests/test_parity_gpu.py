@@ -270,7 +270,9 @@ def test_topk_workspace_reuse_across_calls_and_shapes():
     # the next call's merge would start from a wrong count
     shapes = [(4, 65536, 512), (2, 30000, 256), (3, 16384, 512), (4, 65536, 512)]
     need = max(ops().dsa_topk_workspace_bytes(Q, P, K) for Q, P, K in shapes)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")   # garbage, then the counter block zeroed
+    ops().dsa_topk_workspace_init(ws)
+    assert (ws[: ops().DSA_TOPK_COUNTER_BYTES] == 0).all() and (ws[ops().DSA_TOPK_COUNTER_BYTES:] == 0xA5).all()
     for i, (Q, P, K) in enumerate(shapes):
         s = synth.random_scores(Q, P, seed=90 + i, tie_levels=0 if i % 2 else 64, neg_inf_frac=0.1)
         got = ops().dsa_topk_pools(dev(s), K, workspace=ws).cpu().numpy()
@@ -391,6 +393,40 @@ def test_scores_paths_ragged_causal_and_mixed_rows(H, D, dtype):
                                  dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(row_pos)), kp).cpu().numpy()
     ref = O.index_scores(q, w, D ** -0.5, k_pool, pool_start, pool_valid, gamma, beta, 1e-5, row_seq, row_pos, kp)
     A = score_scale(q, w, D ** -0.5, k_pool, gamma, beta, 1e-5, row_seq, range(Q))
+    assert_scores_close(got, ref, A)
+
+
+@pytest.mark.parametrize("mu_over_sigma", [30.0, 100.0])
+@pytest.mark.parametrize("Q", [4, 80])
+def test_scores_offset_keys_layernorm(mu_over_sigma, Q):
+    # The score kernels fold the LayerNorm into the contraction and take its
+    # statistics from sum x and sum x^2; pooled keys with a large common mean
+    # are where that loses precision.  k_norm subtracts the mean ("Module
+    # glm5next_dsa", "Traps carried from Slice 8"), so these keys must score
+    # as zero-mean ones do.  Keys: mu + sigma * N(0, 1) per channel, with a
+    # per-pool sign on mu; Q = 4 takes the decode kernel, Q = 80 the many-rows
+    # kernel.  The header states |mean| <= 100 sigma as the supported domain.
+    rng = np.random.default_rng(int(mu_over_sigma) * 7 + Q)
+    B, P, kp, H, D = 2, 3000, 4, 32, 128
+    sigma = 0.05
+    sign = np.where(rng.random((B, P, 1)) < 0.5, -1.0, 1.0)
+    x = sign * mu_over_sigma * sigma + sigma * rng.standard_normal((B, P, D))
+    k_pool = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    ps = np.tile((np.arange(P) * kp + 1).astype(np.int32), (B, 1))
+    pv = np.ones((B, P), np.uint8)
+    row_seq = (np.arange(Q) % B).astype(np.int32)
+    row_pos = np.full(Q, P * kp + 3, np.int32)
+    row_pos[1::3] = rng.integers(kp, P * kp, row_pos[1::3].size)  # causal cut inside the row too
+    q = torch.from_numpy(rng.standard_normal((Q, H, D)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.random((Q, H)) / H).astype(np.float32))
+    gamma = torch.from_numpy((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+    beta = torch.from_numpy((0.02 * rng.standard_normal(D)).astype(np.float32))
+    got = ops().dsa_index_scores(dev(q), dev(w), D ** -0.5, dev(tile_pool_cache(k_pool)),
+                                 dev(torch.from_numpy(ps)), dev(torch.from_numpy(pv)), dev(gamma), dev(beta), 1e-5,
+                                 dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(row_pos)), kp).cpu().numpy()
+    ref = O.index_scores(q, w, D ** -0.5, k_pool, ps, pv, gamma, beta, 1e-5, row_seq, row_pos, kp)
+    A = score_scale(q, w, D ** -0.5, k_pool, gamma, beta, 1e-5, row_seq, range(Q))
+    assert np.isfinite(ref).sum() > Q * P // 3
     assert_scores_close(got, ref, A)
 
 
@@ -666,12 +702,28 @@ def test_end_to_end_prefill_chunk_on_gpu():
     assert np.abs(lse.cpu().numpy()[rows] - rl).max() <= 2e-3 * max(1.0, np.abs(rl).max())
 
 
-@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3)])
+def _streamed_vs_oracle(scores: np.ndarray, ids: np.ndarray, tok: np.ndarray, rows, row_seq, pool_start,
+                        kp: int, K: int, W: int) -> None:
+    """The streamed entry's pool ids and token ids on the given rows against
+    the oracle's top-k and expansion of the same score rows (the scores come
+    from the GPU's score kernel: top-k and expansion are exact functions of
+    them, so the comparison is bit-exact)."""
+    rows = list(rows)
+    ref_ids = O.topk_pools(scores[rows], K)
+    np.testing.assert_array_equal(ids[rows], ref_ids)
+    ref_tok = O.expand_selection(ref_ids, np.asarray(row_seq)[rows], pool_start, kp, W)
+    np.testing.assert_array_equal(tok[rows], ref_tok)
+
+
+@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3), (835, 20000, 2)])
 def test_streamed_index_topk_bit_identical(Q, P, B):
     # dsa_index_topk_pools_expand over row blocks of at most 64 MiB of scores
-    # gives the bits of dsa_index_scores + dsa_topk_pools_expand: 2 blocks with
-    # a ragged last block that takes the split top-k (1000 x 20000), one block
-    # with the split top-k (decode rows), and a small case
+    # gives the bits of dsa_index_scores + dsa_topk_pools_expand, and those of
+    # the oracle's top-k and expansion of the same scores: 2 blocks with a
+    # ragged last block that takes the split top-k (1000 x 20000), one block
+    # with the split top-k (decode rows), a small case, and 832 + 3 rows (the
+    # last block of 3 rows takes the decode score kernel while the others take
+    # the many-rows kernel)
     rng = np.random.default_rng(Q + P)
     H, D, kp, K = 32, 128, 4, 512
     W = K * kp + 3
@@ -693,18 +745,23 @@ def test_streamed_index_topk_bit_identical(Q, P, B):
             dev(torch.from_numpy(row_pos)), kp)
     scores = ops().dsa_index_scores(*args)
     ids_a, tok_a = ops().dsa_topk_pools_expand(scores, K, args[9], args[4], kp, W)
-    ws = torch.zeros(ops().dsa_index_topk_workspace_bytes(Q, P, K), dtype=torch.uint8, device="cuda")
+    ws = ops().topk_workspace(ops().dsa_index_topk_workspace_bytes(Q, P, K))
     for _ in range(2):   # twice on one workspace: the top-k counters are left zero
         ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, K, W, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(ids_a, ids_b)
         assert torch.equal(tok_a, tok_b)
-    assert_topk_property(scores.cpu().numpy()[:3], ids_b.cpu().numpy()[:3], K)
+    # against the oracle on the GPU's scores: the first rows, the last rows
+    # (the ragged last block) and a sample
+    rows = sorted(set([0, 1, Q // 2] + list(range(max(0, Q - 4), Q)) + rng.integers(0, Q, 4).tolist()))
+    _streamed_vs_oracle(scores.cpu().numpy(), ids_b.cpu().numpy(), tok_b.cpu().numpy(), rows, row_seq, ps, kp, K, W)
 
 
 def test_streamed_index_topk_prefill_chunk_full_size():
     # the prefill chunk (4096 rows x 32768 pools, forced ties at the cut): 8 row
-    # blocks of 512, bit-identical to the unfused calls
+    # blocks of 512, bit-identical to the unfused calls and, on sampled rows
+    # (row 0, the block edges, row 4095), to the oracle's top-k and expansion of
+    # the GPU's scores
     d = wl_data_prefill()
     wl, ip = d["wl"], d["ip"]
     pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl))
@@ -713,9 +770,15 @@ def test_streamed_index_topk_prefill_chunk_full_size():
             dev(ip["row_pos"]), wl.kp)
     scores = ops().dsa_index_scores(*args)
     ids_a, tok_a = ops().dsa_topk_pools_expand(scores, wl.K, args[9], args[4], wl.kp, wl.W)
+    rows = [0, 511, 512, 1023, 2047, 2048, 3000, 3583, 3584, 4095]
+    s_rows = scores[rows].cpu().numpy()
     del scores
     assert ops().dsa_index_topk_workspace_bytes(wl.Q, wl.P_max, wl.K) == 512 * wl.P_max * 4
     ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, wl.K, wl.W)
     torch.cuda.synchronize()
     assert torch.equal(ids_a, ids_b)
     assert torch.equal(tok_a, tok_b)
+    full = np.zeros((wl.Q, wl.P_max), np.float32)
+    full[rows] = s_rows
+    _streamed_vs_oracle(full, ids_b.cpu().numpy(), tok_b.cpu().numpy(), rows, ip["row_seq"].numpy(),
+                        d["comp"]["pool_start"], wl.kp, wl.K, wl.W)

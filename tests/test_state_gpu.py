@@ -162,7 +162,7 @@ def test_decode_step_in_a_hip_graph_matches_eager():
             tok=torch.empty((Q, W), dtype=torch.int32, device="cuda"),
             out=torch.empty((Q, wl.Hm, wl.Dl), dtype=torch.bfloat16, device="cuda"),
             lse=torch.empty((Q, wl.Hm), dtype=torch.float32, device="cuda"),
-            tws=torch.zeros(max(1, lib.dsa_topk_workspace_bytes(Q, P_max, K)), dtype=torch.uint8, device="cuda"),
+            tws=ops().topk_workspace(lib.dsa_topk_workspace_bytes(Q, P_max, K)),
             mws=torch.zeros(max(1, lib.dsa_sparse_mla_workspace_bytes(Q, wl.Hm, wl.Dl, W, 1)),
                             dtype=torch.uint8, device="cuda"))
         return side
