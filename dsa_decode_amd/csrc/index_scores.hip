@@ -27,8 +27,9 @@
 // keeps its pool tiles in registers and runs a group of rows of one sequence
 // over them (rows staged four at a time in LDS).
 //
-// Per pool the decode kernel reads 256 B of key + 1 B valid + 4 B start and
-// writes 4 B of score: it is HBM-bound.
+// Per pool the decode kernel reads 256 B of key + 1 B valid and writes 4 B of
+// score (the pool's start follows from the sequence's first start): it is
+// HBM-bound.
 #include <climits>
 
 #include "dsa_common.hpp"
@@ -147,15 +148,16 @@ __device__ __forceinline__ TileAcc<NH> tile_mfma(const u32x4 (&x)[4], const bf16
   for (int mb = 0; mb < NH; ++mb) t.acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   t.sacc = f32x4{0.f, 0.f, 0.f, 0.f};
   t.gacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // in each k-step the two products that accumulate into one head block are
+  // separated by other MFMAs (measured faster than issuing them back to back)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bf16x8 bx = as_bf16x8(x[i]);
 #pragma unroll
-    for (int mb = 0; mb < NH; ++mb) {
-      t.acc[mb] = mfma16x16x32(ahi[mb][i], bx, t.acc[mb]);
-      t.acc[mb] = mfma16x16x32(alo[mb][i], bx, t.acc[mb]);
-    }
+    for (int mb = 0; mb < NH; ++mb) t.acc[mb] = mfma16x16x32(ahi[mb][i], bx, t.acc[mb]);
     t.sacc = mfma16x16x32(ones, bx, t.sacc);  // every row: sum_c x_c of pool (lane & 15)
+#pragma unroll
+    for (int mb = 0; mb < NH; ++mb) t.acc[mb] = mfma16x16x32(alo[mb][i], bx, t.acc[mb]);
     t.gacc = mfma16x16x32(bx, bx, t.gacc);    // Gram block: <x_m, x_n>
   }
   return t;
@@ -232,20 +234,26 @@ __device__ __forceinline__ void load_operands(const uint16_t (*ghi)[kIsLd], cons
   }
 }
 
-// Decode kernel.  A workgroup owns 4*NT consecutive 16-pool tiles of one row
-// (wave w takes the NT consecutive tiles w*NT ..: each wave streams one
-// contiguous 4*NT KiB stretch of the pool cache, which measured faster than
-// interleaving the waves tile by tile); each wave runs through its tiles with a
-// kStreamRing-deep register ring (the next tiles' key loads in flight while one
-// is computed).  In the tile-interleaved pool cache each of a tile's 4 key
+// Decode kernel.  A workgroup owns 4*NT 16-pool tiles of one row, taken in
+// blocks of PW = min(NT, 2) consecutive tiles per wave: in block b the row's
+// workgroups cover one contiguous stretch of the pool cache together (wave w
+// of workgroup g reads tiles b*G*4*PW + g*4*PW + PW*w ..), so the requests in
+// flight at any time fall in a window that moves through the cache rather
+// than in 4*G separate stretches (measured faster, as the plain read stream
+// is faster with short per-wave stretches).  Each wave runs through its tiles
+// with a kStreamRing-deep register ring: a ring slot is refilled right after
+// the MFMAs that read it are issued, and scheduling barriers keep the
+// compiler from sinking those loads below the epilogue (it otherwise issues
+// several tiles' MFMAs first and the last loads only after all earlier ones
+// have landed).  In the tile-interleaved pool cache each of a tile's 4 key
 // loads per lane covers 1 KiB of contiguous memory and lands directly in the
-// matrix-core operand layout; keys are read non-temporally (each byte is used
-// once).  The row's folded LayerNorm operands are staged once in LDS (8
+// matrix-core operand layout; keys are read non-temporally (each byte is
+// used once).  The row's folded LayerNorm operands are staged once in LDS (8
 // threads per head) while the first ring of keys is in flight.  The scores
-// are gathered in LDS and written with coalesced stores; the candidate test
-// is applied there, from pool_start / pool_valid loaded (coalesced) at the
-// start and held in registers, so the metadata never delays the first tile.
-constexpr int kStreamRing = 4;           // tiles in flight per wave
+// are gathered in LDS and written at the end with coalesced stores (stores
+// interleaved with the key stream measured slower); the candidate test is
+// applied there, from pool_valid loaded at the start.
+constexpr int kStreamRing = 2;           // tiles in flight per wave
 constexpr int kTileElems = 16 * kIsD;    // 4 KiB of bf16 keys
 
 __device__ __forceinline__ u32x4 ld_stream(const uint16_t* p) {
@@ -262,7 +270,9 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int H = NH * 16;
   constexpr int kPools = kIsWaves * NT * 16;  // pools per workgroup
   constexpr int R = NT < kStreamRing ? NT : kStreamRing;
+  constexpr int PW = NT < 2 ? NT : 2;         // consecutive tiles per wave and block
   constexpr int MP = (kPools + kIsThreads - 1) / kIsThreads;  // metadata entries per thread
+  static_assert(NT % R == 0 && NT % PW == 0, "the ring and the blocks divide the wave's tiles");
   __shared__ uint16_t ghi[H][kIsLd];
   __shared__ uint16_t glo[H][kIsLd];
   __shared__ float sQB[H], sW[H];
@@ -276,32 +286,46 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int pos = row_pos[r];
   const bool ok = b >= 0 && b < B;
   const int P_tiles = pool_tiles(P_max);
-  const int t0 = blockIdx.x * (kIsWaves * NT);  // first tile of the workgroup
-  const int p0 = t0 * 16;
+  const int G = gridDim.x;  // workgroups per row
+  // tile of the wave's j-th tile (see above)
+  auto tile_of = [&](int wv, int j) {
+    return (j / PW) * (G * kIsWaves * PW) + int(blockIdx.x) * (kIsWaves * PW) + PW * wv + (j % PW);
+  };
+  // store slot e (< kPools) of the workgroup: in block e / (64 PW), the
+  // (e % (64 PW))-th of its 64 PW contiguous pools; -> (LDS index, pool)
+  auto slot = [&](int e, int& lp) {
+    const int bl = e / (64 * PW), k = (e % (64 * PW)) >> 4;
+    const int wv = k / PW, j = bl * PW + k % PW;
+    lp = (wv * NT + j) * 16 + (e & 15);
+    return tile_of(wv, j) * 16 + (e & 15);
+  };
   const size_t seq0 = size_t(ok ? b : 0) * P_max;
   const uint16_t* kseq = k_pool + size_t(ok ? b : 0) * P_tiles * kTileElems;
 
-  // operand loads first, then the metadata of the pools this thread stores
-  // (used only at the end), then the first ring of key tiles
+  // operand loads first, then the validity of the pools this thread stores
+  // (used only at the end), then the first ring of key tiles.  A pool's start
+  // is the sequence's first start plus p * kpool (pool p begins kpool * p
+  // tokens after the anchor), so one start per sequence is read instead of
+  // one per pool.
   RowIn rin;
   if (tid < H * 8) rin = stage_row_load(q + size_t(r) * H * kIsD, w + size_t(r) * H, gamma, beta, tid);
-  int st[MP];
+  const int start0 = pool_start[seq0];
   uint8_t vl[MP];
 #pragma unroll
   for (int u = 0; u < MP; ++u) {
-    const int lp = u * kIsThreads + tid;
-    const int p = p0 + lp;
-    const size_t pi = (ok && p < P_max && lp < kPools) ? seq0 + p : 0;
-    st[u] = pool_start[pi];
+    const int e = u * kIsThreads + tid;
+    int lp;
+    const int p = slot(e, lp);
+    const size_t pi = (ok && e < kPools && p < P_max) ? seq0 + p : 0;
     vl[u] = pool_valid[pi];
   }
   u32x4 xb[R][4];
-  auto issue = [&](int slot, int j) {
-    const int t = t0 + wave * NT + j;
+  auto issue = [&](int rs, int j) {
+    const int t = tile_of(wave, j);
     const bool in = j < NT && t < P_tiles;
     const uint16_t* src = kseq + size_t(in ? t : 0) * kTileElems + 8 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xb[slot][i] = ld_stream(src + 512 * i);
+    for (int i = 0; i < 4; ++i) xb[rs][i] = ld_stream(src + 512 * i);
   };
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -317,9 +341,11 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   load_operands<NH>(ghi, glo, sQB, sW, kg, ln, scale, ahi, alo, cQ, cW);
   // software pipeline: tile j+1's matrix-core work is issued before tile j's
   // vector epilogue, which then runs while the matrix cores are busy; a ring
-  // slot is refilled once its tile's MFMAs are issued
+  // slot is refilled as soon as its tile's MFMAs are issued, and the
+  // scheduling barriers keep each phase in that order
   TileAcc<NH> cur = tile_mfma<NH>(xb[0], ahi, alo);
   if (R < NT) issue(0, R);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j0 = 0; j0 < NT; j0 += R) {
 #pragma unroll
@@ -331,22 +357,27 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
         nxt = tile_mfma<NH>(xb[s1], ahi, alo);
         if (j + 1 + R < NT) issue(s1, j + 1 + R);  // resolved at compile time (unrolled)
       }
+      __builtin_amdgcn_sched_barrier(0);
       const float sc = tile_epilogue<NH>(cur, cQ, cW, scale, eps, ln, diag_addr);
       // the four lane groups hold the same sum: all write it (no branch)
       sOut[(wave * NT + j) * 16 + ln] = sc;
+      __builtin_amdgcn_sched_barrier(0);
       if (j + 1 < NT) cur = nxt;
     }
   }
   __syncthreads();
   // candidate test (valid pool whose last token is at or before the row's
-  // position) and coalesced stores
-  const int last_ok = pos - (kp - 1);
+  // position: start0 + p * kpool + kpool - 1 <= pos, in 64-bit so that no
+  // position overflows) and coalesced stores
+  const long last_ok = long(pos) - (kp - 1) - start0;
   float* srow = scores + size_t(r) * P_max;
 #pragma unroll
   for (int u = 0; u < MP; ++u) {
-    const int lp = u * kIsThreads + tid;
-    const int p = p0 + lp;
-    if (lp < kPools && p < P_max) srow[p] = (ok && vl[u] != 0 && st[u] <= last_ok) ? sOut[lp] : -INFINITY;
+    const int e = u * kIsThreads + tid;
+    int lp;
+    const int p = slot(e, lp);
+    if (e < kPools && p < P_max)
+      srow[p] = (ok && vl[u] != 0 && long(p) * kp <= last_ok) ? sOut[lp] : -INFINITY;
   }
 }
 
@@ -581,8 +612,8 @@ static IsPlan is_plan(int Q, int P_max) {
   if (Q <= 64) {
     // decode: 8 tiles per wave (512 pools per workgroup, two workgroups per
     // CU) while that gives >= 256 workgroups, else 4 tiles, else 1.  Measured
-    // at 4 x 65536 pools: 8 tiles with a 4-deep ring beat 16 tiles (4- or
-    // 6-deep) and deeper rings at 8 (more key bytes in flight stream worse)
+    // at 4 x 65536 pools: 8 tiles per wave beat 4 (1024 workgroups), and a
+    // 2-deep ring with interleaved tile pairs beat a 4-deep ring
     if (long(Q) * ((ntile + 31) / 32) >= 256) pl.tw = 8;
     else if (long(Q) * ((ntile + 15) / 16) >= 128) pl.tw = 4;
     else pl.tw = 1;
