@@ -39,6 +39,8 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "dsa_sparse_mla_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                                              c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p]),
     "dsa_index_topk_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
     "dsa_index_topk_pools_expand": (c_int, [c_void_p, c_void_p, c_float, c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_float, c_void_p, c_void_p,
@@ -50,11 +52,13 @@ SIGNATURES = {
                                             c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
-DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, -1, -2, -3, -4, -5
+DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP, DSA_ERR_TOO_LARGE = (
+    0, -1, -2, -3, -4, -5, -6)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_MAX_KPOOL = 8
 DSA_MAX_SELECT_K = 2048
 DSA_TOPK_COUNTER_BYTES = 262144
+DSA_MLA_SCRATCH_BYTES = 33554432
 
 _lib = None
 

@@ -9,6 +9,7 @@ extern "C" const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "a dimension is outside what the kernels implement";
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_HIP: return "HIP launch error";
+    case DSA_ERR_TOO_LARGE: return "the call needs more scratch than the fixed-size buffer holds";
     default: return "unknown status";
   }
 }

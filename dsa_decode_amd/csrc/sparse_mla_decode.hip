@@ -32,6 +32,8 @@
 // rounded to bf16 (in the lanes' order: 512 B per store instruction), and
 // their fp32 log-sum-exp; a combine launch merges them in fp32.  The gather is
 // the HBM traffic (1 KiB per selected token).
+#include <mutex>
+
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
 
@@ -846,21 +848,24 @@ extern "C" size_t dsa_sparse_mla_workspace_bytes(int Q, int Hm, int Dl, int W, i
          align256(size_t(Q) * pl.nsplit * Hm * sizeof(float));
 }
 
-extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_seq,
-                                     const int32_t* token_ids, int Q, int Hm, int Dl, int B,
-                                     int T_max, int W, float sm_scale, int dtype, void* out,
-                                     float* lse, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+// Argument checks of dsa_sparse_mla_decode (and its allocation-free variant).
+static int mla_check(const void* q_lat, const void* kv, const int32_t* row_seq, const int32_t* token_ids,
+                     int Q, int Hm, int Dl, int B, int T_max, int W, int dtype, const void* out) {
   if (!q_lat || !kv || !row_seq || !token_ids || !out) return DSA_ERR_NULL;
   if (Q <= 0 || Hm <= 0 || Dl <= 0 || B <= 0 || T_max <= 0 || W <= 0) return DSA_ERR_SHAPE;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
   if (Dl != 64 && Dl != 128 && Dl != 256 && Dl != 512) return DSA_ERR_UNSUPPORTED;
   if (Hm > 128 || Q > 65535) return DSA_ERR_UNSUPPORTED;
   if (long(W) > long(kMlaSplit) * kMaxSplit) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+// The launches of dsa_sparse_mla_decode on a checked argument set, with the
+// split partials in `workspace` (at least dsa_sparse_mla_workspace_bytes).
+static int mla_launch(const void* q_lat, const void* kv, const int32_t* row_seq, const int32_t* token_ids, int Q,
+                      int Hm, int Dl, int B, int T_max, int W, float sm_scale, int dtype, void* out, float* lse,
+                      void* workspace, hipStream_t s) {
   const MlaPlan pl = mla_plan(Q, Hm, Dl, W, dtype);
-  const size_t need = dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
   if (!pl.mfma) {
     dim3 grid(Hm, Q);
     if (dtype == DSA_BF16)
@@ -903,6 +908,69 @@ extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const in
   hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, pl.nsplit,
                      Hm, (uint16_t*)out, lse);
   return launch_status();
+}
+
+extern "C" int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_seq,
+                                     const int32_t* token_ids, int Q, int Hm, int Dl, int B,
+                                     int T_max, int W, float sm_scale, int dtype, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  const int st = mla_check(q_lat, kv, row_seq, token_ids, Q, Hm, Dl, B, T_max, W, dtype, out);
+  if (st) return st;
+  const size_t need = dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  return mla_launch(q_lat, kv, row_seq, token_ids, Q, Hm, Dl, B, T_max, W, sm_scale, dtype, out, lse, workspace,
+                    as_stream(stream));
+}
+
+// The allocation-free variant keeps the split partials in this file-scope
+// device array: every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol); it passes
+// the device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[DSA_MLA_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchDevices];
+
+// the current device's address of `scratch` (looked up on the first call there)
+static int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return DSA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kScratchDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return DSA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+extern "C" int dsa_sparse_mla_decode_noalloc(const void* q_lat, const void* kv, const int32_t* row_seq,
+                                             const int32_t* token_ids, int Q, int Hm, int Dl, int B, int T_max,
+                                             int W, float sm_scale, int dtype, void* out, float* lse,
+                                             void* stream) {
+  int st = mla_check(q_lat, kv, row_seq, token_ids, Q, Hm, Dl, B, T_max, W, dtype, out);
+  if (st) return st;
+  const size_t need = dsa_sparse_mla_workspace_bytes(Q, Hm, Dl, W, dtype);
+  if (need > size_t(DSA_MLA_SCRATCH_BYTES)) return DSA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st) return st;
+  }
+  return mla_launch(q_lat, kv, row_seq, token_ids, Q, Hm, Dl, B, T_max, W, sm_scale, dtype, out, lse, ws,
+                    as_stream(stream));
 }
 
 extern "C" size_t dsa_sparse_mla_paged_workspace_bytes(int Q, int Hm, int Dl, int W) {

@@ -12,7 +12,8 @@ import torch
 
 from . import _lib
 from .layout import pool_cache_pools
-from ._lib import DSA_BF16, DSA_F32, DSA_FP8_E4M3, DSA_TOPK_COUNTER_BYTES, DsaError, check  # noqa: F401
+from ._lib import (DSA_BF16, DSA_F32, DSA_FP8_E4M3, DSA_MLA_SCRATCH_BYTES, DSA_TOPK_COUNTER_BYTES,  # noqa: F401
+                   DsaError, check)
 
 _ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
 
@@ -246,6 +247,22 @@ def dsa_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale: float, out=No
         _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
         ws_ptr, ws_bytes, _stream())
     check("dsa_sparse_mla_decode", st)
+    return out, lse
+
+
+def dsa_sparse_mla_decode_noalloc(q_lat, kv, row_seq, token_ids, sm_scale: float, out, lse=None):
+    """dsa_sparse_mla_decode with the split partials in the library's fixed
+    per-GPU buffer (no workspace; the caller passes out and lse)."""
+    Q, Hm, Dl = q_lat.shape
+    B, T_max, Dl2 = kv.shape
+    if Dl2 != Dl:
+        raise ValueError("q_lat and kv disagree on Dl")
+    st = _lib.load().dsa_sparse_mla_decode_noalloc(
+        _dev(q_lat, "q_lat", kv.dtype), _dev(kv, "kv"), _dev(row_seq, "row_seq", torch.int32),
+        _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, T_max, token_ids.shape[1], float(sm_scale),
+        _act_code(kv), _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
+        _stream())
+    check("dsa_sparse_mla_decode_noalloc", st)
     return out, lse
 
 

@@ -54,6 +54,7 @@ extern "C" {
 #define DSA_ERR_UNSUPPORTED  -3  /* a dimension outside what the kernels implement */
 #define DSA_ERR_WORKSPACE    -4  /* workspace missing or too small */
 #define DSA_ERR_HIP          -5  /* the HIP runtime reported an error at launch */
+#define DSA_ERR_TOO_LARGE    -6  /* the call needs more scratch than a fixed-size buffer holds */
 
 /* Size of the counter block at the start of a dsa_topk_pools workspace: the
  * same for every shape. */
@@ -302,6 +303,28 @@ int dsa_sparse_mla_decode(const void* q_lat, const void* kv, const int32_t* row_
                           const int32_t* token_ids, int Q, int Hm, int Dl, int B, int T_max,
                           int W, float sm_scale, int dtype, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Outputs, arguments, checks and errors are those of dsa_sparse_mla_decode
+ * (the same kernels, so the same bits).  The split partials go to a buffer of
+ * DSA_MLA_SCRATCH_BYTES bytes inside the library instead of a workspace:
+ *   - each GPU has its own copy, held until the process ends; its address is
+ *     looked up on the first call on that GPU (no allocation at any time);
+ *   - a call that needs more, i.e. dsa_sparse_mla_workspace_bytes(Q, Hm, Dl,
+ *     W, dtype) > DSA_MLA_SCRATCH_BYTES, returns DSA_ERR_TOO_LARGE and
+ *     launches nothing;
+ *   - every call on one GPU uses that GPU's buffer: calls that overlap on one
+ *     GPU (different streams, or host threads) race on it, so the caller must
+ *     order them (each call writes every partial it reads; nothing needs
+ *     clearing between calls).
+ */
+#define DSA_MLA_SCRATCH_BYTES 33554432
+int dsa_sparse_mla_decode_noalloc(const void* q_lat, const void* kv, const int32_t* row_seq,
+                                  const int32_t* token_ids, int Q, int Hm, int Dl, int B, int T_max,
+                                  int W, float sm_scale, int dtype, void* out, float* lse, void* stream);
 
 /*
  * dsa_index_topk_pools_expand -- dsa_index_scores, then dsa_topk_pools_expand,
