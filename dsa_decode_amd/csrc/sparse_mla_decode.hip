@@ -7,31 +7,36 @@
 // logits sm_scale * <q_lat_h, kv_j> over the listed tokens j, softmax, and the
 // softmax-weighted sum of the same kv_j rows.
 //
-// MFMA path (bf16, Dl = 512, Hm a multiple of 16).  A workgroup handles one
-// row, one group of 16 heads and a contiguous slice ("split") of 64 ids of the
-// row's list, with 4 waves:
-//   - the 64 listed latent rows (64 KiB) are moved straight into LDS by the
-//     load-to-LDS path, one 1 KiB row per load instruction (16 bytes per lane,
-//     the row swizzle applied through the source addresses); wave w gathers
-//     the rows of ids 16w .. 16w+15.  Each wave loads the 16 heads' q_lat
-//     (16 KiB, read from L2 by every split of the row) into registers;
-//   - wave w forms the logits of its 16 tokens for the 16 heads over the full
-//     latent width on the matrix cores (kv rows from LDS x q^T from
-//     registers), so no partial logits cross waves;
+// MFMA path (bf16, Dl = 512, Hm a multiple of 16), few rows (decode).  A
+// workgroup of 8 waves handles one row, one group of 16 heads and a slice of
+// 128 ids of the row's list, as two halves of 64 ids (waves 0..3 and 4..7):
+//   - the ids are requested first, the gather follows as soon as they are in:
+//     each half's 64 listed latent rows (64 KiB) go straight into LDS by the
+//     load-to-LDS path, one 1 KiB row per instruction (16 bytes per lane, the
+//     row swizzle applied through the source addresses); the 16 heads' q_lat
+//     rows follow into LDS once per workgroup (padded rows, so that the
+//     fragment reads of 16 heads hit distinct banks);
+//   - wave w of a half forms the logits of its 16 tokens for the 16 heads
+//     over the full latent width on the matrix cores (kv rows and q^T from
+//     LDS, every fragment read issued before the first MFMA), so no partial
+//     logits cross waves;
 //   - softmax: each wave takes its own maximum per head and forms P relative
-//     to it; P (bf16) and the per-wave maxima and sums go through LDS, and
-//     the value contraction scales the P operand by 2^(m_wave - m_row): no
-//     barrier waits for a row maximum before P is formed (one barrier
-//     publishes P);
-//   - wave w accumulates latent quarter w of O^T[dl, head] = kv^T . P^T over
-//     all 64 tokens, reading kv^T with the transposing LDS reads.
-// The swizzle spreads both LDS read patterns over the banks.  67 KiB of LDS
-// keeps two workgroups per CU.  The head groups of one (row, split) read the
-// same latent rows; their workgroup ids are spaced by a multiple of 8 so that
-// they share an XCD and its L2.  Splits write normalised partial outputs,
-// rounded to bf16 (in the lanes' order: 512 B per store instruction), and
-// their fp32 log-sum-exp; a combine launch merges them in fp32.  The gather is
-// the HBM traffic (1 KiB per selected token).
+//     to it; P (bf16) and the per-wave maxima and sums go through LDS, and the
+//     value contraction scales the P operand by 2^(m_wave - m_half): no
+//     barrier waits for a maximum before P is formed (one barrier publishes P);
+//   - wave w of a half accumulates latent quarter w of O^T[dl, head] = kv^T .
+//     P^T over its half's 64 tokens, reading kv^T with the transposing LDS
+//     reads;
+//   - the halves are merged in LDS (half 1 parks its unnormalised O, maximum
+//     and sum in its free row buffer; half 0 rescales both to the common
+//     maximum), so one partial per 128 ids leaves the workgroup.
+// The swizzle spreads both LDS read patterns over the banks.  ~150 KiB of LDS:
+// one workgroup per CU.  The head groups of one (row, slice) read the same
+// latent rows; their workgroup ids are spaced by a multiple of 8 so that they
+// share an XCD and its L2.  Slices write normalised partial outputs, rounded
+// to bf16 (in the lanes' order: 512 B per store instruction), and their fp32
+// log-sum-exp; a combine launch merges them in fp32.  The gather is the HBM
+// traffic (1 KiB per selected token).
 #include <mutex>
 
 #include "dsa_common.hpp"
@@ -92,16 +97,43 @@ struct KvPages {
   int max_pages, page_size, num_pages;
 };
 
+// Few rows (decode): one workgroup of 8 waves per (row, group of 16 heads,
+// slice of 128 ids).  The two halves of the slice (waves 0..3: ids 0..63,
+// waves 4..7: ids 64..127) each take the steps of mla_decode_mfma on their own
+// row buffer, and the halves are merged in LDS before the one partial of the
+// slice is written: half the partials of 64-id slices, so half the bytes the
+// combine reads.  The 16 heads' q_lat rows go into LDS once per workgroup
+// (load-to-LDS, one 1 KiB row per instruction, rows padded so that the
+// fragment reads of 16 heads hit distinct banks) instead of once per wave
+// into registers: the per-wave q loads were 4x the gathered bytes and held
+// back the id loads and the gather behind them.  The ids are requested first,
+// then q, then the gather as soon as the ids are in.
+constexpr int kMla2Ids = 2 * kMlaSplit;  // ids per workgroup
+constexpr int kMla2Threads = 512;
+constexpr int kMla2QLd = kMlaDl + 8;     // padded q row (1040 B: 16 heads' reads spread over the banks)
+
+struct alignas(16) Mla2Shared {
+  uint16_t rows[2][kMlaSplit][kMlaDl];  // each half's latent rows (swizzled as in MlaShared), 128 KiB
+  uint16_t q[16][kMla2QLd];             // the 16 heads' q_lat rows
+  struct {
+    uint16_t p[16][kMlaSplit + 8];
+    float m[16][4];
+    float l[16][4];
+  } x[2];                               // each half's softmax exchange
+  float mh[16], lh[16];                 // half 1's row maximum and sum per head, for the merge
+};
+
 template <int KV>
-__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_mfma(
+__global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     const uint16_t* __restrict__ q_lat, const void* __restrict__ kv_v, KvPages pages,
     const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int Hm, int B,
     int T_max, int W, int nsplit, int ns8, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   const uint16_t* __restrict__ kv = static_cast<const uint16_t*>(kv_v);
-  __shared__ MlaShared sh;
+  __shared__ Mla2Shared sh;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = w8 >> 2, w = w8 & 3;
   const int kg = lane >> 4, ln = lane & 15;
   const int HG = Hm >> 4;
   const int hg = blockIdx.x / ns8, sp = blockIdx.x % ns8;
@@ -112,38 +144,30 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   const bool bok = b >= 0 && b < B;
   const size_t seq_base = size_t(bok ? b : 0) * T_max;
 
-  // ids of this wave's 16 tokens (lanes 0..15), -1 when absent or out of
-  // range; for a paged cache, the token's physical row (and its fp8 scale)
+  // ids of this wave's 16 tokens (lanes 0..15), -1 when absent or out of range
+  int raw = -1;
+  const int c = sp * kMla2Ids + kMlaSplit * half + 16 * w + lane;
+  if (lane < 16 && c < W) raw = token_ids[size_t(r) * W + c];
+  // the token's row in the cache (for a paged cache, its physical row, and
+  // for fp8 pages its scale); -1 when absent or out of range
   int myid = -1;
   float mysc = 1.f;
   if (lane < 16) {
-    const int c = sp * kMlaSplit + 16 * w + lane;
-    if (c < W) {
-      const int id = token_ids[size_t(r) * W + c];
-      if (KV == kKvRows) {
-        myid = (bok && id >= 0 && id < T_max) ? id : -1;
-      } else if (bok && id >= 0 && id / pages.page_size < pages.max_pages) {
-        const int pg = pages.block_table[size_t(b) * pages.max_pages + id / pages.page_size];
-        if (pg >= 0 && pg < pages.num_pages) {
-          myid = pg * pages.page_size + id % pages.page_size;
-          if (KV == kKvPagedFp8) mysc = pages.scale[myid];
-        }
+    if (KV == kKvRows) {
+      myid = (bok && raw >= 0 && raw < T_max) ? raw : -1;
+    } else if (bok && raw >= 0 && raw / pages.page_size < pages.max_pages) {
+      const int pg = pages.block_table[size_t(b) * pages.max_pages + raw / pages.page_size];
+      if (pg >= 0 && pg < pages.num_pages) {
+        myid = pg * pages.page_size + raw % pages.page_size;
+        if (KV == kKvPagedFp8) mysc = pages.scale[myid];
       }
     }
   }
-  // q_lat of the 16 heads straight into registers in the matrix-core B layout
-  // (lane (kg, ln): head ln, 16-byte piece 4j + kg of the latent for k-step j);
-  // every split of the row reads the same 16 KiB, so it comes from L2
-  u32x4 qv[16];
-  {
-    const uint16_t* qrow = q_lat + (size_t(r) * Hm + hg * 16 + ln) * kMlaDl + 8 * kg;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
-  }
-  // gather: one row per instruction, lane i fills piece position i with piece
-  // i ^ swz of the token's row; absent ids give a zero row
+  uint16_t (*rows)[kMlaDl] = sh.rows[half];
   uint32_t vmask = 0;
   if (KV != kKvPagedFp8) {
+    // one row per instruction: lane i fills piece position i with piece
+    // i ^ swz of the token's row; absent ids give a zero row
     const size_t base = KV == kKvRows ? seq_base : 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -152,10 +176,9 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       if (id >= 0) {
         vmask |= 1u << i;
         const uint16_t* src = kv + (base + size_t(id)) * kMlaDl + 8 * (lane ^ mla_swz(t));
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&sh.rows[t][0]), 16, 0,
-                                         0);
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&rows[t][0]), 16, 0, 0);
       } else {
-        *reinterpret_cast<u32x4*>(&sh.rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&rows[t][8 * lane]) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   } else {
@@ -163,11 +186,11 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     // first, then widens them (hardware E4M3 decode, times the row's scale,
     // rounded to bf16) into piece position p ^ swz of the row
     const uint8_t* kv8 = static_cast<const uint8_t*>(kv_v);
-    u32x2 raw[16];
+    u32x2 codes[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int id = __builtin_amdgcn_readlane(myid, i);
-      raw[i] = id >= 0 ? *reinterpret_cast<const u32x2*>(kv8 + size_t(id) * kMlaDl + 8 * lane) : u32x2{0u, 0u};
+      codes[i] = id >= 0 ? *reinterpret_cast<const u32x2*>(kv8 + size_t(id) * kMlaDl + 8 * lane) : u32x2{0u, 0u};
       vmask |= (id >= 0 ? 1u : 0u) << i;
     }
 #pragma unroll
@@ -177,34 +200,44 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       u32x4 v;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[i][h2]), false);
-        const f32x2 c2 = __builtin_amdgcn_cvt_pk_f32_fp8(int(raw[i][h2]), true);
-        v[2 * h2] = pack2bf(a[0] * sc, a[1] * sc);
-        v[2 * h2 + 1] = pack2bf(c2[0] * sc, c2[1] * sc);
+        const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes[i][h2]), false);
+        const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes[i][h2]), true);
+        v[2 * h2] = pack2bf(a0[0] * sc, a0[1] * sc);
+        v[2 * h2 + 1] = pack2bf(a1[0] * sc, a1[1] * sc);
       }
-      *reinterpret_cast<u32x4*>(&sh.rows[t][8 * (lane ^ mla_swz(t))]) = v;
+      *reinterpret_cast<u32x4*>(&rows[t][8 * (lane ^ mla_swz(t))]) = v;
     }
+  }
+  // q_lat rows of heads 2 w8, 2 w8 + 1 into LDS, after the gather (q is needed
+  // only after the barrier; issued before the gather it delayed the gather)
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int hh = 2 * w8 + e;
+    __builtin_amdgcn_global_load_lds(q_lat + (size_t(r) * Hm + hg * 16 + hh) * kMlaDl + 8 * lane,
+                                     (__attribute__((address_space(3))) void*)(&sh.q[hh][0]), 16, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // every wave's rows are in LDS
+  __syncthreads();  // every wave's rows and the q rows are in LDS
 
-  // logits of tokens 16w + 4kg + j (j < 4) for head ln, full latent width
-  // (A = kv rows from LDS, B = q^T from registers); two accumulators shorten
-  // the MFMA dependency chain
+  // logits of tokens 16w + 4kg + j (j < 4) of this half for head ln, full
+  // latent width (A = kv rows, B = q^T fragments, both from LDS)
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   {
+    // every fragment read is issued before the first MFMA (one LDS round trip)
     const int t = 16 * w + ln, sw = mla_swz(t);
+    u32x4 fa[16], fb[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      fa[k] = *reinterpret_cast<const u32x4*>(&rows[t][((4 * k + kg) ^ sw) * 8]);
+      fb[k] = *reinterpret_cast<const u32x4*>(&sh.q[ln][(4 * k + kg) * 8]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + kg) ^ sw) * 8]));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.rows[t][((4 * k + 4 + kg) ^ sw) * 8]));
-      acc0 = mfma16x16x32(a0, as_bf16x8(qv[k]), acc0);
-      acc1 = mfma16x16x32(a1, as_bf16x8(qv[k + 1]), acc1);
+      acc0 = mfma16x16x32(as_bf16x8(fa[k]), as_bf16x8(fb[k]), acc0);
+      acc1 = mfma16x16x32(as_bf16x8(fa[k + 1]), as_bf16x8(fb[k + 1]), acc1);
     }
   }
-  // softmax within the wave: its maximum over its 16 tokens per head, P
-  // relative to that maximum; the value contraction rescales by the waves'
-  // maxima, so no barrier separates the maxima from P
   float x[4];
   float m = -INFINITY;
 #pragma unroll
@@ -223,16 +256,16 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
   }
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
-  *reinterpret_cast<u32x2*>(&sh.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+  auto& X = sh.x[half];
+  *reinterpret_cast<u32x2*>(&X.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
   if (kg == 0) {
-    sh.x.m[ln][w] = m_use;
-    sh.x.l[ln][w] = l;
+    X.m[ln][w] = m_use;
+    X.l[ln][w] = l;
   }
-  __syncthreads();  // P, the maxima and the sums published
+  __syncthreads();  // P, the maxima and the sums of both halves published
 
-  // the row's maximum M; tokens of wave v carry the factor 2^(m_v - M)
-  const f32x4 mv = *reinterpret_cast<const f32x4*>(&sh.x.m[ln][0]);
-  const f32x4 lv = *reinterpret_cast<const f32x4*>(&sh.x.l[ln][0]);
+  const f32x4 mv = *reinterpret_cast<const f32x4*>(&X.m[ln][0]);
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&X.l[ln][0]);
   float M = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 4; ++v) M = fmaxf(M, lv[v] > 0.f ? mv[v] : -INFINITY);
@@ -244,47 +277,75 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     fv[v] = lv[v] > 0.f ? __builtin_amdgcn_exp2f(mv[v] - M_use) : 0.f;
     l = fmaf(fv[v], lv[v], l);
   }
-  // O^T[dl, head] over latent quarter w: A = kv^T (16 dl x 32 tokens) from two
-  // transposing reads, B = P^T (32 tokens x 16 heads); the 8 tokens of lane
-  // group kg in k-step ks belong to wave 2ks + kg/2
   bf16x8 pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.x.p[ln][32 * ks + 8 * kg]);
+    const u32x4 rw = *reinterpret_cast<const u32x4*>(&X.p[ln][32 * ks + 8 * kg]);
     const float f = fv[2 * ks + (kg >> 1)];
-    u32x4 sc;
+    u32x4 scv;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      sc[e] = pack2bf(__uint_as_float(raw[e] << 16) * f, __uint_as_float(raw[e] & 0xffff0000u) * f);
-    pb[ks] = as_bf16x8(sc);
+      scv[e] = pack2bf(__uint_as_float(rw[e] << 16) * f, __uint_as_float(rw[e] & 0xffff0000u) * f);
+    pb[ks] = as_bf16x8(scv);
   }
   f32x4 o[8];
+  {
+    // every transposing read is issued before the first MFMA
+    u32x2 tl[8][2], th[8][2];
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-    const int col = 128 * w + 16 * blk + 4 * (ln & 3);
-    const int pc = col >> 3, off = col & 7;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < 8; ++blk) {
+      const int col = 128 * w + 16 * blk + 4 * (ln & 3);
+      const int pc = col >> 3, off = col & 7;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
-      const u32x2 lo = lds_read_tr16(&sh.rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
-      const u32x2 hi = lds_read_tr16(&sh.rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
-      a = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], a);
+      for (int ks = 0; ks < 2; ++ks) {
+        const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
+        tl[blk][ks] = lds_read_tr16(&rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
+        th[blk][ks] = lds_read_tr16(&rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
+      }
     }
-    o[blk] = a;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        a = mfma16x16x32(as_bf16x8(u32x4{tl[blk][ks][0], tl[blk][ks][1], th[blk][ks][0], th[blk][ks][1]}), pb[ks], a);
+      o[blk] = a;
+    }
   }
-  const float m_use_row = M_use;
-
-  // o[blk][j] = sum_t p_t kv[t][dl = 128 w + 16 blk + 4 kg + j] for head h
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const float lse_v = l > 0.f ? (m_use_row + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+  // merge the halves: half 1 parks its unnormalised O (relative to its row
+  // maximum), maximum and sum in LDS (its row buffer is free once every wave
+  // is past the values), half 0 rescales both to the common maximum
+  const float Mh = l > 0.f ? M_use : -INFINITY;
+  __syncthreads();  // every wave is done reading the rows
+  f32x4* park = reinterpret_cast<f32x4*>(&sh.rows[1][0][0]) + (w * 8) * 64 + lane;
+  if (half == 1) {
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) park[blk * 64] = o[blk];
+    if (w == 0 && kg == 0) {
+      sh.mh[ln] = Mh;
+      sh.lh[ln] = l;
+    }
+  }
+  __syncthreads();
+  if (half == 1) return;
+  const float M1 = sh.mh[ln], l1 = sh.lh[ln];
+  const float Mt = fmaxf(Mh, M1);
+  const float Mt_use = Mt == -INFINITY ? 0.f : Mt;
+  const float f0 = l > 0.f ? __builtin_amdgcn_exp2f(M_use - Mt_use) : 0.f;
+  const float f1 = l1 > 0.f ? __builtin_amdgcn_exp2f(M1 - Mt_use) : 0.f;
+  const float lt = fmaf(l, f0, l1 * f1);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (Mt_use + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f : -INFINITY;
+  const float g0 = f0 * inv, g1 = f1 * inv;
   if (nsplit == 1) {
     uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + w * 128 + 4 * kg;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
+      const f32x4 o1 = park[blk * 64];
       u32x2 pkd;
-      pkd[0] = pack2bf(o[blk][0] * inv, o[blk][1] * inv);
-      pkd[1] = pack2bf(o[blk][2] * inv, o[blk][3] * inv);
+      pkd[0] = pack2bf(o[blk][0] * g0 + o1[0] * g1, o[blk][1] * g0 + o1[1] * g1);
+      pkd[1] = pack2bf(o[blk][2] * g0 + o1[2] * g1, o[blk][3] * g0 + o1[3] * g1);
       *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
     }
     if (w == 0 && kg == 0 && lse) lse[size_t(r) * Hm + h] = lse_v;
@@ -292,9 +353,10 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     const size_t rs = size_t(r) * nsplit + sp;
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
+      const f32x4 o1 = park[blk * 64];
       u32x2 pkd;
-      pkd[0] = pack2bf(o[blk][0] * inv, o[blk][1] * inv);
-      pkd[1] = pack2bf(o[blk][2] * inv, o[blk][3] * inv);
+      pkd[0] = pack2bf(o[blk][0] * g0 + o1[0] * g1, o[blk][1] * g0 + o1[1] * g1);
+      pkd[1] = pack2bf(o[blk][2] * g0 + o1[2] * g1, o[blk][3] * g0 + o1[3] * g1);
       __builtin_nontemporal_store(pkd, reinterpret_cast<u32x2*>(part_o + part_off(rs, HG, hg, w, blk, lane)));
     }
     if (w == 0 && kg == 0) part_lse[rs * Hm + h] = lse_v;
@@ -695,13 +757,14 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
 
 // Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  One
 // wave per (row, head group, latent quarter, 16-channel block): lane (kg, ln)
-// owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken 32 at
-// a time; within a batch every lane issues all its loads (the split weights
-// of its head and its slice of every split's partial: one contiguous 512-byte
-// block per split and wave) before using any, and batches are merged with a
-// running maximum.
+// owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken
+// kCombineBatch at a time (16 or 32: the smaller one when it covers the row's
+// splits, so that no load is spent on clamped duplicates); within a batch
+// every lane issues all its loads (the split weights of its head and its
+// slice of every split's partial: one contiguous 512-byte block per split and
+// wave) before using any, and batches are merged with a running maximum.
 constexpr int kMaxSplit = 256;
-constexpr int kCombineBatch = 32;
+template <int kCombineBatch>
 __global__ __launch_bounds__(64) void mla_combine(const uint16_t* __restrict__ part_o,
                                                   const float* __restrict__ part_lse, int nsplit,
                                                   int Hm, uint16_t* __restrict__ out,
@@ -816,22 +879,33 @@ __global__ __launch_bounds__(256) void mla_decode_generic(
 struct MlaPlan {
   bool mfma;
   bool rows;   // many rows: one workgroup per (row, head group) over all ids
-  int nsplit;  // id slices of kMlaSplit per row
+  int nsplit;  // id slices of kMla2Ids per row
   int ns8;     // nsplit rounded up to a multiple of 8 (XCD spacing)
 };
+
+static int mla_slices(int W) { return (W + kMla2Ids - 1) / kMla2Ids; }
 
 static MlaPlan mla_plan(int Q, int Hm, int Dl, int W, int dtype) {
   MlaPlan pl{false, false, 1, 1};
   if (!(dtype == DSA_BF16 && Dl == kMlaDl && Hm % 16 == 0 && Hm <= 128)) return pl;
   pl.mfma = true;
-  pl.nsplit = (W + kMlaSplit - 1) / kMlaSplit;
-  pl.ns8 = (pl.nsplit + 7) / 8 * 8;
-  if (pl.nsplit > 1 && long(Q) * (Hm / 16) >= kMlaRowsMinWgs) {
+  if (W > kMlaSplit && long(Q) * (Hm / 16) >= kMlaRowsMinWgs) {
     pl.rows = true;
-    pl.nsplit = 1;
-    pl.ns8 = 1;
+    return pl;
   }
+  pl.nsplit = mla_slices(W);
+  pl.ns8 = (pl.nsplit + 7) / 8 * 8;
   return pl;
+}
+
+// the combine of nsplit partials per row
+static void launch_combine(int nsplit, int Q, int Hm, const uint16_t* part_o, const float* part_lse, void* out,
+                           float* lse, hipStream_t s) {
+  const dim3 grid((Hm / 16) * 32, Q);
+  if (nsplit <= 16)
+    hipLaunchKernelGGL(mla_combine<16>, grid, dim3(64), 0, s, part_o, part_lse, nsplit, Hm, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(mla_combine<32>, grid, dim3(64), 0, s, part_o, part_lse, nsplit, Hm, (uint16_t*)out, lse);
 }
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -900,13 +974,12 @@ static int mla_launch(const void* q_lat, const void* kv, const int32_t* row_seq,
                                         align256(size_t(Q) * pl.nsplit * Hm * Dl * sizeof(uint16_t)));
   }
   dim3 grid((Hm / 16) * pl.ns8, Q);
-  hipLaunchKernelGGL(mla_decode_mfma<kKvRows>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat, kv,
+  hipLaunchKernelGGL(mla_decode_mfma<kKvRows>, grid, dim3(kMla2Threads), 0, s, (const uint16_t*)q_lat, kv,
                      KvPages{nullptr, nullptr, 0, 1, 0}, row_seq, token_ids, Hm, B, T_max, W, pl.nsplit, pl.ns8,
                      scale_log2, (uint16_t*)out, lse, part_o, part_lse);
   int st = launch_status();
   if (st || pl.nsplit == 1) return st;
-  hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, pl.nsplit,
-                     Hm, (uint16_t*)out, lse);
+  launch_combine(pl.nsplit, Q, Hm, part_o, part_lse, out, lse, s);
   return launch_status();
 }
 
@@ -975,7 +1048,7 @@ extern "C" int dsa_sparse_mla_decode_noalloc(const void* q_lat, const void* kv, 
 
 extern "C" size_t dsa_sparse_mla_paged_workspace_bytes(int Q, int Hm, int Dl, int W) {
   if (Q <= 0 || Hm <= 0 || Dl <= 0 || W <= 0) return 0;
-  const int nsplit = (W + kMlaSplit - 1) / kMlaSplit;
+  const int nsplit = mla_slices(W);
   if (nsplit == 1) return 0;
   return align256(size_t(Q) * nsplit * Hm * Dl * sizeof(uint16_t)) + align256(size_t(Q) * nsplit * Hm * sizeof(float));
 }
@@ -995,7 +1068,7 @@ extern "C" int dsa_sparse_mla_decode_paged(const void* q_lat, const void* kv_pag
   if (long(W) > long(kMlaSplit) * kMaxSplit) return DSA_ERR_UNSUPPORTED;
   if (long(num_pages) * page_size > 2147483647L || long(max_pages) * page_size > 2147483647L)
     return DSA_ERR_UNSUPPORTED;
-  const int nsplit = (W + kMlaSplit - 1) / kMlaSplit;
+  const int nsplit = mla_slices(W);
   const int ns8 = (nsplit + 7) / 8 * 8;
   const size_t need = dsa_sparse_mla_paged_workspace_bytes(Q, Hm, Dl, W);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
@@ -1012,16 +1085,15 @@ extern "C" int dsa_sparse_mla_decode_paged(const void* q_lat, const void* kv_pag
   const int T_logical = max_pages * page_size;
   dim3 grid((Hm / 16) * ns8, Q);
   if (kv_dtype == DSA_BF16)
-    hipLaunchKernelGGL(mla_decode_mfma<kKvPaged>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat, kv_pages,
+    hipLaunchKernelGGL(mla_decode_mfma<kKvPaged>, grid, dim3(kMla2Threads), 0, s, (const uint16_t*)q_lat, kv_pages,
                        pg, row_seq, token_ids, Hm, B, T_logical, W, nsplit, ns8, scale_log2, (uint16_t*)out, lse,
                        part_o, part_lse);
   else
-    hipLaunchKernelGGL(mla_decode_mfma<kKvPagedFp8>, grid, dim3(kMlaThreads), 0, s, (const uint16_t*)q_lat,
+    hipLaunchKernelGGL(mla_decode_mfma<kKvPagedFp8>, grid, dim3(kMla2Threads), 0, s, (const uint16_t*)q_lat,
                        kv_pages, pg, row_seq, token_ids, Hm, B, T_logical, W, nsplit, ns8, scale_log2,
                        (uint16_t*)out, lse, part_o, part_lse);
   int st = launch_status();
   if (st || nsplit == 1) return st;
-  hipLaunchKernelGGL(mla_combine, dim3((Hm / 16) * 32, Q), dim3(64), 0, s, part_o, part_lse, nsplit, Hm,
-                     (uint16_t*)out, lse);
+  launch_combine(nsplit, Q, Hm, part_o, part_lse, out, lse, s);
   return launch_status();
 }

@@ -174,7 +174,7 @@ def test_mla_refuses_bad_arguments_and_sizes_workspace(lib):
 
 def _paged(lib, **kw):
     a = dict(q=FAKE, kv=FAKE, scale=FAKE, bt=FAKE, max_pages=4, page_size=64, num_pages=8, row_seq=FAKE,
-             tok=FAKE, Q=2, Hm=64, Dl=512, B=2, W=128, sm=0.04, dtype=2, out=FAKE, lse=None, ws=FAKE,
+             tok=FAKE, Q=2, Hm=64, Dl=512, B=2, W=256, sm=0.04, dtype=2, out=FAKE, lse=None, ws=FAKE,
              ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return lib.dsa_sparse_mla_decode_paged(*a.values())
@@ -191,8 +191,8 @@ def test_paged_mla_refuses_bad_arguments_and_sizes_workspace(lib):
     assert _paged(lib, Hm=24) == DSA_ERR_UNSUPPORTED
     assert _paged(lib, ws=None) == DSA_ERR_WORKSPACE
     assert _paged(lib, ws_bytes=16) == DSA_ERR_WORKSPACE
-    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 128) > 0
-    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 64) == 0   # one id slice
+    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 256) > 0
+    assert lib.dsa_sparse_mla_paged_workspace_bytes(2, 64, 512, 128) == 0   # one id slice of 128
     # the paged entry splits the ids for any row count (no many-rows path)
     assert lib.dsa_sparse_mla_paged_workspace_bytes(4096, 64, 512, 2048) > 0
 
