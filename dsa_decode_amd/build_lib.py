@@ -11,11 +11,17 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 arithmetic on the device
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-Wno-pass-failed",
 ]
+
+# Per-source extra flags (none at present; the mechanism stays for kernels
+# that need their own code-generation options).
+SOURCE_FLAGS: dict[str, list[str]] = {}
+
+BUILD_DIR = os.path.join(PKG, "_build")
 
 
 PROBE_SRC = os.path.join(PKG, "probe", "read_stream.hip")
@@ -34,19 +40,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def _hipcc(srcs: list[str], lib: str, verbose: bool) -> None:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = lib + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *srcs, "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> subprocess.Popen:
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = [l for l in r.stderr.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l]
-    if r.returncode != 0:
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _check(proc: subprocess.Popen, verbose: bool) -> None:
+    out, err = proc.communicate()
+    errs = [l for l in err.splitlines() if "packed-fp32-ops' is not a recognized feature" not in l]
+    if proc.returncode != 0:
         sys.stderr.write("\n".join(errs) + "\n")
-        raise RuntimeError(f"hipcc failed ({r.returncode})")
+        raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(proc.args)}")
     if verbose and errs:
         sys.stderr.write("\n".join(errs) + "\n")
+
+
+def _hipcc(srcs: list[str], lib: str, verbose: bool) -> None:
+    """Compile each source to an object (in parallel, with its own flags),
+    then link the shared library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    stem = os.path.splitext(os.path.basename(lib))[0]
+    objs, procs = [], []
+    for src in srcs:
+        obj = os.path.join(BUILD_DIR, f"{stem}.{os.path.splitext(os.path.basename(src))[0]}.o")
+        extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+        procs.append(_run([hipcc, *HIPCC_FLAGS, *extra, "-c", src, "-o", obj], verbose))
+        objs.append(obj)
+    for proc in procs:
+        _check(proc, verbose)
+    tmp = lib + ".tmp"
+    _check(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose), verbose)
     os.replace(tmp, lib)
 
 

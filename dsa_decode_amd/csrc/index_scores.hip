@@ -24,8 +24,10 @@
 //
 // Decode kernel: one row per grid row, pools split over grid.x, each wave
 // streaming its tiles through a register ring.  Prefill kernel: a workgroup
-// keeps its pool tiles in registers and runs a group of rows of one sequence
-// over them (rows staged four at a time in LDS).
+// holds 8 rows' operands in registers and streams a range of tiles through
+// LDS.  Both use the same operand layout, statistics, accumulation order and
+// epilogue, so a row's scores are bit-identical whichever kernel computes
+// them.
 //
 // Per pool the decode kernel reads 256 B of key + 1 B valid and writes 4 B of
 // score (the pool's start follows from the sequence's first start): it is
@@ -163,20 +165,20 @@ __device__ __forceinline__ TileAcc<NH> tile_mfma(const u32x4 (&x)[4], const bf16
   return t;
 }
 
-// The folded head dots of a tile alone (its statistics formed elsewhere).
+// The folded head dots of a tile with the head blocks' products interleaved
+// (per accumulator the order is that of tile_mfma: hi, then lo, per k-step).
 template <int NH>
-__device__ __forceinline__ void head_mfma(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
-                                          const bf16x8 (&alo)[NH][4], f32x4 (&acc)[NH]) {
+__device__ __forceinline__ void head_mfma_i(const u32x4 (&x)[4], const bf16x8 (&ahi)[NH][4],
+                                            const bf16x8 (&alo)[NH][4], f32x4 (&acc)[NH]) {
 #pragma unroll
   for (int mb = 0; mb < NH; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const bf16x8 bx = as_bf16x8(x[i]);
 #pragma unroll
-    for (int mb = 0; mb < NH; ++mb) {
-      acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
-      acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
-    }
+    for (int mb = 0; mb < NH; ++mb) acc[mb] = mfma16x16x32(ahi[mb][i], bx, acc[mb]);
+#pragma unroll
+    for (int mb = 0; mb < NH; ++mb) acc[mb] = mfma16x16x32(alo[mb][i], bx, acc[mb]);
   }
 }
 
@@ -381,144 +383,204 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-// Prefill kernel.  A workgroup of WPB waves keeps WPB x 64 pools' keys in registers (wave w:
-// 4 tiles) and runs a group of rows of one sequence over them, staging the
-// folded operands of RPB rows at a time in LDS.  The LayerNorm statistics of
-// a pool do not depend on the row, so they are formed once per tile when the
-// keys are loaded; each (row, tile) then costs the 16 head MFMAs and a short
-// epilogue, the MFMAs of tile t+1 issued before the epilogue of tile t.  After
-// the lane-group sum every lane holds a tile's scores: lane (kg, ln) keeps
-// tile kg's, so a row's 64 pools per wave go out in one 256-byte store.
-template <int NH, int RPB, int KT, int WPB>
-__global__ __launch_bounds__(WPB * 64) void index_scores_rows(
+// Many rows, GEMM-shaped (prefill chunks).  A workgroup of 8 waves takes 8
+// rows (one per wave) and a range of pool tiles.  The rows' folded operands
+// are staged once (the decode kernel's staging arithmetic, through LDS) and
+// then held in each wave's registers for the whole range; the workgroup
+// streams the range's key tiles through two LDS buffers, 16 tiles per stage
+// (two loaded by each wave, which also forms those tiles' LayerNorm
+// statistics, so every tile's statistics are formed once per workgroup),
+// one barrier per stage: while a stage is computed, the next stage's tiles
+// are in flight.  Each (row, tile) costs 16 MFMAs (hi/lo x head blocks x 4
+// k-steps) and a short epilogue, the MFMAs of tile j+1 issued before the
+// epilogue of tile j; lane (kg, ln) keeps tiles kg + 4u of a stage, so a
+// stage's 256 scores of a row go out in four 256-byte stores.  Rows of
+// several sequences in one workgroup take one pass per sequence.  (Measured
+// on the 4096-row chunk: 1.72 ms; four waves with two rows each, and the
+// 32x32x16 MFMA shape over pairs of tiles, were both slower.)
+constexpr int kGemmWaves = 8;
+constexpr int kGemmStage = 16;  // tiles per stage (two per wave)
+
+template <int NH>
+__global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
     const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int rows_per_group,
+    const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int tiles_per_wg,
     float* __restrict__ scores) {
   constexpr int H = NH * 16;
-  constexpr int kTiles = KT;  // tiles per wave: 4 or 8 (lane group kg stores tiles kg, kg + 4)
-  constexpr int NS = KT / 4;  // score stores per row and lane
-  static_assert(KT == 4 || KT == 8, "tiles per wave");
-  __shared__ uint16_t ghi[RPB][H][kIsLd];
-  __shared__ uint16_t glo[RPB][H][kIsLd];
-  __shared__ float sQB[RPB][H], sW[RPB][H];
-  __shared__ int s_pos[RPB], s_seq[RPB];
+  constexpr size_t kStageBytes = 8 * H * kIsLd * 2 * 2 + 8 * H * 4 * 2;  // ghi + glo + QB + W of 8 rows
+  constexpr size_t kKeyBytes = 2 * kGemmStage * kTileElems * 2;          // two stages of key tiles
+  constexpr size_t kLds = kStageBytes > kKeyBytes ? kStageBytes : kKeyBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
+  __shared__ float srs[2][kGemmStage * 16];  // scale / sigma per pool of a stage
+  __shared__ int sseq[kGemmWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
   const int diag_addr = 4 * (16 * (ln >> 2) + ln);
-  const int r_begin = blockIdx.y * rows_per_group;
-  const int r_end = min(Q, r_begin + rows_per_group);
-  const int p_wave = blockIdx.x * (WPB * kTiles * 16) + wave * (kTiles * 16);
-  // the pools whose scores this lane stores: tile kg + 4 u, pool ln
-  int p_mine[NS];
-#pragma unroll
-  for (int u = 0; u < NS; ++u) p_mine[u] = p_wave + 64 * u + lane;
-
-  // keys of this wave's tiles for the sequence of the group's first row, and
-  // 1/sigma of their pools; a row of another sequence reloads them (correct,
-  // slower)
-  int b_loaded = row_seq[r_begin];
-  u32x4 xk[kTiles][4];
-  float rsig[kTiles];
-  int ps_mine[NS], pv_mine[NS];
+  const int r0 = blockIdx.y * kGemmWaves;
+  const int r = r0 + wave;
+  const bool rok = r < Q;
+  const int b_row = rok ? row_seq[r] : -1;
+  const bool ok = rok && b_row >= 0 && b_row < B;
+  const int pos = rok ? row_pos[r] : 0;
   const int P_tiles = pool_tiles(P_max);
-  auto load_keys = [&](int b) {
-    const bool bok = b >= 0 && b < B;
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const int tile = (p_wave >> 4) + t;
-      const size_t ti = (bok && tile < P_tiles) ? size_t(b) * P_tiles + tile : 0;
-      const uint16_t* src = k_pool + ti * (16 * kIsD) + 8 * lane;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xk[t][i] = *reinterpret_cast<const u32x4*>(src + 512 * i);
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const size_t pi = (bok && p_mine[u] < P_max) ? size_t(b) * P_max + p_mine[u] : 0;
-      ps_mine[u] = pool_start[pi];
-      pv_mine[u] = pool_valid[pi];
-    }
-    const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, gacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 bx = as_bf16x8(xk[t][i]);
-        sacc = mfma16x16x32(ones, bx, sacc);
-        gacc = mfma16x16x32(bx, bx, gacc);
-      }
-      const int jd = ln & 3;
-      float dg = gacc[0];
-      dg = jd == 1 ? gacc[1] : dg;
-      dg = jd == 2 ? gacc[2] : dg;
-      dg = jd == 3 ? gacc[3] : dg;
-      const float sumsq = __int_as_float(__builtin_amdgcn_ds_bpermute(diag_addr, __float_as_int(dg)));
-      const float mu = sacc[0] * (1.0f / kIsD);
-      const float var = fmaxf(sumsq * (1.0f / kIsD) - mu * mu, 0.f);
-      rsig[t] = scale * __builtin_amdgcn_rsqf(var + eps);
-    }
-  };
-  load_keys(b_loaded);
+  const int tb = blockIdx.x * tiles_per_wg;
+  const int te = min(P_tiles, tb + tiles_per_wg);
+  const int nstage = te > tb ? (te - tb + kGemmStage - 1) / kGemmStage : 0;
 
-  for (int rb = r_begin; rb < r_end; rb += RPB) {
-    const int nr = min(RPB, r_end - rb);
-    __syncthreads();  // the previous batch's LDS reads are finished
-    for (int u = tid; u < nr * H * 8; u += WPB * 64) {
+  // 1. the 8 rows' folded operands: staged in LDS with the decode kernel's
+  // arithmetic, then each wave takes its row's fragments into registers
+  {
+    uint16_t (*ghi)[H][kIsLd] = reinterpret_cast<uint16_t (*)[H][kIsLd]>(lds);
+    uint16_t (*glo)[H][kIsLd] = reinterpret_cast<uint16_t (*)[H][kIsLd]>(lds + 8 * H * kIsLd * 2);
+    float (*sQB)[H] = reinterpret_cast<float (*)[H]>(lds + 8 * H * kIsLd * 4);
+    float (*sW)[H] = reinterpret_cast<float (*)[H]>(lds + 8 * H * kIsLd * 4 + 8 * H * 4);
+    const int nr = min(kGemmWaves, Q - r0);
+    for (int u = tid; u < nr * H * 8; u += kGemmWaves * 64) {
       const int rr = u / (H * 8);
-      const RowIn rin = stage_row_load(q + size_t(rb + rr) * H * kIsD, w + size_t(rb + rr) * H, gamma, beta,
+      const RowIn rin = stage_row_load(q + size_t(r0 + rr) * H * kIsD, w + size_t(r0 + rr) * H, gamma, beta,
                                        u - rr * H * 8);
       stage_row_store(rin, ghi[rr], glo[rr], sQB[rr], sW[rr], u - rr * H * 8);
     }
-    if (tid < nr) {
-      s_pos[tid] = row_pos[rb + tid];
-      s_seq[tid] = row_seq[rb + tid];
-    }
+    if (lane == 0) sseq[wave] = ok ? b_row : -1;
     __syncthreads();
-    for (int rr = 0; rr < nr; ++rr) {
-      const int r = rb + rr;
-      const int b = s_seq[rr];
-      const int pos = s_pos[rr];
-      const bool ok = b >= 0 && b < B;
-      if (ok && b != b_loaded) {
-        b_loaded = b;
-        load_keys(b);
+  }
+  bf16x8 ahi[NH][4], alo[NH][4];
+  float cQ[NH][4], cW[NH][4];
+  if (rok) {
+    uint16_t (*ghi)[H][kIsLd] = reinterpret_cast<uint16_t (*)[H][kIsLd]>(lds);
+    uint16_t (*glo)[H][kIsLd] = reinterpret_cast<uint16_t (*)[H][kIsLd]>(lds + 8 * H * kIsLd * 2);
+    float (*sQB)[H] = reinterpret_cast<float (*)[H]>(lds + 8 * H * kIsLd * 4);
+    float (*sW)[H] = reinterpret_cast<float (*)[H]>(lds + 8 * H * kIsLd * 4 + 8 * H * 4);
+    load_operands<NH>(ghi[wave], glo[wave], sQB[wave], sW[wave], kg, ln, scale, ahi, alo, cQ, cW);
+  }
+  __syncthreads();  // the staging area is reused for the key tiles
+  uint16_t (*skeys)[kGemmStage][kTileElems] = reinterpret_cast<uint16_t (*)[kGemmStage][kTileElems]>(lds);
+  const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+
+  for (int i8 = 0; i8 < kGemmWaves; ++i8) {
+    const int b = sseq[i8];
+    bool first = b >= 0;
+    for (int j = 0; j < i8; ++j) first = first && sseq[j] != b;
+    if (!first) continue;  // uniform: every wave reads the same LDS words
+    const bool mine = ok && b_row == b;
+    const uint16_t* kseq = k_pool + size_t(b) * P_tiles * kTileElems;
+    const int start0 = pool_start[size_t(b) * P_max];
+    const long last_ok = long(pos) - (kp - 1) - start0;
+    float* srow = scores + size_t(r) * P_max;
+    // this wave's tile of stage s: keys into registers (and the validity of
+    // the pools this lane stores in stage s)
+    constexpr int TW = kGemmStage / kGemmWaves;  // tiles per wave and stage
+    constexpr int NU = kGemmStage / 4;           // scores per lane and stage
+    u32x4 xk[TW][4];
+    uint8_t vl[NU];
+    auto fetch = [&](int s) {
+#pragma unroll
+      for (int e = 0; e < TW; ++e) {
+        const int t = tb + kGemmStage * s + TW * wave + e;
+        const uint16_t* src = kseq + size_t(t < te ? t : tb) * kTileElems + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xk[e][i] = *reinterpret_cast<const u32x4*>(src + 512 * i);
       }
-      bf16x8 ahi[NH][4], alo[NH][4];
-      float cQ[NH][4], cW[NH][4];
-      load_operands<NH>(ghi[rr], glo[rr], sQB[rr], sW[rr], kg, ln, scale, ahi, alo, cQ, cW);
-      float mine[NS];
 #pragma unroll
-      for (int u = 0; u < NS; ++u) mine[u] = 0.f;
-      f32x4 cur[NH];
-      head_mfma<NH>(xk[0], ahi, alo, cur);
+      for (int u = 0; u < NU; ++u) {
+        const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+        vl[u] = pool_valid[size_t(b) * P_max + (p < P_max ? p : 0)];
+      }
+    };
+    // publish this wave's tile of stage s: keys to LDS, scale/sigma of its pools
+    auto publish = [&](int s) {
+      const int buf = s & 1;
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        f32x4 nxt[NH];
-        if (t + 1 < kTiles) head_mfma<NH>(xk[t + 1], ahi, alo, nxt);
-        float part = 0.f;
+      for (int e = 0; e < TW; ++e) {
 #pragma unroll
-        for (int mb = 0; mb < NH; ++mb)
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4*>(&skeys[buf][TW * wave + e][8 * lane + 512 * i]) = xk[e][i];
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) part = fmaf(cW[mb][j], fmaxf(0.f, fmaf(rsig[t], cur[mb][j], cQ[mb][j])), part);
-        const float sc = sum_lane_groups(part);
-        mine[t >> 2] = kg == (t & 3) ? sc : mine[t >> 2];
-        if (t + 1 < kTiles) {
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 bx = as_bf16x8(xk[e][i]);
+          sacc = mfma16x16x32(ones, bx, sacc);
+          gacc = mfma16x16x32(bx, bx, gacc);
+        }
+        const int jd = ln & 3;
+        float dg = gacc[0];
+        dg = jd == 1 ? gacc[1] : dg;
+        dg = jd == 2 ? gacc[2] : dg;
+        dg = jd == 3 ? gacc[3] : dg;
+        const float sumsq = __int_as_float(__builtin_amdgcn_ds_bpermute(diag_addr, __float_as_int(dg)));
+        const float mu = sacc[0] * (1.0f / kIsD);
+        const float var = fmaxf(sumsq * (1.0f / kIsD) - mu * mu, 0.f);
+        if (kg == 0) srs[buf][(TW * wave + e) * 16 + ln] = scale * __builtin_amdgcn_rsqf(var + eps);
+      }
+    };
+    uint8_t vcur[NU];
+    fetch(0);
 #pragma unroll
-          for (int mb = 0; mb < NH; ++mb) cur[mb] = nxt[mb];
+    for (int u = 0; u < NU; ++u) vcur[u] = vl[u];
+    publish(0);
+    __syncthreads();
+    for (int s = 0; s < nstage; ++s) {
+      const int buf = s & 1;
+      if (s + 1 < nstage) fetch(s + 1);  // in flight while stage s is computed
+      if (mine) {
+        float mine_sc[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) mine_sc[u] = 0.f;
+        // software pipeline: tile j+1's MFMAs are issued before tile j's
+        // epilogue; the fragments of tile j+2 are read meanwhile
+        u32x4 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const u32x4*>(&skeys[buf][0][8 * lane + 512 * i]);
+        f32x4 cur[NH];
+        head_mfma_i<NH>(x, ahi, alo, cur);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const u32x4*>(&skeys[buf][1][8 * lane + 512 * i]);
+#pragma unroll
+        for (int j = 0; j < kGemmStage; ++j) {
+          f32x4 nxt[NH];
+          if (j + 1 < kGemmStage) {
+            head_mfma_i<NH>(x, ahi, alo, nxt);
+            if (j + 2 < kGemmStage) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                x[i] = *reinterpret_cast<const u32x4*>(&skeys[buf][j + 2][8 * lane + 512 * i]);
+            }
+          }
+          const float rs = srs[buf][j * 16 + ln];
+          float part = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < NH; ++mb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) part = fmaf(cW[mb][jj], fmaxf(0.f, fmaf(rs, cur[mb][jj], cQ[mb][jj])), part);
+          const float sc = sum_lane_groups(part);
+          mine_sc[j >> 2] = kg == (j & 3) ? sc : mine_sc[j >> 2];
+          if (j + 1 < kGemmStage) {
+#pragma unroll
+            for (int mb = 0; mb < NH; ++mb) cur[mb] = nxt[mb];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+          if (p < P_max) srow[p] = (vcur[u] != 0 && long(p) * kp <= last_ok) ? mine_sc[u] : -INFINITY;
         }
       }
+      if (s + 1 < nstage) {
+        publish(s + 1);
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        if (p_mine[u] < P_max) {
-          const bool cand = ok && pv_mine[u] != 0 && ps_mine[u] + kp - 1 <= pos;
-          scores[size_t(r) * P_max + p_mine[u]] = cand ? mine[u] : -INFINITY;
-        }
+        for (int u = 0; u < NU; ++u) vcur[u] = vl[u];
       }
+      __syncthreads();
     }
+  }
+  // rows naming no sequence: -inf throughout
+  if (rok && !ok) {
+    for (int t = tb; t < te; ++t)
+      if (t * 16 + ln < P_max && kg == 0) scores[size_t(r) * P_max + t * 16 + ln] = -INFINITY;
   }
 }
 
@@ -588,45 +650,16 @@ __global__ __launch_bounds__(256) void index_scores_generic(
   *out = s;
 }
 
-// Launch shapes of the MFMA path.
-// prefill kernel: waves per workgroup (8: 512 pools per workgroup, so each row's
-// folded operands are staged by half as many workgroups as with 4 waves; 2.84
-// -> 2.44 ms on the prefill chunk; 207 registers leave room for one such
-// workgroup per CU)
-constexpr int kRowsWaves = 8;
-// prefill kernel: rows whose folded operands are staged in LDS per batch (8:
-// 139 KiB of LDS, still one workgroup per CU, half the barriers per row of 4;
-// 2.44 -> 2.35 ms on the prefill chunk)
-constexpr int kRowsBatch = 8;
-constexpr int kRowsTiles = 4;  // prefill kernel: key tiles per wave (256 pools per workgroup; 8 needs 316 registers, one wave per SIMD, and measured 10 % slower)
-// Decode launch shape (tuned on MI355X at 4 x 65536 pools)
-struct IsPlan {
-  bool rows;  // false: decode kernel (one row per grid row)
-  int tw;     // decode: tiles per wave
-  int rows_per_group;
-};
-
-static IsPlan is_plan(int Q, int P_max) {
-  IsPlan pl{false, 8, 1};
+// Decode launch shape: tiles per wave (tuned on MI355X at 4 x 65536 pools: 8
+// tiles per wave, 512 pools per workgroup and two workgroups per CU, while
+// that still gives >= 256 workgroups, then 4, then 1; 8 tiles per wave beat
+// 4 (1024 workgroups), and a 2-deep ring with interleaved tile pairs beat a
+// 4-deep ring).
+static int stream_tiles(int Q, int P_max) {
   const long ntile = (P_max + 15) / 16;
-  if (Q <= 64) {
-    // decode: 8 tiles per wave (512 pools per workgroup, two workgroups per
-    // CU) while that gives >= 256 workgroups, else 4 tiles, else 1.  Measured
-    // at 4 x 65536 pools: 8 tiles per wave beat 4 (1024 workgroups), and a
-    // 2-deep ring with interleaved tile pairs beat a 4-deep ring
-    if (long(Q) * ((ntile + 31) / 32) >= 256) pl.tw = 8;
-    else if (long(Q) * ((ntile + 15) / 16) >= 128) pl.tw = 4;
-    else pl.tw = 1;
-    return pl;
-  }
-  // many rows: groups of rows of one sequence share the keys held in registers
-  pl.rows = true;
-  const long chunks = (P_max + kRowsWaves * kRowsTiles * 16 - 1) / (kRowsWaves * kRowsTiles * 16);
-  int groups = int((2048 + chunks - 1) / chunks);
-  if (groups < 1) groups = 1;
-  const int per = (Q + groups - 1) / groups;
-  pl.rows_per_group = per > 16 ? per : 16;
-  return pl;
+  if (long(Q) * ((ntile + 31) / 32) >= 256) return 8;
+  if (long(Q) * ((ntile + 15) / 16) >= 128) return 4;
+  return 1;
 }
 
 }  // namespace dsa
@@ -646,38 +679,48 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
   if (kpool > DSA_MAX_KPOOL) return DSA_ERR_UNSUPPORTED;
   if (H > 64 || (D != 32 && D != 64 && D != 128)) return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
-  if (Q > 65535 * 16) return DSA_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
   if (dtype == DSA_BF16 && D == 128 && (H == 16 || H == 32)) {
-    const IsPlan pl = is_plan(Q, P_max);
-    if (!pl.rows) {
-      dim3 grid(ceil_div(P_max, kIsWaves * pl.tw * 16), Q);
+    if (Q <= 64) {
+      // decode kernel: one row per grid row
+      const int tw = stream_tiles(Q, P_max);
+      dim3 grid(ceil_div(P_max, kIsWaves * tw * 16), Q);
 #define DSA_IS_STREAM(NH, NT)                                                                       \
   hipLaunchKernelGGL((index_scores_stream<NH, NT>), grid, dim3(kIsThreads), 0, s, (const uint16_t*)q, w, \
                      scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps,   \
                      row_seq, row_pos, B, P_max, kpool, scores)
       if (H == 32) {
-        if (pl.tw == 8) DSA_IS_STREAM(2, 8);
-        else if (pl.tw == 4) DSA_IS_STREAM(2, 4);
+        if (tw == 8) DSA_IS_STREAM(2, 8);
+        else if (tw == 4) DSA_IS_STREAM(2, 4);
         else DSA_IS_STREAM(2, 1);
       } else {
-        if (pl.tw == 8) DSA_IS_STREAM(1, 8);
-        else if (pl.tw == 4) DSA_IS_STREAM(1, 4);
+        if (tw == 8) DSA_IS_STREAM(1, 8);
+        else if (tw == 4) DSA_IS_STREAM(1, 4);
         else DSA_IS_STREAM(1, 1);
       }
 #undef DSA_IS_STREAM
       return launch_status();
     }
-    dim3 grid(ceil_div(P_max, kRowsWaves * kRowsTiles * 16), ceil_div(Q, pl.rows_per_group));
-    if (grid.y > 65535) return DSA_ERR_UNSUPPORTED;
-#define DSA_IS_ROWS(NH)                                                                               \
-  hipLaunchKernelGGL((index_scores_rows<NH, kRowsBatch, kRowsTiles, kRowsWaves>), grid, dim3(kRowsWaves * 64), 0, s,       \
-                     (const uint16_t*)q,                                                                  \
-                     w, scale, (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta,     \
-                     ln_eps, row_seq, row_pos, Q, B, P_max, kpool, pl.rows_per_group, scores)
-    if (H == 32) DSA_IS_ROWS(2);
-    else DSA_IS_ROWS(1);
-#undef DSA_IS_ROWS
+    // prefill kernel: 8 rows per workgroup; pool ranges (whole stages) so that
+    // the grid has about 512 workgroups, two rounds over the CUs at one
+    // workgroup per CU
+    const int batches = ceil_div(Q, kGemmWaves);
+    if (batches > 65535) return DSA_ERR_UNSUPPORTED;
+    const int ptiles = pool_tiles(P_max);
+    const int max_nx = ceil_div(ptiles, kGemmStage);
+    int nx = ceil_div(512, batches);
+    if (nx > max_nx) nx = max_nx;
+    if (nx < 1) nx = 1;
+    const int tiles_per_wg = ceil_div(ceil_div(ptiles, nx), kGemmStage) * kGemmStage;
+    nx = ceil_div(ptiles, tiles_per_wg);
+    dim3 g(nx, batches);
+#define DSA_IS_GEMM(NH)                                                                              \
+  hipLaunchKernelGGL((index_scores_gemm<NH>), g, dim3(kGemmWaves * 64), 0, s, (const uint16_t*)q, w, scale, \
+                     (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,   \
+                     row_pos, Q, B, P_max, kpool, tiles_per_wg, scores)
+    if (H == 32) DSA_IS_GEMM(2);
+    else DSA_IS_GEMM(1);
+#undef DSA_IS_GEMM
     return launch_status();
   }
   if (Q > 65535) return DSA_ERR_UNSUPPORTED;
