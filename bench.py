@@ -702,13 +702,13 @@ def bench_prefill(args) -> int:
     mla_flops = 4 * wl.Hm * wl.Dl * listed
     mla_achieved = mla_flops / (mla_us * 1e-6) / 1e12
     kernels = {
-        "index_scores_rows": {"launch_us": round(score_us, 2), "achieved": round(achieved, 1),
+        "index_scores_gemm": {"launch_us": round(score_us, 2), "achieved": round(achieved, 1),
                               "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
         "mla_rows64w8_mfma": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
                           "frac": round(mla_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": mla_flops,
                           "listed_ids": listed},
     }
-    dom = "index_scores_rows" if score_us >= mla_us else "mla_rows64w8_mfma"
+    dom = "index_scores_gemm" if score_us >= mla_us else "mla_rows64w8_mfma"
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, ip, mi, comp, k_pool, args.cpu_seconds)
     line = {
         "metric": "DSA prefill chunk (index_scores + top-k + expand + sparse MLA) chunks/s; % MFMA roofline",
