@@ -87,8 +87,9 @@ __device__ __forceinline__ size_t part_off(size_t rs, int HG, int hg, int dq, in
 // of sequence b is row b*T_max + t).  kKvPaged: bf16 pages [num_pages,
 // page_size, Dl] behind a page table [B, max_pages] (token t of sequence b is
 // row t % page_size of page block_table[b, t / page_size]).  kKvPagedFp8: the
-// same pages holding OCP FP8 E4M3 codes with one fp32 scale per row, widened
-// to bf16 (value * scale, rounded to nearest even) on the way into LDS.
+// same pages holding OCP FP8 E4M3 codes with one fp32 scale per row; the codes
+// are widened to bf16 exactly on the way into LDS, and the row's scale
+// multiplies the token's logit and its softmax weight in the value sum.
 enum KvLayout { kKvRows = 0, kKvPaged = 1, kKvPagedFp8 = 2 };
 
 struct KvPages {
@@ -183,8 +184,11 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     }
   } else {
     // fp8 rows (512 B): lane p loads the 8 codes of piece p of every row
-    // first, then widens them (hardware E4M3 decode, times the row's scale,
-    // rounded to bf16) into piece position p ^ swz of the row
+    // first, then widens them into piece position p ^ swz of the row.  An
+    // E4M3 value is exactly a bf16 value, so the widening rounds nothing (one
+    // scaled-convert instruction per two codes, scale 1); the row's scale is
+    // applied to the token's logits and to its P instead of to its 512 values
+    // (logit_j = scale_j <q, codes_j>, sum_j p_j v_j = sum_j (p_j scale_j) codes_j)
     const uint8_t* kv8 = static_cast<const uint8_t*>(kv_v);
     u32x2 codes[16];
 #pragma unroll
@@ -196,14 +200,11 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = 16 * w + i;
-      const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mysc), i));
       u32x4 v;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes[i][h2]), false);
-        const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8(int(codes[i][h2]), true);
-        v[2 * h2] = pack2bf(a0[0] * sc, a0[1] * sc);
-        v[2 * h2 + 1] = pack2bf(a1[0] * sc, a1[1] * sc);
+        v[2 * h2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][h2], 1.0f, false));
+        v[2 * h2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][h2], 1.0f, true));
       }
       *reinterpret_cast<u32x4*>(&rows[t][8 * (lane ^ mla_swz(t))]) = v;
     }
@@ -238,11 +239,16 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
       acc1 = mfma16x16x32(as_bf16x8(fa[k + 1]), as_bf16x8(fb[k + 1]), acc1);
     }
   }
+  // fp8 rows: the scale of token 4 kg + j of the wave (its lane < 16 holds it)
+  float tsc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tsc[j] = KV == kKvPagedFp8 ? __shfl(mysc, 4 * kg + j, kWave) : 1.f;
   float x[4];
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    x[j] = (vmask >> (4 * kg + j)) & 1u ? (acc0[j] + acc1[j]) * scale_log2 : -INFINITY;
+    const float lg = KV == kKvPagedFp8 ? (acc0[j] + acc1[j]) * tsc[j] : acc0[j] + acc1[j];
+    x[j] = (vmask >> (4 * kg + j)) & 1u ? lg * scale_log2 : -INFINITY;
     m = fmaxf(m, x[j]);
   }
   m = fmaxf(m, __shfl_xor(m, 16, kWave));
@@ -257,6 +263,12 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
   auto& X = sh.x[half];
+  // the value operand: P, times the token's scale for fp8 rows (l stays the
+  // sum of the unscaled P)
+  if (KV == kKvPagedFp8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] *= tsc[j];
+  }
   *reinterpret_cast<u32x2*>(&X.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
   if (kg == 0) {
     X.m[ln][w] = m_use;

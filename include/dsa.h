@@ -365,9 +365,11 @@ int dsa_index_topk_pools_expand(const void* q, const float* w, float scale, cons
  * Token t of sequence b (the ids of token_ids, as in dsa_sparse_mla_decode)
  * is row t % page_size of page block_table[b, t / page_size]; a token whose
  * page index is >= max_pages or whose table entry is outside [0, num_pages)
- * counts as absent, like -1.  fp8 rows are widened to bf16 (value * scale,
- * rounded to nearest even) as they are gathered; the attention is then that of
- * dsa_sparse_mla_decode.  q_lat and out are bf16; Dl must be 512, Hm a
+ * counts as absent, like -1.  fp8 codes are widened to bf16 exactly as they
+ * are gathered (an E4M3 value is a bf16 value) and the row's scale is applied
+ * to the token's logit and to its softmax weight in the value sum, which in
+ * exact arithmetic is the attention of dsa_sparse_mla_decode over the rows
+ * decode(code) * scale.  q_lat and out are bf16; Dl must be 512, Hm a
  * multiple of 16 up to 128.  Every row runs the split-ids path, so W > 64
  * needs the workspace sized by dsa_sparse_mla_paged_workspace_bytes.  Other
  * arguments, ownership and errors as for dsa_sparse_mla_decode.
