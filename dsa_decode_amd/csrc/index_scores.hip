@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // epilogue of tile j; lane (kg, ln) keeps tiles kg + 4u of a stage, so a
 // stage's 256 scores of a row go out in four 256-byte stores.  Rows of
 // several sequences in one workgroup take one pass per sequence.  (Measured
-// on the 4096-row chunk: 1.72 ms; four waves with two rows each, and the
+// on the 4096-row chunk: 1.61 ms; four waves with two rows each, and the
 // 32x32x16 MFMA shape over pairs of tiles, were both slower.)
 constexpr int kGemmWaves = 8;
 constexpr int kGemmStage = 16;  // tiles per stage (two per wave)
@@ -541,6 +541,15 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
         for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const u32x4*>(&skeys[buf][1][8 * lane + 512 * i]);
 #pragma unroll
         for (int j = 0; j < kGemmStage; ++j) {
+          // the two waves of a SIMD share its matrix core; the older one wins
+          // the arbitration, runs ahead and then waits at the stage barrier
+          // while the other runs alone.  A wave's priority falls as it works
+          // through the stage, so the wave that is behind wins instead (the
+          // schedule measured best of several: 1.69 -> 1.61 ms per chunk)
+          if (j < 6) __builtin_amdgcn_s_setprio(3);
+          else if (j < 10) __builtin_amdgcn_s_setprio(2);
+          else if (j < 13) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
           f32x4 nxt[NH];
           if (j + 1 < kGemmStage) {
             head_mfma_i<NH>(x, ahi, alo, nxt);
@@ -569,6 +578,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
           if (p < P_max) srow[p] = (vcur[u] != 0 && long(p) * kp <= last_ok) ? mine_sc[u] : -INFINITY;
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (s + 1 < nstage) {
         publish(s + 1);
 #pragma unroll
