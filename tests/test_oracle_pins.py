@@ -13,6 +13,7 @@ import torch.nn.functional as F
 
 from oracle import dsa_oracle as O
 from dsa_decode_amd import synth
+from tests import brute
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -469,3 +470,48 @@ def test_fp8_paged_latent_is_the_dequantized_cache():
     # and the quantisation itself stays within E4M3's half-ulp of the bf16 cache (2^-4 relative)
     err = np.abs(dense.numpy() - kv.double().numpy())
     assert (err <= np.abs(kv.double().numpy()) * 2.0 ** -4 + pg["kv_scale"].max().item() * 2.0 ** -9).all()
+
+
+# ---------------------------------------------------------------- whole pipeline
+def test_tiny_pipeline_matches_loop_twin():
+    """The tiny workload (1 x 256 tokens, 5 left-pad, kpool 4, 4 x 32 index heads,
+    select_k 8, 4 x 64 MLA, fp32) through compress -> scores -> top-k -> expand ->
+    sparse MLA, by the oracle and by tests/brute.py (scalar loops written
+    separately from the same definitions), each stage on its own outputs:
+    float results agree to 1e-12, integer results exactly."""
+    wl = synth.workload("tiny")
+    ti, ip, mi = synth.token_inputs(wl), synth.index_params(wl), synth.mla_inputs(wl)
+    L = lambda t: t.double().tolist() if hasattr(t, "double") else list(t)
+    row_seq, row_pos = [int(x) for x in ip["row_seq"]], [int(x) for x in ip["row_pos"]]
+
+    comp = O.kpool_compress(ti["k"], ti["gate"], ti["valid"], ti["ape"], ti["seq_len"], wl.kp, wl.P_max)
+    pools = brute.compress(L(ti["k"]), L(ti["gate"]), ti["valid"].tolist(), L(ti["ape"]),
+                           [int(x) for x in ti["seq_len"]], wl.kp)
+    assert len(pools[0]) == comp["n_pools"][0] == 62
+    for p, (start, ok, key) in enumerate(pools[0]):
+        assert comp["pool_start"][0, p] == start and bool(comp["pool_valid"][0, p]) == ok
+        assert np.abs(comp["k_pool"][0, p] - np.array(key)).max() <= 1e-12
+    assert (comp["pool_start"][0, 62:] == -1).all() and not comp["pool_valid"][0, 62:].any()
+
+    sc = O.index_scores(ip["q"], ip["w"], ip["scale"], comp["k_pool"], comp["pool_start"], comp["pool_valid"],
+                        ip["gamma"], ip["beta"], ip["eps"], ip["row_seq"], ip["row_pos"], wl.kp)
+    s64, s32 = brute.scores(L(ip["q"]), L(ip["w"]), ip["scale"], pools, L(ip["gamma"]), L(ip["beta"]),
+                            ip["eps"], row_seq, row_pos, wl.kp, wl.P_max)
+    s64, s32 = np.array(s64), np.array(s32, dtype=np.float32)
+    fin = np.isfinite(s64)
+    assert fin[0, :62].all() and not fin[0, 62:].any()
+    np.testing.assert_array_equal(sc, s32)                       # same fp32 rounding of each score
+    assert np.abs(sc[fin].astype(np.float64) - s64[fin]).max() <= 2.0 ** -24 * np.abs(s64[fin]).max()
+
+    ids = O.topk_pools(sc, wl.K)
+    ids_b = brute.topk(s32.astype(np.float64).tolist(), wl.K)
+    np.testing.assert_array_equal(ids, np.array(ids_b))
+
+    tok = O.expand_selection(ids, ip["row_seq"], comp["pool_start"], wl.kp, wl.W)
+    tok_b = brute.expand(ids_b, row_seq, pools, wl.kp, wl.W)
+    np.testing.assert_array_equal(tok, np.array(tok_b))
+
+    out, lse = O.sparse_mla_decode(mi["q_lat"], mi["kv"], ip["row_seq"], tok, mi["sm_scale"])
+    out_b, lse_b = brute.attend(L(mi["q_lat"]), L(mi["kv"]), row_seq, tok_b, mi["sm_scale"])
+    assert np.abs(out - np.array(out_b)).max() <= 1e-12
+    assert np.abs(lse - np.array(lse_b)).max() <= 1e-12
