@@ -407,11 +407,21 @@ struct ExpandArgs {
   int B, P_max, kp;
   int32_t* token_ids;  // nullptr: no expansion
   int W;
+  int seq;  // the sequence of the workgroup's row (row_seq, read once at kernel entry)
 };
 
+// ex with seq set for row: one uniform load at kernel entry, so that a pool's
+// start is a single load once the pool is known (not behind a load of the
+// row's sequence in every lane that expands)
+__device__ __forceinline__ ExpandArgs expand_for_row(const ExpandArgs& ex, int row) {
+  ExpandArgs r = ex;
+  r.seq = ex.token_ids ? ex.row_seq[row] : -1;
+  return r;
+}
+
 // pool_start of pool pid for the row's sequence (-1: absent or nonexistent)
-__device__ __forceinline__ int32_t expand_start(int row, int32_t pid, const ExpandArgs& ex) {
-  const int b = ex.row_seq[row];
+__device__ __forceinline__ int32_t expand_start(int32_t pid, const ExpandArgs& ex) {
+  const int b = ex.seq;
   int32_t ps = -1;
   if (pid >= 0 && pid < ex.P_max && b >= 0 && b < ex.B) ps = ex.pool_start[size_t(b) * ex.P_max + pid];
   return ps;
@@ -423,7 +433,7 @@ __device__ __forceinline__ void expand_write(int row, int j, int32_t ps, const E
 }
 
 __device__ __forceinline__ void expand_one(int row, int j, int32_t pid, const ExpandArgs& ex) {
-  expand_write(row, j, expand_start(row, pid, ex), ex);
+  expand_write(row, j, expand_start(pid, ex), ex);
 }
 
 template <int NT>
@@ -670,7 +680,7 @@ __device__ __forceinline__ bool merge_heads(TkShared<NT>& sh, int row, int S, in
   int32_t ps[KPT];
   if (ex.token_ids) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) ps[j] = (vmask >> j) & 1u ? expand_start(row, int32_t(0xffffffffu - lo[j]), ex) : -1;
+    for (int j = 0; j < KPT; ++j) ps[j] = (vmask >> j) & 1u ? expand_start(int32_t(0xffffffffu - lo[j]), ex) : -1;
   }
   if (tid == 0) sh.flag = 0;
   for (int u = tid; u < kBins; u += NT) sh.hist[u] = 0;
@@ -733,10 +743,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   uint64_t* __restrict__ keys_out,
                                                   int32_t* __restrict__ pool_ids, ExpandArgs ex) {
   __shared__ TkShared<NT> sh;
+  const ExpandArgs exr = expand_for_row(ex, blockIdx.y);
   if constexpr (FINAL)
     if (ex.token_ids) expand_pad<NT>(blockIdx.y, K, ex);
   topk_block<NT, KPT, FROM_SCORES, FINAL>(sh, blockIdx.y, blockIdx.x, gridDim.x, scores, keys_in, P, chunk,
-                                          nsplit_in, K, keys_out, pool_ids, ex);
+                                          nsplit_in, K, keys_out, pool_ids, exr);
 }
 
 // Split rows in one launch: workgroup (c, row) selects chunk c's K winners,
@@ -752,6 +763,7 @@ __global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict_
                                                         int32_t* __restrict__ pool_ids, ExpandArgs ex) {
   __shared__ TkShared<NT> sh;
   const int row = blockIdx.y;
+  const ExpandArgs exr = expand_for_row(ex, row);
   topk_block<NT, KPT1, true, false>(sh, row, blockIdx.x, nsplit, scores, nullptr, P, chunk, 0, K, keys, nullptr,
                                     ExpandArgs{});
   // every thread's winner stores are complete before the row's counter moves
@@ -765,9 +777,9 @@ __global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict_
   // for the next call and merge
   if (threadIdx.x == 0) __hip_atomic_store(&counters[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (ex.token_ids) expand_pad<NT>(row, K, ex);
-  if (m < K && merge_heads<NT, KPTH>(sh, row, nsplit, m, K, keys, pool_ids, ex)) return;
+  if (m < K && merge_heads<NT, KPTH>(sh, row, nsplit, m, K, keys, pool_ids, exr)) return;
   __syncthreads();
-  topk_block<NT, KPT2, false, true>(sh, row, 0, 1, nullptr, keys, P, 0, nsplit, K, nullptr, pool_ids, ex);
+  topk_block<NT, KPT2, false, true>(sh, row, 0, 1, nullptr, keys, P, 0, nsplit, K, nullptr, pool_ids, exr);
 }
 
 struct TkPlan {

@@ -255,7 +255,7 @@ def test_prefill_topk_forced_ties_full_size():
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("Q,P,K,ties", [(1, 1, 1, 0), (3, 7, 8, 0), (2, 1000, 8, 3), (4, 4097, 512, 50),
                                         (2, 65537, 512, 0), (4, 65536, 512, 40), (1, 65536, 2048, 0),
-                                        (5, 300000, 64, 1000), (300, 5000, 100, 20)])
+                                        (5, 300000, 64, 1000), (300, 5000, 100, 20), (4, 65536, 128, 30)])
 def test_topk_shapes_ties_and_padding(Q, P, K, ties):
     s = synth.random_scores(Q, P, seed=Q * 1000 + P, tie_levels=ties, neg_inf_frac=0.3, signed_zeros=True)
     s[0, : P // 2] = -np.inf          # a row with few candidates
