@@ -51,21 +51,36 @@ constexpr int kMlaThreads = 256;
 struct alignas(16) MlaShared {
   uint16_t rows[kMlaSplit][kMlaDl];  // latent rows, 16-byte pieces swizzled per row (64 KiB)
   struct {                           // the softmax exchange
-    uint16_t p[16][kMlaSplit + 8];   // P[head][token] relative to its wave's maximum, bf16
-                                     // (rows padded to 144 B: the 16 heads' rows start in
-                                     // different banks)
+    uint16_t p[16][kMlaSplit];       // P[head][token] relative to its wave's maximum, bf16
+                                     // (8-token groups swizzled per head, mla_pidx)
     float m[16][4];                  // per head: each wave's maximum (log2 domain)
     float l[16][4];                  // per head: each wave's sum of P
   } x;
 };
 
-// Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t).  Over any 8
-// consecutive rows the swizzle takes 8 distinct values mod 8 (and over 16 rows
-// 16 distinct values), so the logits reads (one piece of 16 consecutive rows
-// per lane group) hit distinct banks; rows 8g .. 8g+3 (and 8g+4 .. 8g+7) take
-// values whose halves (v >> 1) differ, so the transposing reads (4 rows x 2
-// adjacent pieces per 16 lanes) do too.
-__device__ __forceinline__ int mla_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1) | (t & 8); }
+// LDS banks, as measured on gfx950 with the bank-conflict counter: a 16-byte
+// read is served in passes of 16 lanes over 256 bytes (16 slots of 16 bytes),
+// each 32-lane half of the wave in two passes that take its lane quads 0, 3,
+// 5, 6 and 1, 2, 4, 7 (the parity of lane bits 2..4); 8-byte reads, including
+// the transposing ones, in passes of 32 lanes over 256 bytes; writes in passes
+// over 128 bytes (8 lanes for 16 bytes, 16 lanes for 8 bytes).  A pass costs
+// one extra cycle for every further distinct address in the same slot.
+//
+// Piece c (16 bytes) of token row t sits at piece c ^ mla_swz(t), with
+// mla_swz(t) = rotl4(t) ^ (t & 8) on the low four bits of t.  The logits reads
+// (lane (ln, kg) reads piece 4k + kg of row 16w + ln) then fill every slot of
+// each 16-lane pass once, and so do the transposing reads of the value
+// contraction (rows 8g .. 8g+3 and 8g+8 .. 8g+11 by two adjacent pieces in a
+// 32-lane pass): no bank conflicts.  (A swizzle that spreads 16 consecutive
+// rows over the slots is not enough: the pass takes lanes of two lane groups.)
+__device__ __forceinline__ int mla_swz(int t) { return ((((t << 1) & 14) | ((t >> 3) & 1)) ^ (t & 8)); }
+
+// The softmax weights P of one head: 64 tokens (128 bytes); the 8-token group
+// g of head h sits at group g ^ mla_pswz(h), so the 16-byte reads of 16 heads
+// (lane (ln, kg) reads group 4ks + kg of head ln) fill every slot of a pass.
+__device__ __forceinline__ int mla_pswz(int h) { return (h & 1) | ((h & 2) << 1) | ((h & 4) >> 1); }
+// element index of token tok of head h in its P row
+__device__ __forceinline__ int mla_pidx(int h, int tok) { return ((((tok >> 3) ^ mla_pswz(h)) << 3) | (tok & 7)); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -111,13 +126,12 @@ struct KvPages {
 // then q, then the gather as soon as the ids are in.
 constexpr int kMla2Ids = 2 * kMlaSplit;  // ids per workgroup
 constexpr int kMla2Threads = 512;
-constexpr int kMla2QLd = kMlaDl + 8;     // padded q row (1040 B: 16 heads' reads spread over the banks)
 
 struct alignas(16) Mla2Shared {
   uint16_t rows[2][kMlaSplit][kMlaDl];  // each half's latent rows (swizzled as in MlaShared), 128 KiB
-  uint16_t q[16][kMla2QLd];             // the 16 heads' q_lat rows
+  uint16_t q[16][kMlaDl];               // the 16 heads' q_lat rows (pieces swizzled as the rows)
   struct {
-    uint16_t p[16][kMlaSplit + 8];
+    uint16_t p[16][kMlaSplit];
     float m[16][4];
     float l[16][4];
   } x[2];                               // each half's softmax exchange
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int hh = 2 * w8 + e;
-    __builtin_amdgcn_global_load_lds(q_lat + (size_t(r) * Hm + hg * 16 + hh) * kMlaDl + 8 * lane,
+    __builtin_amdgcn_global_load_lds(q_lat + (size_t(r) * Hm + hg * 16 + hh) * kMlaDl + 8 * (lane ^ mla_swz(hh)),
                                      (__attribute__((address_space(3))) void*)(&sh.q[hh][0]), 16, 0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -225,12 +239,12 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   {
     // every fragment read is issued before the first MFMA (one LDS round trip)
-    const int t = 16 * w + ln, sw = mla_swz(t);
+    const int t = 16 * w + ln, sw = mla_swz(t), swq = mla_swz(ln);
     u32x4 fa[16], fb[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       fa[k] = *reinterpret_cast<const u32x4*>(&rows[t][((4 * k + kg) ^ sw) * 8]);
-      fb[k] = *reinterpret_cast<const u32x4*>(&sh.q[ln][(4 * k + kg) * 8]);
+      fb[k] = *reinterpret_cast<const u32x4*>(&sh.q[ln][((4 * k + kg) ^ swq) * 8]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] *= tsc[j];
   }
-  *reinterpret_cast<u32x2*>(&X.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+  *reinterpret_cast<u32x2*>(&X.p[ln][mla_pidx(ln, 16 * w + 4 * kg)]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
   if (kg == 0) {
     X.m[ln][w] = m_use;
     X.l[ln][w] = l;
@@ -292,7 +306,7 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
   bf16x8 pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    const u32x4 rw = *reinterpret_cast<const u32x4*>(&X.p[ln][32 * ks + 8 * kg]);
+    const u32x4 rw = *reinterpret_cast<const u32x4*>(&X.p[ln][mla_pidx(ln, 32 * ks + 8 * kg)]);
     const float f = fv[2 * ks + (kg >> 1)];
     u32x4 scv;
 #pragma unroll
@@ -483,7 +497,8 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    *reinterpret_cast<u32x2*>(&sh.x.p[ln][16 * w + 4 * kg]) = u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+    *reinterpret_cast<u32x2*>(&sh.x.p[ln][mla_pidx(ln, 16 * w + 4 * kg)]) =
+        u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
     if (kg == 0) {
       sh.x.m[ln][w] = m_use;
       sh.x.l[ln][w] = l;
@@ -512,7 +527,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
     bf16x8 pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.x.p[ln][32 * ks + 8 * kg]);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.x.p[ln][mla_pidx(ln, 32 * ks + 8 * kg)]);
       const float f = fv[2 * ks + (kg >> 1)];
       u32x4 sc;
 #pragma unroll
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
 // is computed.
 struct alignas(16) Mla64x8Shared {
   uint16_t rows[2][kMlaSplit][kMlaDl];  // latent rows, pieces swizzled by mla_swz
-  uint16_t p[64][kMlaSplit + 8];        // P[head][token] relative to its half's maximum
+  uint16_t p[64][kMlaSplit];            // P[head][token] relative to its half's maximum (mla_pidx)
   float m[64][2];                       // per head and token half: maximum (log2 domain, 0 if none)
   float l[64][2];                       // per head and token half: sum of P
 };
@@ -685,7 +700,7 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
         p[j] = __builtin_amdgcn_exp2f(acc[t][j] - m_use);
         lh += p[j];
       }
-      *reinterpret_cast<u32x2*>(&sh.p[hq][32 * th + 16 * t + 4 * kg]) =
+      *reinterpret_cast<u32x2*>(&sh.p[hq][mla_pidx(hq, 32 * th + 16 * t + 4 * kg)]) =
           u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
     }
     lh += __shfl_xor(lh, 16, kWave);
@@ -727,7 +742,7 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
       bf16x8 pb[4];
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][32 * ks + 8 * kg]);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][mla_pidx(ln, 32 * ks + 8 * kg)]);
         const float f = fh[ht][ks];
         u32x4 sc;
 #pragma unroll
