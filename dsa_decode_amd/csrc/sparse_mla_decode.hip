@@ -92,6 +92,29 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Transposing LDS read of 8-bit elements: within each group of 16 lanes, lane
+// i receives byte (i & 7) of the 8-byte words read by lanes 2e + (i >> 3),
+// e = 0..7 (so lanes 2e, 2e+1 reading row e's bytes 0..7 and 8..15 of a
+// 16-column block give lane i column i of rows 0..7).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Eight OCP FP8 E4M3 codes (byte i of the pair = element i) -> eight bf16,
+// exactly (every E4M3 value is a bf16 value): one scaled convert per two codes.
+__device__ __forceinline__ u32x4 widen_fp8x8(u32x2 c) {
+  u32x4 v;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    v[2 * h2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h2], 1.0f, false));
+    v[2 * h2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[h2], 1.0f, true));
+  }
+  return v;
+}
+
 // offset (in elements) of partial-output element (head group hg, lane, dl) of a
 // (row, split): [hg][dq][blk][lane][j], dl = 128 dq + 16 blk + 4 kg + j
 __device__ __forceinline__ size_t part_off(size_t rs, int HG, int hg, int dq, int blk, int lane) {
@@ -103,8 +126,9 @@ __device__ __forceinline__ size_t part_off(size_t rs, int HG, int hg, int dq, in
 // page_size, Dl] behind a page table [B, max_pages] (token t of sequence b is
 // row t % page_size of page block_table[b, t / page_size]).  kKvPagedFp8: the
 // same pages holding OCP FP8 E4M3 codes with one fp32 scale per row; the codes
-// are widened to bf16 exactly on the way into LDS, and the row's scale
-// multiplies the token's logit and its softmax weight in the value sum.
+// go into LDS as they are (half the bytes of a bf16 row) and are widened to
+// bf16 exactly as the fragments are read, and the row's scale multiplies the
+// token's logit and its softmax weight in the value sum.
 enum KvLayout { kKvRows = 0, kKvPaged = 1, kKvPagedFp8 = 2 };
 
 struct KvPages {
@@ -179,8 +203,11 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     }
   }
   uint16_t (*rows)[kMlaDl] = sh.rows[half];
+  // fp8 rows: 512 bytes of codes each, the half's 64 rows in the first 32 KiB
+  // of its row buffer; the 16-byte piece c of row t sits at piece c ^ (t & 15)
+  uint8_t (*rows8)[kMlaDl] = reinterpret_cast<uint8_t (*)[kMlaDl]>(&sh.rows[half][0][0]);
   uint32_t vmask = 0;
-  if (KV != kKvPagedFp8) {
+  if constexpr (KV != kKvPagedFp8) {
     // one row per instruction: lane i fills piece position i with piece
     // i ^ swz of the token's row; absent ids give a zero row
     const size_t base = KV == kKvRows ? seq_base : 0;
@@ -197,30 +224,28 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
       }
     }
   } else {
-    // fp8 rows (512 B): lane p loads the 8 codes of piece p of every row
-    // first, then widens them into piece position p ^ swz of the row.  An
-    // E4M3 value is exactly a bf16 value, so the widening rounds nothing (one
-    // scaled-convert instruction per two codes, scale 1); the row's scale is
-    // applied to the token's logits and to its P instead of to its 512 values
+    // two rows per instruction (lanes 0..31: row 2i, lanes 32..63: row 2i+1),
+    // codes straight into LDS; absent ids give zero rows.  The codes are
+    // widened to bf16 when the fragments are read (an E4M3 value is exactly a
+    // bf16 value, so nothing is rounded), and the row's scale is applied to
+    // the token's logits and to its P instead of to its 512 values
     // (logit_j = scale_j <q, codes_j>, sum_j p_j v_j = sum_j (p_j scale_j) codes_j)
     const uint8_t* kv8 = static_cast<const uint8_t*>(kv_v);
-    u32x2 codes[16];
+    const int hl = lane >> 5, pl = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int id = __builtin_amdgcn_readlane(myid, i);
-      codes[i] = id >= 0 ? *reinterpret_cast<const u32x2*>(kv8 + size_t(id) * kMlaDl + 8 * lane) : u32x2{0u, 0u};
-      vmask |= (id >= 0 ? 1u : 0u) << i;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * w + i;
-      u32x4 v;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        v[2 * h2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][h2], 1.0f, false));
-        v[2 * h2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][h2], 1.0f, true));
+    for (int i = 0; i < 8; ++i) {
+      const int id0 = __builtin_amdgcn_readlane(myid, 2 * i), id1 = __builtin_amdgcn_readlane(myid, 2 * i + 1);
+      vmask |= (id0 >= 0 ? 1u : 0u) << (2 * i);
+      vmask |= (id1 >= 0 ? 1u : 0u) << (2 * i + 1);
+      const int id = hl ? id1 : id0;
+      const int t = 16 * w + 2 * i + hl;
+      if (id >= 0) {
+        const uint8_t* src = kv8 + size_t(id) * kMlaDl + 16 * (pl ^ (t & 15));
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(&rows8[16 * w + 2 * i][0]),
+                                         16, 0, 0);
+      } else {
+        *reinterpret_cast<u32x4*>(&rows8[t][16 * pl]) = u32x4{0u, 0u, 0u, 0u};
       }
-      *reinterpret_cast<u32x4*>(&rows[t][8 * (lane ^ mla_swz(t))]) = v;
     }
   }
   // q_lat rows of heads 2 w8, 2 w8 + 1 into LDS, after the gather (q is needed
@@ -241,11 +266,20 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     // every fragment read is issued before the first MFMA (one LDS round trip)
     const int t = 16 * w + ln, sw = mla_swz(t), swq = mla_swz(ln);
     u32x4 fa[16], fb[16];
+    if constexpr (KV != kKvPagedFp8) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      fa[k] = *reinterpret_cast<const u32x4*>(&rows[t][((4 * k + kg) ^ sw) * 8]);
-      fb[k] = *reinterpret_cast<const u32x4*>(&sh.q[ln][((4 * k + kg) ^ swq) * 8]);
+      for (int k = 0; k < 16; ++k) fa[k] = *reinterpret_cast<const u32x4*>(&rows[t][((4 * k + kg) ^ sw) * 8]);
+    } else {
+      // latent columns 32k + 8kg .. +7 of row t: half of piece 2k + (kg >> 1)
+      u32x2 c8[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        c8[k] = *reinterpret_cast<const u32x2*>(&rows8[t][(((2 * k + (kg >> 1)) ^ (t & 15)) << 4) + ((kg & 1) << 3)]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) fa[k] = widen_fp8x8(c8[k]);
     }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) fb[k] = *reinterpret_cast<const u32x4*>(&sh.q[ln][((4 * k + kg) ^ swq) * 8]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 16; k += 2) {
@@ -320,13 +354,20 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     u32x2 tl[8][2], th[8][2];
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
-      const int col = 128 * w + 16 * blk + 4 * (ln & 3);
-      const int pc = col >> 3, off = col & 7;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
-        tl[blk][ks] = lds_read_tr16(&rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
-        th[blk][ks] = lds_read_tr16(&rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
+        if constexpr (KV != kKvPagedFp8) {
+          const int col = 128 * w + 16 * blk + 4 * (ln & 3);
+          const int pc = col >> 3, off = col & 7;
+          const int t0 = 32 * ks + 8 * kg + (ln >> 2), t1 = t0 + 4;
+          tl[blk][ks] = lds_read_tr16(&rows[t0][((pc ^ mla_swz(t0)) << 3) + off]);
+          th[blk][ks] = lds_read_tr16(&rows[t1][((pc ^ mla_swz(t1)) << 3) + off]);
+        } else {
+          // codes of tokens 32ks + 8kg .. +7 at latent column 128w + 16blk + ln:
+          // lane 2e + j reads 8 codes of token 32ks + 8kg + e from piece 8w + blk
+          const int t0 = 32 * ks + 8 * kg + (ln >> 1);
+          tl[blk][ks] = lds_read_tr8(&rows8[t0][(((8 * w + blk) ^ (t0 & 15)) << 4) + ((ln & 1) << 3)]);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -334,8 +375,11 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     for (int blk = 0; blk < 8; ++blk) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        a = mfma16x16x32(as_bf16x8(u32x4{tl[blk][ks][0], tl[blk][ks][1], th[blk][ks][0], th[blk][ks][1]}), pb[ks], a);
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 av = KV != kKvPagedFp8 ? u32x4{tl[blk][ks][0], tl[blk][ks][1], th[blk][ks][0], th[blk][ks][1]}
+                                           : widen_fp8x8(tl[blk][ks]);
+        a = mfma16x16x32(as_bf16x8(av), pb[ks], a);
+      }
       o[blk] = a;
     }
   }
