@@ -618,13 +618,15 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
 // logits of heads 16 (w & 3) .. +15 over token half w >> 2 of each 64-id block
 // (q^T of its 16 heads in registers), and accumulates latent eighth w of O^T
 // for all 64 heads (64 accumulators per lane instead of 128).  The two token
-// halves of a head meet in LDS: each wave writes P relative to its own maximum
-// with that maximum and its sum; every wave then forms, for each of the 64
-// heads, the new running maximum, the rescale 2^(M_old - M_new) of its
-// accumulators and the factors 2^(m_half - M_new) it applies to P as it reads
-// it (all waves form the same values from the same LDS words).  Rows are
-// gathered 8 per wave, the next block into the second buffer while this one
-// is computed.
+// halves of a head meet in LDS twice per block: first their maxima, so that
+// each logits wave forms P against the head's new running maximum M_new (the
+// running maximum and both halves' maxima), then P and the halves' sums;
+// every wave then forms, for each of the 64 heads, the same M_new from the
+// same LDS words, rescales its accumulators by 2^(M_old - M_new) and reads P
+// as it is.  (Forming P against each half's own maximum and scaling it by
+// 2^(m_half - M_new) as it was read spared a barrier but cost more vector
+// work: 1.91 against 1.72 ms per 4096-row chunk.)  Rows are gathered 8 per
+// wave, the next block into the second buffer while this one is computed.
 struct alignas(16) Mla64x8Shared {
   uint16_t rows[2][kMlaSplit][kMlaDl];  // latent rows, pieces swizzled by mla_swz
   uint16_t p[64][kMlaSplit];            // P[head][token] relative to its half's maximum (mla_pidx)
@@ -734,14 +736,24 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
       }
     m = fmaxf(m, __shfl_xor(m, 16, kWave));
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const float m_use = m == -INFINITY ? 0.f : m;
+    // the two token halves' maxima meet first, so that P is formed against the
+    // block's new running maximum and the value contraction reads it as it is
+    // (a factor per half applied as P is read cost more than this barrier)
+    if (kg == 0) sh.m[hq][th] = m;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const float m_other = sh.m[hq][th ^ 1];
+    float Mrun_q = M_run[0];  // running maximum of head hq (a select chain, not a dynamic index)
+#pragma unroll
+    for (int ht = 1; ht < 4; ++ht) Mrun_q = hgw == ht ? M_run[ht] : Mrun_q;
+    const float Mq = fmaxf(Mrun_q, fmaxf(m, m_other));
+    const float Mq_use = Mq == -INFINITY ? 0.f : Mq;
     float lh = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(acc[t][j] - m_use);
+        p[j] = __builtin_amdgcn_exp2f(acc[t][j] - Mq_use);
         lh += p[j];
       }
       *reinterpret_cast<u32x2*>(&sh.p[hq][mla_pidx(hq, 32 * th + 16 * t + 4 * kg)]) =
@@ -749,29 +761,22 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
     }
     lh += __shfl_xor(lh, 16, kWave);
     lh += __shfl_xor(lh, 32, kWave);
-    if (kg == 0) {
-      sh.m[hq][th] = m_use;
-      sh.l[hq][th] = lh;
-    }
-    // P and the halves' maxima and sums of all 64 heads published: LDS writes
-    // done, then the barrier alone (the next block's gather stays in flight)
+    if (kg == 0) sh.l[hq][th] = lh;
+    // P and the halves' sums of all 64 heads published: LDS writes done, then
+    // the barrier alone (the next block's gather stays in flight)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // merge the two halves into each head's running sums (the factors of the
-    // halves are applied to P^T as it is read, one token half at a time)
-    float fh[4][2];
+    // each head's new running maximum (the same value its logits wave formed,
+    // from the same words) and the rescale of what is accumulated
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const int h = 16 * ht + ln;
       const f32x2 mh = *reinterpret_cast<const f32x2*>(&sh.m[h][0]);
       const f32x2 lhv = *reinterpret_cast<const f32x2*>(&sh.l[h][0]);
-      const float Mb = fmaxf(lhv[0] > 0.f ? mh[0] : -INFINITY, lhv[1] > 0.f ? mh[1] : -INFINITY);
-      const float M_new = fmaxf(M_run[ht], Mb);
+      const float M_new = fmaxf(M_run[ht], fmaxf(mh[0], mh[1]));
       const float M_use = M_new == -INFINITY ? 0.f : M_new;
       const float alpha = M_run[ht] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run[ht] - M_use);
-      fh[ht][0] = lhv[0] > 0.f ? __builtin_amdgcn_exp2f(mh[0] - M_use) : 0.f;
-      fh[ht][1] = lhv[1] > 0.f ? __builtin_amdgcn_exp2f(mh[1] - M_use) : 0.f;
-      l_run[ht] = fmaf(l_run[ht], alpha, fmaf(fh[ht][0], lhv[0], fh[ht][1] * lhv[1]));
+      l_run[ht] = fmaf(l_run[ht], alpha, lhv[0] + lhv[1]);
       M_run[ht] = M_new;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) o[ht][kk] *= alpha;
@@ -785,15 +790,8 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pb[4];
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][mla_pidx(ln, 32 * ks + 8 * kg)]);
-        const float f = fh[ht][ks];
-        u32x4 sc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sc[e] = pack2bf(__uint_as_float(raw[e] << 16) * f, __uint_as_float(raw[e] & 0xffff0000u) * f);
-        pb[ht] = as_bf16x8(sc);
-      }
+      for (int ht = 0; ht < 4; ++ht)
+        pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][mla_pidx(ln, 32 * ks + 8 * kg)]));
       const int t0 = 32 * ks + 8 * kgv + (lnv >> 2), t1 = t0 + 4;
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
