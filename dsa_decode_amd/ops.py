@@ -377,6 +377,30 @@ def bind_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale, out, lse, wo
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
 
 
+def bind_sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_size, row_seq, token_ids, sm_scale,
+                                 out, lse, workspace) -> BoundCall:
+    Q, Hm, Dl = q_lat.shape
+    num_pages, ps, Dl2 = kv_pages.shape
+    if Dl2 != Dl or ps != page_size:
+        raise ValueError("kv_pages disagrees with q_lat / page_size")
+    B, max_pages = block_table.shape
+    if kv_pages.dtype == torch.bfloat16:
+        code, sc_ptr = DSA_BF16, None
+    elif kv_pages.dtype == torch.uint8:
+        if kv_scale is None or tuple(kv_scale.shape) != (num_pages, page_size):
+            raise ValueError("fp8 pages need kv_scale [num_pages, page_size]")
+        code, sc_ptr = DSA_FP8_E4M3, _dev(kv_scale, "kv_scale", torch.float32)
+    else:
+        raise ValueError(f"kv_pages dtype {kv_pages.dtype} not supported")
+    return BoundCall("dsa_sparse_mla_decode_paged", (
+        _dev(q_lat, "q_lat", torch.bfloat16), _dev(kv_pages, "kv_pages"), sc_ptr,
+        _dev(block_table, "block_table", torch.int32), max_pages, page_size, num_pages,
+        _dev(row_seq, "row_seq", torch.int32), _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B,
+        token_ids.shape[1], float(sm_scale), code, _dev(out, "out", torch.bfloat16),
+        _dev(lse, "lse", torch.float32) if lse is not None else None,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
+
+
 def bind_kpool_append(k, gate, valid, ape, seq_len, kpool, state, max_new_pools=1) -> BoundCall:
     B, T_max, D = k.shape
     P_max = state["pool_start"].shape[1]

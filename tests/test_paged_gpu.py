@@ -97,3 +97,27 @@ def test_paged_fp8_long_context_rows():
     tok = np.stack([rng.choice(wl.T_max, wl.W, replace=False) for _ in range(wl.Q)]).astype(np.int32)
     pg = synth.paged_latent(mi["kv"], 64, seed=64, fp8=True)
     _check(mi["q_lat"], pg, 64, np.arange(wl.Q, dtype=np.int32), tok, mi["sm_scale"])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_bound_paged_call_matches_entry_point(fp8):
+    # the pre-bound call (arguments marshalled once, as the benchmark launches
+    # it) writes exactly what the entry point writes
+    B, T, Hm, Q, W, ps = 2, 4096, 64, 3, 2048, 64
+    kv, q, row_seq, tok = _case(B, T, Hm, Q, W, seed=77 + fp8)
+    pg = synth.paged_latent(kv, ps, seed=5, fp8=fp8)
+    kvp, bt = dev(pg["kv_pages"]), dev(pg["block_table"])
+    sc = dev(pg["kv_scale"]) if fp8 else None
+    rs, tk = dev(torch.from_numpy(row_seq)), dev(torch.from_numpy(tok.astype(np.int32)))
+    ref_o, ref_l = ops().dsa_sparse_mla_decode_paged(dev(q), kvp, sc, bt, ps, rs, tk, 512 ** -0.5)
+    out = torch.full((Q, Hm, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Q, Hm), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, ops().dsa_sparse_mla_paged_workspace_bytes(Q, Hm, 512, W)), dtype=torch.uint8,
+                     device="cuda")
+    qd = dev(q)
+    call = ops().bind_sparse_mla_decode_paged(qd, kvp, sc, bt, ps, rs, tk, 512 ** -0.5, out, lse, ws)
+    for _ in range(2):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
+        assert torch.equal(lse, ref_l)
