@@ -8,6 +8,8 @@ arithmetic runs in the library's kernels; there is no fallback.
 """
 from __future__ import annotations
 
+import threading
+
 import torch
 
 from . import _lib
@@ -16,6 +18,10 @@ from ._lib import (DSA_BF16, DSA_F32, DSA_FP8_E4M3, DSA_MLA_SCRATCH_BYTES, DSA_T
                    DsaError, check)
 
 _ACT = {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16}
+
+
+# tensors referenced by the call being bound (see _bind); None outside a bind
+_binding = threading.local()
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
@@ -29,6 +35,9 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if t.data_ptr() % 16:
         raise ValueError(f"{name} must be 16-byte aligned")
+    keep = getattr(_binding, "keep", None)
+    if keep is not None:
+        keep.append(t)
     return t.data_ptr()
 
 
@@ -313,12 +322,13 @@ def dsa_sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_siz
 # once, for loops that launch the same stage many times (benchmarks, serving
 # steps).  Calling the result launches on the stream captured at bind time.
 class BoundCall:
-    __slots__ = ("name", "fn", "args")
+    __slots__ = ("name", "fn", "args", "keep")
 
-    def __init__(self, name: str, args: tuple):
+    def __init__(self, name: str, args: tuple, keep: tuple = ()):
         self.name = name
         self.fn = getattr(_lib.load(), name)
         self.args = args
+        self.keep = keep  # the tensors behind the pointers in args, alive as long as the call
 
     def __call__(self) -> None:
         st = self.fn(*self.args)
@@ -326,12 +336,25 @@ class BoundCall:
             check(self.name, st)
 
 
+def _bind(name: str, build) -> BoundCall:
+    """A BoundCall whose argument tuple build() marshals; every tensor that
+    build() turns into a pointer is kept with the call, so that no buffer it
+    launches on can be freed while the call exists."""
+    _binding.keep = []
+    try:
+        args = build()
+        keep = tuple(_binding.keep)
+    finally:
+        _binding.keep = None
+    return BoundCall(name, args, keep)
+
+
 def bind_index_scores(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,
                       row_pos, kpool, scores) -> BoundCall:
     Q, H, D = q.shape
     B, P_max = pool_start.shape
     _check_pool_cache(k_pool, B, P_max, D)
-    return BoundCall("dsa_index_scores", (
+    return _bind("dsa_index_scores", lambda: (
         _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
         _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
         _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps),
@@ -341,17 +364,17 @@ def bind_index_scores(q, w, scale, k_pool, pool_start, pool_valid, ln_gamma, ln_
 
 def bind_topk_pools(scores, K, pool_ids, workspace) -> BoundCall:
     Q, P = scores.shape
-    workspace = _topk_ws(workspace, 1, scores.device)
-    return BoundCall("dsa_topk_pools", (
+    workspace = _topk_ws(workspace, max(1, dsa_topk_workspace_bytes(Q, P, K)), scores.device)
+    return _bind("dsa_topk_pools", lambda: (
         _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()))
 
 
 def bind_topk_pools_expand(scores, K, pool_ids, row_seq, pool_start, kpool, token_ids, workspace) -> BoundCall:
     Q, P = scores.shape
-    workspace = _topk_ws(workspace, 1, scores.device)
+    workspace = _topk_ws(workspace, max(1, dsa_topk_workspace_bytes(Q, P, K)), scores.device)
     B, P_max = pool_start.shape
-    return BoundCall("dsa_topk_pools_expand", (
+    return _bind("dsa_topk_pools_expand", lambda: (
         _dev(scores, "scores", torch.float32), Q, P, K, _dev(pool_ids, "pool_ids", torch.int32),
         _dev(row_seq, "row_seq", torch.int32), _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool,
         _dev(token_ids, "token_ids", torch.int32), token_ids.shape[1],
@@ -361,7 +384,7 @@ def bind_topk_pools_expand(scores, K, pool_ids, row_seq, pool_start, kpool, toke
 def bind_expand_selection(pool_ids, row_seq, pool_start, kpool, token_ids) -> BoundCall:
     Q, K = pool_ids.shape
     B, P_max = pool_start.shape
-    return BoundCall("dsa_expand_selection", (
+    return _bind("dsa_expand_selection", lambda: (
         _dev(pool_ids, "pool_ids", torch.int32), Q, K, _dev(row_seq, "row_seq", torch.int32),
         _dev(pool_start, "pool_start", torch.int32), B, P_max, kpool, _dev(token_ids, "token_ids", torch.int32),
         token_ids.shape[1], _stream()))
@@ -370,7 +393,7 @@ def bind_expand_selection(pool_ids, row_seq, pool_start, kpool, token_ids) -> Bo
 def bind_sparse_mla_decode(q_lat, kv, row_seq, token_ids, sm_scale, out, lse, workspace) -> BoundCall:
     Q, Hm, Dl = q_lat.shape
     B, T_max, _ = kv.shape
-    return BoundCall("dsa_sparse_mla_decode", (
+    return _bind("dsa_sparse_mla_decode", lambda: (
         _dev(q_lat, "q_lat", kv.dtype), _dev(kv, "kv"), _dev(row_seq, "row_seq", torch.int32),
         _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B, T_max, token_ids.shape[1], float(sm_scale),
         _act_code(kv), _dev(out, "out", kv.dtype), _dev(lse, "lse", torch.float32) if lse is not None else None,
@@ -392,7 +415,7 @@ def bind_sparse_mla_decode_paged(q_lat, kv_pages, kv_scale, block_table, page_si
         code, sc_ptr = DSA_FP8_E4M3, _dev(kv_scale, "kv_scale", torch.float32)
     else:
         raise ValueError(f"kv_pages dtype {kv_pages.dtype} not supported")
-    return BoundCall("dsa_sparse_mla_decode_paged", (
+    return _bind("dsa_sparse_mla_decode_paged", lambda: (
         _dev(q_lat, "q_lat", torch.bfloat16), _dev(kv_pages, "kv_pages"), sc_ptr,
         _dev(block_table, "block_table", torch.int32), max_pages, page_size, num_pages,
         _dev(row_seq, "row_seq", torch.int32), _dev(token_ids, "token_ids", torch.int32), Q, Hm, Dl, B,
@@ -405,7 +428,7 @@ def bind_kpool_append(k, gate, valid, ape, seq_len, kpool, state, max_new_pools=
     B, T_max, D = k.shape
     P_max = state["pool_start"].shape[1]
     _check_pool_cache(state["k_pool"], B, P_max, D)
-    return BoundCall("dsa_kpool_append", (
+    return _bind("dsa_kpool_append", lambda: (
         _dev(k, "k", k.dtype), _dev(gate, "gate", k.dtype), _dev(valid, "valid", torch.uint8),
         _dev(ape, "ape", torch.float32), _dev(seq_len, "seq_len", torch.int32),
         B, T_max, D, kpool, P_max, int(max_new_pools), _act_code(k),
@@ -419,8 +442,8 @@ def bind_index_topk_pools_expand(q, w, scale, k_pool, pool_start, pool_valid, ln
     Q, H, D = q.shape
     B, P_max = pool_start.shape
     _check_pool_cache(k_pool, B, P_max, D)
-    workspace = _topk_ws(workspace, 1, q.device)
-    return BoundCall("dsa_index_topk_pools_expand", (
+    workspace = _topk_ws(workspace, max(1, dsa_index_topk_workspace_bytes(Q, P_max, K)), q.device)
+    return _bind("dsa_index_topk_pools_expand", lambda: (
         _dev(q, "q", k_pool.dtype), _dev(w, "w", torch.float32), float(scale), _dev(k_pool, "k_pool"),
         _dev(pool_start, "pool_start", torch.int32), _dev(pool_valid, "pool_valid", torch.uint8),
         _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32), float(ln_eps),

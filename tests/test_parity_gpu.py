@@ -782,3 +782,28 @@ def test_streamed_index_topk_prefill_chunk_full_size():
     full[rows] = s_rows
     _streamed_vs_oracle(full, ids_b.cpu().numpy(), tok_b.cpu().numpy(), rows, ip["row_seq"].numpy(),
                         d["comp"]["pool_start"], wl.kp, wl.K, wl.W)
+
+
+def test_bound_call_keeps_its_buffers_and_sizes_its_workspace():
+    # a pre-bound top-k made from temporaries (output created inline, no
+    # workspace given, on the decode shape whose split rows need a workspace)
+    # holds those buffers for as long as the call exists, so new allocations
+    # cannot land on them, and writes what the entry point writes
+    import gc
+    import weakref
+    s = dev(synth.random_scores(4, 65536, seed=12, tie_levels=20))
+    ref = ops().dsa_topk_pools(s, 512)
+    out = torch.full((4, 512), 0x7fffffff, dtype=torch.int32, device="cuda")
+    call = ops().bind_topk_pools(s, 512, out.clone(), None)
+    held = [weakref.ref(t) for t in call.keep]
+    assert len(held) == 3                       # scores, pool_ids, the workspace made for the call
+    gc.collect()
+    junk = [torch.full((1 << 18,), -7, dtype=torch.int32, device="cuda") for _ in range(32)]
+    for _ in range(2):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(call.keep[1], ref)
+    assert all(h() is not None for h in held)
+    del call, junk
+    gc.collect()
+    assert held[2]() is None                    # the call's own workspace goes with it
