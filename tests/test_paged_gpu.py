@@ -65,7 +65,7 @@ def test_paged_bf16_matches_contiguous_bitwise_and_oracle(Hm, W, ps):
     assert torch.equal(lse, c_lse)
 
 
-@pytest.mark.parametrize("Hm,W,ps", [(64, 2048, 64), (16, 64, 32), (64, 700, 16)])
+@pytest.mark.parametrize("Hm,W,ps", [(64, 2048, 64), (16, 64, 32), (64, 700, 16), (128, 300, 1), (32, 129, 8)])
 def test_paged_fp8_matches_oracle(Hm, W, ps):
     B, T, Q = 3, 4096, 4
     kv, q, row_seq, tok = _case(B, T, Hm, Q, W, seed=3 * Hm + W + ps)
