@@ -139,16 +139,33 @@ __device__ __forceinline__ void block_stats(const uint32_t (&hi)[KPT], TkShared<
     sh.red[wave][2] = b;
   }
   __syncthreads();
-  n = 0;
-  mx = 0;
-  b = 0;
+  if constexpr (TkShared<NT>::NW > 8) {
+    // lane w of every wave takes wave w's partials and the wave reductions
+    // combine them: three registers, where reading all 16 waves' partials at
+    // once held 48 and pushed the 32-key kernel into spills (the histogram
+    // loop then reloaded its key mask from scratch for every key)
+    uint32_t c2 = 0, a2 = 0, b2 = 0;
+    if (lane < TkShared<NT>::NW) {
+      c2 = sh.red[lane][0];
+      a2 = sh.red[lane][1];
+      b2 = sh.red[lane][2];
+    }
+    n = __builtin_amdgcn_readlane(wave_incl_sum(c2), 63);
+    mx = wave_max_u32(a2);
+    mn = ~wave_max_u32(b2);
+  } else {
+    // up to 8 waves: every lane reads all the partials (shorter latency)
+    n = 0;
+    mx = 0;
+    b = 0;
 #pragma unroll
-  for (int w = 0; w < TkShared<NT>::NW; ++w) {
-    n += sh.red[w][0];
-    mx = max(mx, sh.red[w][1]);
-    b = max(b, sh.red[w][2]);
+    for (int w = 0; w < TkShared<NT>::NW; ++w) {
+      n += sh.red[w][0];
+      mx = max(mx, sh.red[w][1]);
+      b = max(b, sh.red[w][2]);
+    }
+    mn = ~b;
   }
-  mn = ~b;
 }
 
 // Wave 0: scans the histogram from the highest bin down and finds the bin where
