@@ -36,6 +36,7 @@
 
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
+#include "dsa_select.hpp"
 
 namespace dsa {
 
@@ -398,17 +399,40 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // several sequences in one workgroup take one pass per sequence.  (Measured
 // on the 4096-row chunk: 1.61 ms; four waves with two rows each, and the
 // 32x32x16 MFMA shape over pairs of tiles, were both slower.)
+//
+// With FILTER the scores are not stored: each wave keeps its row's candidate
+// keys (the top-k order keys of score and pool index) over its workgroup's
+// pool range in a list of fo.cap keys, leaving out the pools that score below
+// its threshold (dsa_select.hpp: such a key has K larger keys in the row).
+// A list that could not take the next stage is shrunk by a radix select that
+// raises the threshold; the waves publish their list lengths in LDS at every
+// stage, and when one list is full every wave whose list holds more than the
+// target shrinks it in the same stage, so that the shrinks overlap rather
+// than each holding the workgroup at the stage barrier (measured on the
+// prefill chunk's scores + top-k, same run: 1.89 -> 1.80 ms).  The list of row r and
+// pool range x is fo.keys[(r * gridDim.x + x) * fo.cap ..], its length
+// fo.counts[r * gridDim.x + x]; a top-k over the lists gives the row's K
+// largest keys.  The scores themselves are those of the storing kernel, bit
+// for bit.
 constexpr int kGemmWaves = 8;
 constexpr int kGemmStage = 16;  // tiles per stage (two per wave)
 
-template <int NH>
+struct FilterOut {
+  uint64_t* keys;    // [Q, ranges, cap] candidate keys
+  uint32_t* counts;  // [Q, ranges] list lengths
+  int cap;           // keys per list: >= K + 512 (room for one stage after a shrink)
+  int K;             // keys the row's selection keeps
+  int target;        // a shrink keeps at most this many keys (exactly K at the last bit)
+};
+
+template <int NH, bool FILTER>
 __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     const uint16_t* __restrict__ q, const float* __restrict__ w, float scale,
     const uint16_t* __restrict__ k_pool, const int32_t* __restrict__ pool_start,
     const uint8_t* __restrict__ pool_valid, const float* __restrict__ gamma,
     const float* __restrict__ beta, float eps, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_pos, int Q, int B, int P_max, int kp, int tiles_per_wg,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, FilterOut fo) {
   constexpr int H = NH * 16;
   constexpr size_t kStageBytes = 8 * H * kIsLd * 2 * 2 + 8 * H * 4 * 2;  // ghi + glo + QB + W of 8 rows
   constexpr size_t kKeyBytes = 2 * kGemmStage * kTileElems * 2;          // two stages of key tiles
@@ -416,6 +440,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
   __shared__ float srs[2][kGemmStage * 16];  // scale / sigma per pool of a stage
   __shared__ int sseq[kGemmWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t shist[FILTER ? kGemmWaves : 1][256];  // list shrinks
+  __shared__ uint32_t sfn[2][kGemmWaves];  // FILTER: list lengths after the appends of a stage (by parity)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
@@ -446,6 +472,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
       stage_row_store(rin, ghi[rr], glo[rr], sQB[rr], sW[rr], u - rr * H * 8);
     }
     if (lane == 0) sseq[wave] = ok ? b_row : -1;
+    if (FILTER && lane == 0) sfn[0][wave] = sfn[1][wave] = 0;
     __syncthreads();
   }
   bf16x8 ahi[NH][4], alo[NH][4];
@@ -460,6 +487,11 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
   __syncthreads();  // the staging area is reused for the key tiles
   uint16_t (*skeys)[kGemmStage][kTileElems] = reinterpret_cast<uint16_t (*)[kGemmStage][kTileElems]>(lds);
   const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  // FILTER: this wave's candidate list (length, threshold)
+  uint64_t* fbuf = FILTER && rok ? fo.keys + (size_t(r) * gridDim.x + blockIdx.x) * size_t(fo.cap) : nullptr;
+  uint32_t fn = 0;
+  uint64_t fthr = 0;
+  float fthr_s = -INFINITY;  // the score of fthr's hi: hi >= fthr's hi exactly when the score is >= this
 
   for (int i8 = 0; i8 < kGemmWaves; ++i8) {
     const int b = sseq[i8];
@@ -470,7 +502,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     const uint16_t* kseq = k_pool + size_t(b) * P_tiles * kTileElems;
     const int start0 = pool_start[size_t(b) * P_max];
     const long last_ok = long(pos) - (kp - 1) - start0;
-    float* srow = scores + size_t(r) * P_max;
+    float* srow = FILTER ? nullptr : scores + size_t(r) * P_max;
     // this wave's tile of stage s: keys into registers (and the validity of
     // the pools this lane stores in stage s)
     constexpr int TW = kGemmStage / kGemmWaves;  // tiles per wave and stage
@@ -525,6 +557,23 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     __syncthreads();
     for (int s = 0; s < nstage; ++s) {
       const int buf = s & 1;
+      if constexpr (FILTER) {
+        // a list that could not take this stage's candidates is shrunk first
+        // (before the next stage's keys are requested: their registers are
+        // free here)
+        // when any wave's list is full, every wave whose list holds more than
+        // the target shrinks it now, so that the shrinks of a workgroup's
+        // waves overlap instead of each holding the others at the barrier
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < kGemmWaves; ++i) mx = max(mx, sfn[(s + 1) & 1][i]);
+        if (mine && mx > uint32_t(fo.cap - kGemmStage * 16) && fn > uint32_t(fo.target)) {
+          const uint64_t t = list_compact(fbuf, fn, uint32_t(fo.K), uint32_t(fo.target), shist[wave]);
+          fthr = t > fthr ? t : fthr;
+          // (a threshold below the key of -FLT_MAX stands for no score: keep all)
+          fthr_s = uint32_t(fthr >> 32) < 0x00800000u ? -INFINITY : key_float(uint32_t(fthr >> 32));
+        }
+      }
       if (s + 1 < nstage) fetch(s + 1);  // in flight while stage s is computed
       if (mine) {
         float mine_sc[NU];
@@ -572,10 +621,33 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
             for (int mb = 0; mb < NH; ++mb) cur[mb] = nxt[mb];
           }
         }
+        if constexpr (FILTER) {
+          // append the candidates whose score reaches the threshold's (a
+          // superset of the keys >= the threshold: the score map is
+          // monotone); at most 256, and the list has room for them.  The keys
+          // are formed only when some lane keeps one.
+          uint32_t add = 0;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
-          if (p < P_max) srow[p] = (vcur[u] != 0 && long(p) * kp <= last_ok) ? mine_sc[u] : -INFINITY;
+          for (int u = 0; u < NU; ++u) {
+            const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+            const bool keep = p < P_max && vcur[u] != 0 && long(p) * kp <= last_ok && mine_sc[u] >= fthr_s &&
+                              mine_sc[u] > -INFINITY;
+            const uint64_t m = __ballot(keep);
+            if (m) {
+              const uint32_t at = fn + add + lane_rank(m);
+              if (keep && at < uint32_t(fo.cap))  // always in range: a shrink leaves <= cap - 256
+                fbuf[at] = (uint64_t(score_key(mine_sc[u])) << 32) | (0xffffffffu - uint32_t(p));
+              add += uint32_t(__builtin_popcountll(m));
+            }
+          }
+          fn += add;
+          if (lane == 0) sfn[s & 1][wave] = fn;
+        } else {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+            if (p < P_max) srow[p] = (vcur[u] != 0 && long(p) * kp <= last_ok) ? mine_sc[u] : -INFINITY;
+          }
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -587,10 +659,14 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
       __syncthreads();
     }
   }
-  // rows naming no sequence: -inf throughout
-  if (rok && !ok) {
-    for (int t = tb; t < te; ++t)
-      if (t * 16 + ln < P_max && kg == 0) scores[size_t(r) * P_max + t * 16 + ln] = -INFINITY;
+  if constexpr (FILTER) {
+    if (rok && lane == 0) fo.counts[size_t(r) * gridDim.x + blockIdx.x] = fn;  // 0 for rows naming no sequence
+  } else {
+    // rows naming no sequence: -inf throughout
+    if (rok && !ok) {
+      for (int t = tb; t < te; ++t)
+        if (t * 16 + ln < P_max && kg == 0) scores[size_t(r) * P_max + t * 16 + ln] = -INFINITY;
+    }
   }
 }
 
@@ -672,6 +748,49 @@ static int stream_tiles(int Q, int P_max) {
   return 1;
 }
 
+// Prefill launch shape: 8 rows per workgroup; pool ranges of whole stages so
+// that the grid has about 512 workgroups (two rounds over the CUs at one
+// workgroup per CU), at most max_nx ranges per row.
+static void gemm_grid(int Q, int P_max, int max_nx, int& nx, int& tiles_per_wg) {
+  const int batches = ceil_div(Q, kGemmWaves);
+  const int ptiles = pool_tiles(P_max);
+  int lim = ceil_div(ptiles, kGemmStage);
+  if (lim > max_nx) lim = max_nx;
+  nx = ceil_div(512, batches);
+  if (nx > lim) nx = lim;
+  if (nx < 1) nx = 1;
+  tiles_per_wg = ceil_div(ceil_div(ptiles, nx), kGemmStage) * kGemmStage;
+  nx = ceil_div(ptiles, tiles_per_wg);
+}
+
+int filter_supported(int Q, int H, int D, int dtype) {
+  return dtype == DSA_BF16 && D == 128 && (H == 16 || H == 32) && Q > 64 && ceil_div(Q, kGemmWaves) <= 65535;
+}
+
+int filter_ranges(int Q, int P_max, int max_ranges) {
+  int nx, tpw;
+  gemm_grid(Q, P_max, max_ranges, nx, tpw);
+  return nx;
+}
+
+int index_scores_filter(const void* q, const float* w, float scale, const void* k_pool, const int32_t* pool_start,
+                        const uint8_t* pool_valid, const float* ln_gamma, const float* ln_beta, float ln_eps,
+                        const int32_t* row_seq, const int32_t* row_pos, int Q, int H, int B, int P_max, int kpool,
+                        int K, int cap, int max_ranges, uint64_t* keys, uint32_t* counts, hipStream_t s) {
+  int nx, tiles_per_wg;
+  gemm_grid(Q, P_max, max_ranges, nx, tiles_per_wg);
+  dim3 g(nx, ceil_div(Q, kGemmWaves));
+  const FilterOut fo{keys, counts, cap, K, K + (cap - kGemmStage * 16 - K) / 2};
+#define DSA_IS_FILTER(NH)                                                                                   \
+  hipLaunchKernelGGL((index_scores_gemm<NH, true>), g, dim3(kGemmWaves * 64), 0, s, (const uint16_t*)q, w, scale, \
+                     (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq, row_pos, \
+                     Q, B, P_max, kpool, tiles_per_wg, nullptr, fo)
+  if (H == 32) DSA_IS_FILTER(2);
+  else DSA_IS_FILTER(1);
+#undef DSA_IS_FILTER
+  return launch_status();
+}
+
 }  // namespace dsa
 
 using namespace dsa;
@@ -711,23 +830,16 @@ extern "C" int dsa_index_scores(const void* q, const float* w, float scale, cons
 #undef DSA_IS_STREAM
       return launch_status();
     }
-    // prefill kernel: 8 rows per workgroup; pool ranges (whole stages) so that
-    // the grid has about 512 workgroups, two rounds over the CUs at one
-    // workgroup per CU
+    // prefill kernel (launch shape: gemm_grid)
     const int batches = ceil_div(Q, kGemmWaves);
     if (batches > 65535) return DSA_ERR_UNSUPPORTED;
-    const int ptiles = pool_tiles(P_max);
-    const int max_nx = ceil_div(ptiles, kGemmStage);
-    int nx = ceil_div(512, batches);
-    if (nx > max_nx) nx = max_nx;
-    if (nx < 1) nx = 1;
-    const int tiles_per_wg = ceil_div(ceil_div(ptiles, nx), kGemmStage) * kGemmStage;
-    nx = ceil_div(ptiles, tiles_per_wg);
+    int nx, tiles_per_wg;
+    gemm_grid(Q, P_max, INT_MAX, nx, tiles_per_wg);
     dim3 g(nx, batches);
-#define DSA_IS_GEMM(NH)                                                                              \
-  hipLaunchKernelGGL((index_scores_gemm<NH>), g, dim3(kGemmWaves * 64), 0, s, (const uint16_t*)q, w, scale, \
-                     (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,   \
-                     row_pos, Q, B, P_max, kpool, tiles_per_wg, scores)
+#define DSA_IS_GEMM(NH)                                                                                    \
+  hipLaunchKernelGGL((index_scores_gemm<NH, false>), g, dim3(kGemmWaves * 64), 0, s, (const uint16_t*)q, w, scale, \
+                     (const uint16_t*)k_pool, pool_start, pool_valid, ln_gamma, ln_beta, ln_eps, row_seq,         \
+                     row_pos, Q, B, P_max, kpool, tiles_per_wg, scores, FilterOut{})
     if (H == 32) DSA_IS_GEMM(2);
     else DSA_IS_GEMM(1);
 #undef DSA_IS_GEMM

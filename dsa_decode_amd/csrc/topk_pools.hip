@@ -34,26 +34,12 @@
 // and else from the full lists.  Otherwise a second launch merges.
 #include "dsa_common.hpp"
 #include "dsa_host.hpp"
+#include "dsa_select.hpp"
 
 namespace dsa {
 
 constexpr int kTkMaxChunk = 32768;  // keys per workgroup (1024 threads x 32)
 constexpr int kTkMaxSplit = 16;     // chunks merged by one merge launch
-
-// Order-preserving map of a score to a nonzero u32; 0 for a non-candidate
-// (-inf, and NaN, which the interface excludes).
-// Written with selects only, so that a loop of them stays branch-free.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = (u << 1) == 0u ? 0u : u;  // -0 -> +0
-  const uint32_t k = int32_t(u) < 0 ? ~u : (u | 0x80000000u);
-  return f > -INFINITY ? k : 0u;
-}
-
-// The score a key stands for (inverse of score_key for candidates).
-__device__ __forceinline__ float key_float(uint32_t k) {
-  return __uint_as_float(int32_t(k) < 0 ? (k & 0x7fffffffu) : ~k);
-}
 
 constexpr int kDig = 11;              // radix digit width
 constexpr int kBins = 1 << kDig;      // 2048 bins, 32 per lane of the scanning wave
@@ -65,40 +51,6 @@ constexpr int kRankCap = 256;         // largest bin that is ordered by pairwise
 template <int N>
 constexpr int first_pass_bins() {
   return N <= 2048 ? 512 : (N <= 4096 ? 1024 : kBins);
-}
-
-// ---------------------------------------------------------------- wave helpers
-// v from lane (lane - n) of the same row of 16 lanes, 0 for the first n lanes
-template <int N>
-__device__ __forceinline__ uint32_t row_shr(uint32_t v) {
-  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x110 + N, 0xF, 0xF, true));
-}
-
-// inclusive prefix sum over the wave: DPP shifts within rows of 16, then the
-// row broadcasts (lane 15 of a row into the next row, lane 31 into rows 2, 3)
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
-  v += row_shr<1>(v);
-  v += row_shr<2>(v);
-  v += row_shr<4>(v);
-  v += row_shr<8>(v);
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return v;
-}
-
-// maximum over the wave (wave-uniform result)
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, row_shr<1>(v));
-  v = max(v, row_shr<2>(v));
-  v = max(v, row_shr<4>(v));
-  v = max(v, row_shr<8>(v));
-  return max(max(uint32_t(__builtin_amdgcn_readlane(v, 15)), uint32_t(__builtin_amdgcn_readlane(v, 31))),
-             max(uint32_t(__builtin_amdgcn_readlane(v, 47)), uint32_t(__builtin_amdgcn_readlane(v, 63))));
-}
-
-// number of set bits of m below this lane
-__device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
 
 template <int NT>
@@ -462,11 +414,14 @@ __device__ __forceinline__ void expand_pad(int row, int K, const ExpandArgs& ex)
 // .. of the scores; otherwise the nsplit_in chunk winner lists of the row) ->
 // its K largest keys, written to chunk slot c of keys_out (partial) or sorted
 // to pool_ids (FINAL).  nchunk: chunk slots per row of keys_out.
+// With lcounts (and FROM_SCORES false) the input is instead the row's
+// nsplit_in candidate lists of the filtering score pass, lcap keys apart (lcap
+// a power of two), list l holding lcounts[row * nsplit_in + l] keys.
 template <int NT, int KPT, bool FROM_SCORES, bool FINAL>
 __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int nchunk, const float* __restrict__ scores,
                            const uint64_t* __restrict__ keys_in, int P, int chunk, int nsplit_in, int K,
                            uint64_t* __restrict__ keys_out, int32_t* __restrict__ pool_ids,
-                           const ExpandArgs& ex) {
+                           const ExpandArgs& ex, const uint32_t* __restrict__ lcounts = nullptr, int lcap = 0) {
   static_assert(KPT <= 32, "selection masks are 32-bit");
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t hi[KPT];
@@ -488,6 +443,29 @@ __device__ __forceinline__ void topk_block(TkShared<NT>& sh, int row, int c, int
       uint32_t in = base + j * NT + tid < end ? 0xffffffffu : 0u;
       asm volatile("" : "+v"(in));
       hi[j] = score_key(v[j]) & in;
+    }
+  } else if (lcounts) {
+    // candidate lists: only each list's first lcounts keys are loaded
+    const int n = nsplit_in * lcap;
+    const int lsh = __builtin_ctz(uint32_t(lcap));
+    const uint64_t* src = keys_in + size_t(row) * n;
+    uint32_t len[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = j * NT + tid;
+      len[j] = i < n ? lcounts[size_t(row) * nsplit_in + (i >> lsh)] : 0u;
+    }
+    uint64_t k[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = j * NT + tid;
+      k[j] = uint32_t(i & (lcap - 1)) < len[j] ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      hi[j] = uint32_t(k[j] >> 32);  // 0 past a list's end
+      lo[j] = uint32_t(k[j]);
     }
   } else {
     // chunk winners published by other workgroups of this launch: agent-scope
@@ -758,13 +736,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   const uint64_t* __restrict__ keys_in,
                                                   int P, int chunk, int nsplit_in, int K,
                                                   uint64_t* __restrict__ keys_out,
-                                                  int32_t* __restrict__ pool_ids, ExpandArgs ex) {
+                                                  int32_t* __restrict__ pool_ids, ExpandArgs ex,
+                                                  const uint32_t* __restrict__ lcounts, int lcap) {
   __shared__ TkShared<NT> sh;
   const ExpandArgs exr = expand_for_row(ex, blockIdx.y);
   if constexpr (FINAL)
     if (ex.token_ids) expand_pad<NT>(blockIdx.y, K, ex);
   topk_block<NT, KPT, FROM_SCORES, FINAL>(sh, blockIdx.y, blockIdx.x, gridDim.x, scores, keys_in, P, chunk,
-                                          nsplit_in, K, keys_out, pool_ids, exr);
+                                          nsplit_in, K, keys_out, pool_ids, exr, lcounts, lcap);
 }
 
 // Split rows in one launch: workgroup (c, row) selects chunk c's K winners,
@@ -870,10 +849,10 @@ static_assert(DSA_TOPK_COUNTER_BYTES >= 65535 * sizeof(uint32_t), "one counter p
 template <int NT, bool FROM_SCORES, bool FINAL>
 static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, const uint64_t* keys_in,
                       int P, int chunk, int nsplit_in, int K, uint64_t* keys_out, int32_t* pool_ids,
-                      const ExpandArgs& ex) {
+                      const ExpandArgs& ex, const uint32_t* lcounts, int lcap) {
 #define DSA_TK(KPT)                                                                                \
   hipLaunchKernelGGL((topk_kernel<NT, KPT, FROM_SCORES, FINAL>), grid, dim3(NT), 0, s, scores,    \
-                     keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex)
+                     keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex, lcounts, lcap)
   switch (kpt) {
     case 1: DSA_TK(1); break;
     case 2: DSA_TK(2); break;
@@ -888,13 +867,31 @@ static void launch_tk(int kpt, dim3 grid, hipStream_t s, const float* scores, co
 template <bool FROM_SCORES, bool FINAL>
 static void launch_tk_nt(int nt, int kpt, dim3 grid, hipStream_t s, const float* scores,
                          const uint64_t* keys_in, int P, int chunk, int nsplit_in, int K,
-                         uint64_t* keys_out, int32_t* pool_ids, const ExpandArgs& ex) {
+                         uint64_t* keys_out, int32_t* pool_ids, const ExpandArgs& ex,
+                         const uint32_t* lcounts = nullptr, int lcap = 0) {
   if (nt == 256)
-    launch_tk<256, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
+    launch_tk<256, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex,
+                                       lcounts, lcap);
   else if (nt == 512)
-    launch_tk<512, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
+    launch_tk<512, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex,
+                                       lcounts, lcap);
   else
-    launch_tk<1024, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex);
+    launch_tk<1024, FROM_SCORES, FINAL>(kpt, grid, s, scores, keys_in, P, chunk, nsplit_in, K, keys_out, pool_ids, ex,
+                                        lcounts, lcap);
+}
+
+// The row's K largest keys from the candidate lists of the filtering score
+// pass (nseg lists of cap keys per row), sorted to pool ids and expanded.
+int topk_lists(const uint64_t* keys, const uint32_t* counts, int nseg, int cap, int Q, int P_max, int K,
+               int32_t* pool_ids, const int32_t* row_seq, const int32_t* pool_start, int B, int kpool,
+               int32_t* token_ids, int W, hipStream_t s) {
+  const ExpandArgs ex{row_seq, pool_start, B, P_max, kpool, token_ids, W};
+  int nt, kpt;
+  tk_shape(long(nseg) * cap, nt, kpt);
+  if (kpt > 32 || Q > 65535) return DSA_ERR_UNSUPPORTED;
+  launch_tk_nt<false, true>(nt, kpt, dim3(1, Q), s, nullptr, keys, P_max, 0, nseg, K, nullptr, pool_ids, ex, counts,
+                            cap);
+  return launch_status();
 }
 
 }  // namespace dsa

@@ -331,13 +331,25 @@ int dsa_sparse_mla_decode_noalloc(const void* q_lat, const void* kv, const int32
  * for many rows (a prefill chunk) without the [Q, P_max] score tensor.  Same
  * operations as those two calls ("Module glm5next_dsa", "Shape of the
  * pipeline": index_scores -> topk_pools -> expand_selection; see them for the
- * arguments): the rows are taken in blocks whose fp32 scores fit 64 MiB, each
- * block's scores written into the workspace and consumed by its top-k before
- * the next block, so pool_ids [Q, K] and token_ids [Q, W] are bit-identical to
- * the two calls while at most 64 MiB of scores exist at a time.
- *   workspace  dsa_index_topk_workspace_bytes(Q, P_max, K) bytes.  When rows
- *              are few enough for the top-k to split them, the workspace
- *              starts with the top-k counter block: its first
+ * arguments); pool_ids [Q, K] and token_ids [Q, W] are bit-identical to the
+ * two calls.  Two paths:
+ *   filtered     bf16 q and keys, D = 128, H = 16 or 32, Q > 64, when the
+ *                lists below fit (at most min(32768, P_max) slots per row,
+ *                256 MiB in all): the score kernel stores no scores.  Each
+ *                of its waves keeps, for one row and one pool range, a list
+ *                of the candidates that can still be among the row's K best
+ *                (one is left out only once K better ones of the same range
+ *                have been seen), and a top-k over the lists selects and
+ *                expands.  The lists hold 2048 keys of 8 bytes per row and
+ *                range for K <= 768 (64 MiB at Q = 4096, one range per row).
+ *   row-blocked  every other call: the rows are taken in blocks whose fp32
+ *                scores fit 64 MiB, each block's scores written into the
+ *                workspace and consumed by its top-k before the next block.
+ *   workspace  dsa_index_topk_workspace_bytes(Q, P_max, K) bytes: enough for
+ *              either path (the sizer does not know H, D or dtype).  No state
+ *              is kept in it between calls, except the top-k counter block
+ *              that it may start with (the row-blocked top-k uses it when it
+ *              splits rows; the filtered path leaves it untouched): its first
  *              DSA_TOPK_COUNTER_BYTES must be zero before the first use, and
  *              every call leaves them zero (as for dsa_topk_pools).
  * Every argument check of both stages is made before any launch.

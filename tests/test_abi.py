@@ -215,8 +215,14 @@ def test_streamed_index_topk_refuses_bad_arguments_and_sizes_workspace(lib):
     assert _streamed(lib, kpool=9, W=9 * 512) == DSA_ERR_UNSUPPORTED
     assert _streamed(lib, ws=None) == DSA_ERR_WORKSPACE
     assert _streamed(lib, ws_bytes=1 << 20) == DSA_ERR_WORKSPACE
-    # the prefill chunk: blocks of 512 rows, 64 MiB of scores, no top-k split
-    assert lib.dsa_index_topk_workspace_bytes(4096, 32768, 512) == 512 * 32768 * 4
+    # the prefill chunk: the larger of the filtered path's layout (the top-k
+    # counter block, one list of 2048 8-byte keys per row, the 4096 list
+    # lengths) and the row-blocked path's (blocks of 512 rows, 64 MiB of
+    # scores, no top-k split)
+    from dsa_decode_amd._lib import DSA_TOPK_COUNTER_BYTES
+    filtered = DSA_TOPK_COUNTER_BYTES + 4096 * 2048 * 8 + 4096 * 4
+    assert filtered > 512 * 32768 * 4
+    assert lib.dsa_index_topk_workspace_bytes(4096, 32768, 512) == filtered
     # few rows: one block, the split top-k's workspace (counter block first) plus the scores
     n = lib.dsa_index_topk_workspace_bytes(4, 65536, 512)
     assert n >= lib.dsa_topk_workspace_bytes(4, 65536, 512) + 4 * 65536 * 4
@@ -225,12 +231,19 @@ def test_streamed_index_topk_refuses_bad_arguments_and_sizes_workspace(lib):
 def test_streamed_workspace_covers_a_ragged_last_block(lib):
     # 1000 rows x 20000 pools: blocks of 832 rows (64 MiB / 80000 B, a multiple of 8)
     # and a last block of 168 rows, whose top-k splits the rows and needs the
-    # counter block; the workspace holds the larger of the two top-k needs
-    # (aligned to 256 B) and one block of scores
+    # counter block; the workspace holds the larger of that layout (the larger
+    # of the two top-k needs, aligned to 256 B, and one block of scores) and
+    # the filtered path's (125 workgroup rows give each row 5 pool ranges of
+    # 256 tiles: 5 lists of 2048 keys per row, 10240 slots <= 20000 pools)
+    from dsa_decode_amd._lib import DSA_TOPK_COUNTER_BYTES
     R, rem, P, K = 832, 168, 20000, 512
     tk = max(lib.dsa_topk_workspace_bytes(R, P, K), lib.dsa_topk_workspace_bytes(rem, P, K))
     assert lib.dsa_topk_workspace_bytes(rem, P, K) > 0
-    assert lib.dsa_index_topk_workspace_bytes(1000, P, K) == ((tk + 255) // 256) * 256 + R * P * 4
-    # rows that fit one block: all of them at once
+    blocked = ((tk + 255) // 256) * 256 + R * P * 4
+    filtered = DSA_TOPK_COUNTER_BYTES + 1000 * 5 * 2048 * 8 + 1000 * 5 * 4
+    assert lib.dsa_index_topk_workspace_bytes(1000, P, K) == max(blocked, filtered)
+    # 100 rows: the score kernel gives each row 40 pool ranges, whose lists
+    # (40 x 2048 slots) would outgrow the row's 20000 scores, so only the
+    # row-blocked layout counts: all rows in one block
     assert lib.dsa_index_topk_workspace_bytes(100, P, K) == \
         ((lib.dsa_topk_workspace_bytes(100, P, K) + 255) // 256) * 256 + 100 * P * 4

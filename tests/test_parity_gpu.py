@@ -715,15 +715,15 @@ def _streamed_vs_oracle(scores: np.ndarray, ids: np.ndarray, tok: np.ndarray, ro
     np.testing.assert_array_equal(tok[rows], ref_tok)
 
 
-@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3), (835, 20000, 2)])
+@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3), (835, 20000, 2), (100, 20000, 2)])
 def test_streamed_index_topk_bit_identical(Q, P, B):
-    # dsa_index_topk_pools_expand over row blocks of at most 64 MiB of scores
-    # gives the bits of dsa_index_scores + dsa_topk_pools_expand, and those of
-    # the oracle's top-k and expansion of the same scores: 2 blocks with a
-    # ragged last block that takes the split top-k (1000 x 20000), one block
-    # with the split top-k (decode rows), a small case, and 832 + 3 rows (the
-    # last block of 3 rows takes the decode score kernel while the others take
-    # the many-rows kernel)
+    # dsa_index_topk_pools_expand gives the bits of dsa_index_scores +
+    # dsa_topk_pools_expand, and those of the oracle's top-k and expansion of
+    # the same scores: 1000 and 835 rows take the filtered path (5 pool ranges
+    # per row, rows of two sequences in one workgroup; 835 leaves the last
+    # workgroup partial); 4 (decode rows: one block with the split top-k), 9
+    # and 100 rows (40 pool ranges per row would outgrow the scores) take the
+    # row-blocked path
     rng = np.random.default_rng(Q + P)
     H, D, kp, K = 32, 128, 4, 512
     W = K * kp + 3
@@ -758,10 +758,11 @@ def test_streamed_index_topk_bit_identical(Q, P, B):
 
 
 def test_streamed_index_topk_prefill_chunk_full_size():
-    # the prefill chunk (4096 rows x 32768 pools, forced ties at the cut): 8 row
-    # blocks of 512, bit-identical to the unfused calls and, on sampled rows
-    # (row 0, the block edges, row 4095), to the oracle's top-k and expansion of
-    # the GPU's scores
+    # the prefill chunk (4096 rows x 32768 pools, forced ties at the cut): the
+    # filtered path (one candidate list of 2048 keys per row), bit-identical to
+    # the unfused calls and, on sampled rows (row 0, row 4095 and rows of
+    # several workgroups), to the oracle's top-k and expansion of the GPU's
+    # scores
     d = wl_data_prefill()
     wl, ip = d["wl"], d["ip"]
     pc = scores_inputs(d, k_pool_override=synth.codebook_keys(wl))
@@ -773,7 +774,6 @@ def test_streamed_index_topk_prefill_chunk_full_size():
     rows = [0, 511, 512, 1023, 2047, 2048, 3000, 3583, 3584, 4095]
     s_rows = scores[rows].cpu().numpy()
     del scores
-    assert ops().dsa_index_topk_workspace_bytes(wl.Q, wl.P_max, wl.K) == 512 * wl.P_max * 4
     ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, wl.K, wl.W)
     torch.cuda.synchronize()
     assert torch.equal(ids_a, ids_b)
@@ -782,6 +782,87 @@ def test_streamed_index_topk_prefill_chunk_full_size():
     full[rows] = s_rows
     _streamed_vs_oracle(full, ids_b.cpu().numpy(), tok_b.cpu().numpy(), rows, ip["row_seq"].numpy(),
                         d["comp"]["pool_start"], wl.kp, wl.K, wl.W)
+
+
+def _shaped_rows_inputs(kind: str, Q: int, P: int, B: int, H: int, seed: int):
+    """Score-kernel inputs whose score rows take a chosen shape along the pool
+    index: "rising" (every pool scores above the ones before it, up to small
+    per-row wiggles: a candidate list keeps growing and is shrunk about every
+    other stage), "falling", "equal" (all pools of a row score the same: the
+    order is the pool index alone) and "codebook" (pooled keys drawn from 256
+    rows: ~128-fold ties, as in the prefill chunk)."""
+    rng = np.random.default_rng(seed)
+    D, kp = 128, 4
+    u = np.tile([1.0, -1.0], D // 2)            # zero-mean, orthogonal, |u|^2 = |v|^2 = D
+    v = np.tile([1.0, 1.0, -1.0, -1.0], D // 4)
+    if kind in ("rising", "falling"):
+        t = np.arange(P) / (P - 1)
+        theta = (np.pi / 2) * (1 - t if kind == "rising" else t)
+        keys = np.cos(theta)[:, None] * u + np.sin(theta)[:, None] * v
+    elif kind == "equal":
+        keys = np.broadcast_to(u, (P, D))
+    else:
+        keys = rng.standard_normal((256, D))[rng.integers(0, 256, P)]
+    k_pool = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(keys, (B, P, D)), np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy((u + 0.1 * rng.standard_normal((Q, H, D))).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((0.5 + rng.random((Q, H))).astype(np.float32) / H)
+    gamma = torch.ones(D, dtype=torch.float32)
+    beta = torch.zeros(D, dtype=torch.float32)
+    ps = np.broadcast_to(7 + kp * np.arange(P, dtype=np.int32), (B, P)).copy()
+    pv = (rng.random((B, P)) > 0.02).astype(np.uint8)
+    row_seq = np.sort(rng.integers(0, B, Q)).astype(np.int32)
+    # most rows see (nearly) every pool; a few see fewer than K candidates
+    row_pos = (7 + kp * P - 1 - rng.integers(0, 400, Q)).astype(np.int32)
+    row_pos[rng.integers(0, Q, 6)] = 7 + kp * rng.integers(0, 300, 6)
+    args = (dev(q), dev(w), D ** -0.5, dev(tile_pool_cache(k_pool)), dev(torch.from_numpy(ps)),
+            dev(torch.from_numpy(pv)), dev(gamma), dev(beta), 1e-5, dev(torch.from_numpy(row_seq)),
+            dev(torch.from_numpy(row_pos)), kp)
+    return args, row_seq, ps, kp
+
+
+@pytest.mark.parametrize("kind,Q,P,H,K", [("rising", 4096, 32768, 32, 512), ("equal", 2048, 32768, 32, 512),
+                                          ("falling", 1024, 32768, 16, 100), ("codebook", 2048, 32768, 32, 512),
+                                          ("rising", 1024, 32768, 32, 1024), ("equal", 515, 20000, 16, 8)])
+def test_filtered_index_topk_shaped_score_rows(kind, Q, P, H, K):
+    # the filtered path of dsa_index_topk_pools_expand (bf16, D = 128, H = 16
+    # or 32, Q > 64: each score-kernel wave keeps a list of its row's
+    # candidates over its pool range and shrinks it as it fills) gives the bits
+    # of dsa_index_scores + dsa_topk_pools_expand and the oracle's top-k and
+    # expansion of the same scores.  The cases cover 1 (4096 rows), 2, 4 and 8
+    # pool ranges per row (515 rows, the last workgroup partial), K = 8 .. 1024
+    # (lists of 2048 and 4096 keys), and score rows that force shrinks every
+    # other stage (rising), ties through the index bits (equal, codebook)
+    args, row_seq, ps, kp = _shaped_rows_inputs(kind, Q, P, 2, H, seed=Q + K)
+    W = K * kp + 5
+    scores = ops().dsa_index_scores(*args)
+    ids_a, tok_a = ops().dsa_topk_pools_expand(scores, K, args[9], args[4], kp, W)
+    ws = ops().topk_workspace(ops().dsa_index_topk_workspace_bytes(Q, P, K))
+    for _ in range(2):   # twice on one workspace: nothing of the first call's lists is read
+        ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, K, W, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids_a, ids_b)
+        assert torch.equal(tok_a, tok_b)
+    rng = np.random.default_rng(Q)
+    rows = sorted(set([0, Q - 1] + rng.integers(0, Q, 6).tolist()))
+    s_np = scores[rows].cpu().numpy()
+    full = np.zeros((Q, P), np.float32)
+    full[rows] = s_np
+    _streamed_vs_oracle(full, ids_b.cpu().numpy(), tok_b.cpu().numpy(), rows, row_seq, ps, kp, K, W)
+    # the rows have the intended shape
+    fin = [r[np.isfinite(r)] for r in s_np]
+    if kind == "equal":
+        assert all(len(f) and np.all(f == f[0]) for f in fin)
+        ids = ids_b.cpu().numpy()
+        for i, r in enumerate(rows):   # then the first K candidates by pool index
+            cand = np.flatnonzero(np.isfinite(s_np[i]))[:K]
+            np.testing.assert_array_equal(ids[r][:len(cand)], cand)
+    elif kind in ("rising", "falling"):
+        # rank correlation with the pool index (bf16 keys make the rows
+        # staircases with small steps back, so not every step is up)
+        for f in fin:
+            if len(f) > 1000:
+                rho = np.corrcoef(np.argsort(np.argsort(f, kind="stable")), np.arange(len(f)))[0, 1]
+                assert rho > 0.95 if kind == "rising" else rho < -0.95
 
 
 def test_bound_call_keeps_its_buffers_and_sizes_its_workspace():
