@@ -610,13 +610,17 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 def bench_prefill(args) -> int:
     """The prefill chunk (4096 query rows at the end of a 131072-token sequence,
-    32768 pools): dsa_index_scores over every (row, pool) pair on the matrix
-    cores, then dsa_topk_pools_expand, then dsa_sparse_mla_decode over the
-    selected tokens (the many-rows path).  Inputs follow the workload recipe: q on
+    32768 pools).  A step is dsa_index_topk_pools_expand (index scores over
+    every (row, pool) pair on the matrix cores, each row's candidates kept in a
+    list instead of a score tensor, then top-k and expansion over the lists)
+    followed by dsa_sparse_mla_decode over the selected tokens (the many-rows
+    path).  The unfused dsa_index_scores + dsa_topk_pools_expand (same outputs,
+    bit for bit) are timed beside it.  Inputs follow the workload recipe: q on
     the 1/8 grid, pooled keys from a 256-row codebook on the 1/8 grid (exact
     score ties straddle the cut), pool metadata from dsa_kpool_compress over
-    the synthetic tokens.  The score kernel is timed per launch with events;
-    its roofline uses the algorithmic flops (2*H*D per candidate pair)."""
+    the synthetic tokens.  Stages are timed per launch with events; the
+    rooflines use the algorithmic flops (2*H*D per candidate pair for the
+    scores, 4*Hm*Dl per listed id for the MLA)."""
     import numpy as np
     import torch
 
@@ -650,68 +654,77 @@ def bench_prefill(args) -> int:
     last = np.sort(ps[pv] + wl.kp - 1)
     pairs = int(np.searchsorted(last, ip["row_pos"].numpy().astype(np.int64), side="right").sum())
     flops = 2 * wl.H * wl.D * pairs
+    st_ws = ops.topk_workspace(ops.dsa_index_topk_workspace_bytes(Q, P, K))
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        stc = ops.bind_index_topk_pools_expand(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"],
+                                               gamma, beta, ip["eps"], row_seq, row_pos, wl.kp, K, ids, tok, st_ws)
+        ml = ops.bind_sparse_mla_decode(q_lat, kv, row_seq, tok, mi["sm_scale"], out, lse, mla_ws)
+        for _ in range(args.warmup):
+            stc()
+            ml()
+        stream.synchronize()
+        tev = TimingEvents(3 * args.steps)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            tev.record(3 * i, sh)
+            stc()
+            tev.record(3 * i + 1, sh)
+            ml()
+            tev.record(3 * i + 2, sh)
+        stream.synchronize()
+        t1 = time.perf_counter()
+    fused_us = float(np.mean([tev.elapsed_us(3 * i, 3 * i + 1) for i in range(args.steps)]))
+    mla_us = float(np.mean([tev.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    tev.close()
+    # the unfused stages on the same inputs: dsa_index_scores into a [Q, P]
+    # tensor, then dsa_topk_pools_expand; their pool ids must be the step's
+    u_ids = torch.empty_like(ids)
+    u_tok = torch.empty_like(tok)
     with torch.cuda.stream(stream):
         sc = ops.bind_index_scores(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"], gamma, beta,
                                    ip["eps"], row_seq, row_pos, wl.kp, scores)
-        tk = ops.bind_topk_pools_expand(scores, K, ids, row_seq, comp["pool_start"], wl.kp, tok, tk_ws)
-        ml = ops.bind_sparse_mla_decode(q_lat, kv, row_seq, tok, mi["sm_scale"], out, lse, mla_ws)
-        for _ in range(args.warmup):
-            sc()
-            tk()
-            ml()
+        tk = ops.bind_topk_pools_expand(scores, K, u_ids, row_seq, comp["pool_start"], wl.kp, u_tok, tk_ws)
+        sc()
+        tk()
         stream.synchronize()
-        tev = TimingEvents(4 * args.steps)
-        sh = stream.cuda_stream
-        t0 = time.perf_counter()
+        uev = TimingEvents(3 * args.steps)
         for i in range(args.steps):
-            tev.record(4 * i, sh)
+            uev.record(3 * i, sh)
             sc()
-            tev.record(4 * i + 1, sh)
+            uev.record(3 * i + 1, sh)
             tk()
-            tev.record(4 * i + 2, sh)
-            ml()
-            tev.record(4 * i + 3, sh)
+            uev.record(3 * i + 2, sh)
         stream.synchronize()
-        t1 = time.perf_counter()
-    # the same scores + top-k + expand streamed over row blocks (at most 64 MiB of
-    # scores at a time), timed separately on the same stream
-    st_ws = ops.topk_workspace(ops.dsa_index_topk_workspace_bytes(Q, P, K))
-    st_ids = torch.empty((Q, K), dtype=torch.int32, device="cuda")
-    st_tok = torch.empty((Q, W), dtype=torch.int32, device="cuda")
-    with torch.cuda.stream(stream):
-        stc = ops.bind_index_topk_pools_expand(q, w, ip["scale"], k_pool, comp["pool_start"], comp["pool_valid"],
-                                               gamma, beta, ip["eps"], row_seq, row_pos, wl.kp, K, st_ids, st_tok,
-                                               st_ws)
-        stc()
-        stream.synchronize()
-        sev = TimingEvents(2 * args.steps)
-        for i in range(args.steps):
-            sev.record(2 * i, stream.cuda_stream)
-            stc()
-            sev.record(2 * i + 1, stream.cuda_stream)
-        stream.synchronize()
-    streamed_us = float(np.mean([sev.elapsed_us(2 * i, 2 * i + 1) for i in range(args.steps)]))
-    sev.close()
-    score_us = float(np.mean([tev.elapsed_us(4 * i, 4 * i + 1) for i in range(args.steps)]))
-    topk_us = float(np.mean([tev.elapsed_us(4 * i + 1, 4 * i + 2) for i in range(args.steps)]))
-    mla_us = float(np.mean([tev.elapsed_us(4 * i + 2, 4 * i + 3) for i in range(args.steps)]))
-    tev.close()
+    if not (torch.equal(u_ids, ids) and torch.equal(u_tok, tok)):
+        raise RuntimeError("the fused and the unfused scores -> top-k disagree")
+    score_us = float(np.mean([uev.elapsed_us(3 * i, 3 * i + 1) for i in range(args.steps)]))
+    topk_us = float(np.mean([uev.elapsed_us(3 * i + 1, 3 * i + 2) for i in range(args.steps)]))
+    uev.close()
     ms = (t1 - t0) * 1e3 / args.steps
     achieved = flops / (score_us * 1e-6) / 1e12
+    fused_achieved = flops / (fused_us * 1e-6) / 1e12
     # sparse MLA: per (row, listed id) 2*Hm*Dl flops for the logits and as many for the values
     listed = int((tok >= 0).sum().item())
     mla_flops = 4 * wl.Hm * wl.Dl * listed
     mla_achieved = mla_flops / (mla_us * 1e-6) / 1e12
     kernels = {
+        # the step's two stages: the filtering score kernel + the top-k over
+        # its lists (one entry point, timed together), and the sparse MLA
+        "index_topk_pools_expand": {"launch_us": round(fused_us, 2), "achieved": round(fused_achieved, 1),
+                                    "frac": round(fused_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "algorithmic_flops": flops,
+                                    "kernels": "index_scores_gemm<2, true> + topk_kernel<512, 4, false, true>"},
+        "mla_rows64w8_mfma": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
+                              "frac": round(mla_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": mla_flops,
+                              "listed_ids": listed},
+        # the unfused score kernel (reference, not in the step)
         "index_scores_gemm": {"launch_us": round(score_us, 2), "achieved": round(achieved, 1),
                               "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
-        "mla_rows64w8_mfma": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
-                          "frac": round(mla_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": mla_flops,
-                          "listed_ids": listed},
     }
-    dom = "index_scores_gemm" if score_us >= mla_us else "mla_rows64w8_mfma"
+    dom = "index_topk_pools_expand" if fused_us >= mla_us else "mla_rows64w8_mfma"
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, ip, mi, comp, k_pool, args.cpu_seconds)
     line = {
         "metric": "DSA prefill chunk (index_scores + top-k + expand + sparse MLA) chunks/s; % MFMA roofline",
@@ -722,9 +735,8 @@ def bench_prefill(args) -> int:
                                "sequence, kpool 4 (32768 pools), 32 index heads x 128, select_k 512, bf16, "
                                "q and keys on the 1/8 grid (forced ties)",
                    "rows": Q, "pools": P, "select_k": K},
-        "stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2),
-                      "sparse_mla_decode": round(mla_us, 2)},
-        "streamed_index_topk_us": round(streamed_us, 2),
+        "stages_us": {"index_topk_pools_expand": round(fused_us, 2), "sparse_mla_decode": round(mla_us, 2)},
+        "unfused_stages_us": {"index_scores": round(score_us, 2), "topk_pools_expand": round(topk_us, 2)},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kernels[dom]["achieved"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
                      "traffic": None, "launch_us": kernels[dom]["launch_us"],

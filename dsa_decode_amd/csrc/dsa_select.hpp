@@ -96,30 +96,14 @@ constexpr int kListChunk = 16;  // keys per lane per read round of a list
 // stay in list order.  hist: this wave's 256 LDS counters.  Wave-uniform
 // control flow; every lane returns the same threshold and n.
 __device__ __forceinline__ uint64_t list_compact(uint64_t* buf, uint32_t& n, uint32_t K, uint32_t target,
-                                              uint32_t* hist) {
+                                              uint32_t* hist, uint64_t& lor, uint64_t& land) {
   const int lane = threadIdx.x & 63;
   const uint32_t cnt_in = n;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's appends have left it
-  // bits shared by every listed key: OR and AND over the list
-  uint32_t oh = 0, ol = 0, ah = ~0u, al = ~0u;
-  for (uint32_t c0 = 0; c0 < cnt_in; c0 += 64 * kListChunk) {
-    uint64_t k[kListChunk];
-#pragma unroll
-    for (int j = 0; j < kListChunk; ++j) {
-      const uint32_t i = c0 + j * 64 + lane;
-      k[j] = i < cnt_in ? list_load(buf + i) : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < kListChunk; ++j) {
-      const bool in = c0 + j * 64 + lane < cnt_in;
-      oh |= uint32_t(k[j] >> 32);
-      ol |= uint32_t(k[j]);
-      ah &= in ? uint32_t(k[j] >> 32) : ~0u;
-      al &= in ? uint32_t(k[j]) : ~0u;
-    }
-  }
-  const uint64_t kor = (uint64_t(wave_or_u32(oh)) << 32) | wave_or_u32(ol);
-  const uint64_t kand = ~((uint64_t(wave_or_u32(~ah)) << 32) | wave_or_u32(~al));
+  // bits shared by every listed key: the OR and AND of the lanes' running
+  // OR / AND of the keys they listed
+  const uint64_t kor = (uint64_t(wave_or_u32(uint32_t(lor >> 32))) << 32) | wave_or_u32(uint32_t(lor));
+  const uint64_t kand = ~((uint64_t(wave_or_u32(~uint32_t(land >> 32))) << 32) | wave_or_u32(~uint32_t(land)));
   int h = 63 - __builtin_clzll(kor ^ kand);  // keys are distinct and n >= 2: some bit differs
   uint64_t pre = h >= 63 ? 0ull : (kor & ~((2ull << h) - 1ull));
   uint32_t need = K, above_tot = 0;
@@ -174,6 +158,8 @@ __device__ __forceinline__ uint64_t list_compact(uint64_t* buf, uint32_t& n, uin
   // a read round has landed completely before its kept keys are written, and
   // they go to slots at or before their old ones, never into a later round's
   uint32_t w = 0;
+  lor = 0ull;
+  land = ~0ull;
   for (uint32_t c0 = 0; c0 < cnt_in; c0 += 64 * kListChunk) {
     uint64_t k[kListChunk];
 #pragma unroll
@@ -186,7 +172,11 @@ __device__ __forceinline__ uint64_t list_compact(uint64_t* buf, uint32_t& n, uin
     for (int j = 0; j < kListChunk; ++j) {
       const bool keep = c0 + j * 64 + lane < cnt_in && k[j] >= pre;
       const uint64_t m = __ballot(keep);
-      if (keep) buf[w + lane_rank(m)] = k[j];
+      if (keep) {
+        buf[w + lane_rank(m)] = k[j];
+        lor |= k[j];
+        land &= k[j];
+      }
       w += uint32_t(__builtin_popcountll(m));
     }
   }

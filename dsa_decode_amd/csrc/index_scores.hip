@@ -491,7 +491,8 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
   uint64_t* fbuf = FILTER && rok ? fo.keys + (size_t(r) * gridDim.x + blockIdx.x) * size_t(fo.cap) : nullptr;
   uint32_t fn = 0;
   uint64_t fthr = 0;
-  float fthr_s = -INFINITY;  // the score of fthr's hi: hi >= fthr's hi exactly when the score is >= this
+  float fthr_s = -INFINITY;
+  uint64_t flor = 0ull, fland = ~0ull;  // this lane's OR / AND of the keys it listed  // the score of fthr's hi: hi >= fthr's hi exactly when the score is >= this
 
   for (int i8 = 0; i8 < kGemmWaves; ++i8) {
     const int b = sseq[i8];
@@ -568,7 +569,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
 #pragma unroll
         for (int i = 0; i < kGemmWaves; ++i) mx = max(mx, sfn[(s + 1) & 1][i]);
         if (mine && mx > uint32_t(fo.cap - kGemmStage * 16) && fn > uint32_t(fo.target)) {
-          const uint64_t t = list_compact(fbuf, fn, uint32_t(fo.K), uint32_t(fo.target), shist[wave]);
+          const uint64_t t = list_compact(fbuf, fn, uint32_t(fo.K), uint32_t(fo.target), shist[wave], flor, fland);
           fthr = t > fthr ? t : fthr;
           // (a threshold below the key of -FLT_MAX stands for no score: keep all)
           fthr_s = uint32_t(fthr >> 32) < 0x00800000u ? -INFINITY : key_float(uint32_t(fthr >> 32));
@@ -635,8 +636,12 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
             const uint64_t m = __ballot(keep);
             if (m) {
               const uint32_t at = fn + add + lane_rank(m);
-              if (keep && at < uint32_t(fo.cap))  // always in range: a shrink leaves <= cap - 256
-                fbuf[at] = (uint64_t(score_key(mine_sc[u])) << 32) | (0xffffffffu - uint32_t(p));
+              if (keep && at < uint32_t(fo.cap)) {  // always in range: a shrink leaves <= cap - 256
+                const uint64_t key = (uint64_t(score_key(mine_sc[u])) << 32) | (0xffffffffu - uint32_t(p));
+                fbuf[at] = key;
+                flor |= key;
+                fland &= key;
+              }
               add += uint32_t(__builtin_popcountll(m));
             }
           }

@@ -715,7 +715,8 @@ def _streamed_vs_oracle(scores: np.ndarray, ids: np.ndarray, tok: np.ndarray, ro
     np.testing.assert_array_equal(tok[rows], ref_tok)
 
 
-@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3), (835, 20000, 2), (100, 20000, 2)])
+@pytest.mark.parametrize("Q,P,B", [(1000, 20000, 2), (4, 65536, 4), (9, 3000, 3), (835, 20000, 2), (100, 20000, 2),
+                                   (8387, 2000, 2)])
 def test_streamed_index_topk_bit_identical(Q, P, B):
     # dsa_index_topk_pools_expand gives the bits of dsa_index_scores +
     # dsa_topk_pools_expand, and those of the oracle's top-k and expansion of
@@ -723,7 +724,9 @@ def test_streamed_index_topk_bit_identical(Q, P, B):
     # per row, rows of two sequences in one workgroup; 835 leaves the last
     # workgroup partial); 4 (decode rows: one block with the split top-k), 9
     # and 100 rows (40 pool ranges per row would outgrow the scores) take the
-    # row-blocked path
+    # row-blocked path, as do 8387 rows of 2000 pools (a 2048-key list would
+    # outgrow the row): blocks of 8384 rows and a last block of 3 that takes
+    # the decode score kernel
     rng = np.random.default_rng(Q + P)
     H, D, kp, K = 32, 128, 4, 512
     W = K * kp + 3
