@@ -762,7 +762,21 @@ __global__ __launch_bounds__(NT) void topk_split_kernel(const float* __restrict_
   const ExpandArgs exr = expand_for_row(ex, row);
   topk_block<NT, KPT1, true, false>(sh, row, blockIdx.x, nsplit, scores, nullptr, P, chunk, 0, K, keys, nullptr,
                                     ExpandArgs{});
-  // every thread's winner stores are complete before the row's counter moves
+  // Ordering of the hand-over (what release / acquire at agent scope would
+  // give, built from its parts).  On gfx950 an agent-scope release is a
+  // write-back of the L2's dirty lines followed by a wait for the workgroup's
+  // stores to complete, and an agent-scope acquire invalidates the caches that
+  // are not coherent across the XCDs.  Here the only data handed over are the
+  // winners, and they are stored with agent-scope atomics, which write through
+  // to the device's coherence point and leave no dirty line of theirs in the
+  // L2: the write-back has nothing of this hand-over to do, and the wait below
+  // (every thread's stores acknowledged, then the workgroup barrier) is the
+  // rest of the release.  The ticket is an agent-scope atomic at that same
+  // point, so it moves only after the winners are there.  On the other side
+  // the merging workgroup reads the winners only with agent-scope atomic loads,
+  // which are served at the coherence point and never from a stale cache line,
+  // which is what the acquire's invalidation would otherwise ensure.
+  // (Measured: the full release + acquire cost ~12 µs per launch here.)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
