@@ -405,11 +405,13 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // pool range in a list of fo.cap keys, leaving out the pools that score below
 // its threshold (dsa_select.hpp: such a key has K larger keys in the row).
 // A list that could not take the next stage is shrunk by a radix select that
-// raises the threshold; the waves publish their list lengths in LDS at every
-// stage, and when one list is full every wave whose list holds more than the
-// target shrinks it in the same stage, so that the shrinks overlap rather
-// than each holding the workgroup at the stage barrier (measured on the
-// prefill chunk's scores + top-k, same run: 1.89 -> 1.80 ms).  The list of row r and
+// raises the threshold.  A wave whose list is full after a stage stamps that
+// stage in LDS, and at the next stage every wave whose list holds more than
+// the target shrinks it too, so that the shrinks overlap rather than each
+// holding the workgroup at the stage barrier (measured on the prefill
+// chunk's scores + top-k, same run: 1.89 -> 1.80 ms; a full list is shrunk
+// on its own length, so the stamp decides only when the others shrink, never
+// whether a full list does).  The list of row r and
 // pool range x is fo.keys[(r * gridDim.x + x) * fo.cap ..], its length
 // fo.counts[r * gridDim.x + x]; a top-k over the lists gives the row's K
 // largest keys.  The scores themselves are those of the storing kernel, bit
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
   __shared__ float srs[2][kGemmStage * 16];  // scale / sigma per pool of a stage
   __shared__ int sseq[kGemmWaves];
   __shared__ __attribute__((aligned(16))) uint32_t shist[FILTER ? kGemmWaves : 1][256];  // list shrinks
-  __shared__ uint32_t sfn[2][kGemmWaves];  // FILTER: list lengths after the appends of a stage (by parity)
+  __shared__ uint32_t sfull[2];  // FILTER: stamp (pass, stage) + 1 of the last stage that left a list full (by parity)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, ln = lane & 15;
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
       stage_row_store(rin, ghi[rr], glo[rr], sQB[rr], sW[rr], u - rr * H * 8);
     }
     if (lane == 0) sseq[wave] = ok ? b_row : -1;
-    if (FILTER && lane == 0) sfn[0][wave] = sfn[1][wave] = 0;
+    if (FILTER && tid == 0) sfull[0] = sfull[1] = 0u;
     __syncthreads();
   }
   bf16x8 ahi[NH][4], alo[NH][4];
@@ -562,13 +564,13 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
         // a list that could not take this stage's candidates is shrunk first
         // (before the next stage's keys are requested: their registers are
         // free here)
-        // when any wave's list is full, every wave whose list holds more than
-        // the target shrinks it now, so that the shrinks of a workgroup's
-        // waves overlap instead of each holding the others at the barrier
-        uint32_t mx = 0;
-#pragma unroll
-        for (int i = 0; i < kGemmWaves; ++i) mx = max(mx, sfn[(s + 1) & 1][i]);
-        if (mine && mx > uint32_t(fo.cap - kGemmStage * 16) && fn > uint32_t(fo.target)) {
+        // a full list is shrunk now; so is every list above the target when
+        // some wave's list was full after the last stage (its stamp: the
+        // shrinks of a workgroup's waves overlap instead of each holding the
+        // others at the barrier)
+        const uint32_t room = uint32_t(fo.cap - kGemmStage * 16);
+        const bool any_full = s > 0 && sfull[(s + 1) & 1] == ((uint32_t(i8) << 16) | uint32_t(s));
+        if (mine && (fn > room || (any_full && fn > uint32_t(fo.target)))) {
           const uint64_t t = list_compact(fbuf, fn, uint32_t(fo.K), uint32_t(fo.target), shist[wave], flor, fland);
           fthr = t > fthr ? t : fthr;
           // (a threshold below the key of -FLT_MAX stands for no score: keep all)
@@ -626,17 +628,25 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
           // append the candidates whose score reaches the threshold's (a
           // superset of the keys >= the threshold: the score map is
           // monotone); at most 256, and the list has room for them.  The keys
-          // are formed only when some lane keeps one.
+          // are formed only when some lane keeps one (one ballot per stage:
+          // after the first shrinks most stages keep nothing).
           uint32_t add = 0;
+          bool keep[NU];
+          bool any = false;
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
             const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
-            const bool keep = p < P_max && vcur[u] != 0 && long(p) * kp <= last_ok && mine_sc[u] >= fthr_s &&
-                              mine_sc[u] > -INFINITY;
-            const uint64_t m = __ballot(keep);
-            if (m) {
+            keep[u] = p < P_max && vcur[u] != 0 && long(p) * kp <= last_ok && mine_sc[u] >= fthr_s &&
+                      mine_sc[u] > -INFINITY;
+            any = any || keep[u];
+          }
+          if (__ballot(any)) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+              const uint64_t m = __ballot(keep[u]);
               const uint32_t at = fn + add + lane_rank(m);
-              if (keep && at < uint32_t(fo.cap)) {  // always in range: a shrink leaves <= cap - 256
+              if (keep[u] && at < uint32_t(fo.cap)) {  // always in range: a shrink leaves <= cap - 256
                 const uint64_t key = (uint64_t(score_key(mine_sc[u])) << 32) | (0xffffffffu - uint32_t(p));
                 fbuf[at] = key;
                 flor |= key;
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
             }
           }
           fn += add;
-          if (lane == 0) sfn[s & 1][wave] = fn;
+          if (lane == 0 && fn > uint32_t(fo.cap - kGemmStage * 16)) sfull[s & 1] = ((uint32_t(i8) << 16) | uint32_t(s)) + 1u;
         } else {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
