@@ -223,6 +223,15 @@ def test_streamed_index_topk_refuses_bad_arguments_and_sizes_workspace(lib):
     filtered = DSA_TOPK_COUNTER_BYTES + 4096 * 2048 * 8 + 4096 * 4
     assert filtered > 512 * 32768 * 4
     assert lib.dsa_index_topk_workspace_bytes(4096, 32768, 512) == filtered
+    # larger select_k: lists of 4096 keys (K = 1024; 1024 rows -> 4 pool ranges
+    # per row) and of 8192 keys (K = 2048; 2048 rows -> 2 ranges, 256 MiB of
+    # lists, the most the filtered path takes)
+    assert lib.dsa_index_topk_workspace_bytes(1024, 32768, 1024) == \
+        DSA_TOPK_COUNTER_BYTES + 1024 * 4 * 4096 * 8 + 1024 * 4 * 4
+    assert lib.dsa_index_topk_workspace_bytes(2048, 32768, 2048) == \
+        DSA_TOPK_COUNTER_BYTES + 2048 * 2 * 8192 * 8 + 2048 * 2 * 4
+    # 8192 rows at K = 2048 would take 512 MiB of lists: the row-blocked layout
+    assert lib.dsa_index_topk_workspace_bytes(8192, 32768, 2048) == 512 * 32768 * 4
     # few rows: one block, the split top-k's workspace (counter block first) plus the scores
     n = lib.dsa_index_topk_workspace_bytes(4, 65536, 512)
     assert n >= lib.dsa_topk_workspace_bytes(4, 65536, 512) + 4 * 65536 * 4

@@ -870,6 +870,43 @@ def test_filtered_index_topk_shaped_score_rows(kind, Q, P, H, K):
                 assert rho > 0.95 if kind == "rising" else rho < -0.95
 
 
+def test_streamed_index_topk_paths_share_one_workspace():
+    # one workspace for both paths of dsa_index_topk_pools_expand, called in
+    # turn: the filtered path (1000 rows of 20000 pools) writes its lists past
+    # the top-k counter block and leaves that block zero, so the row-blocked
+    # path's split top-k (4 decode rows of 65536 pools, whose merge counters
+    # live there) still gives the unfused calls' bits, and so does the
+    # filtered path after it
+    cases = []
+    for Q, P, B in ((1000, 20000, 2), (4, 65536, 4)):
+        rng = np.random.default_rng(Q + 7)
+        H, D, kp, K = 32, 128, 4, 512
+        W = K * kp
+        k_pool = torch.from_numpy(rng.standard_normal((B, P, D)).astype(np.float32)).to(torch.bfloat16)
+        q = torch.from_numpy(rng.standard_normal((Q, H, D)).astype(np.float32)).to(torch.bfloat16)
+        w = torch.from_numpy((rng.random((Q, H)) / H).astype(np.float32))
+        gamma = torch.from_numpy((1 + 0.02 * rng.standard_normal(D)).astype(np.float32))
+        beta = torch.from_numpy((0.02 * rng.standard_normal(D)).astype(np.float32))
+        ps = np.broadcast_to(7 + kp * np.arange(P, dtype=np.int32), (B, P)).copy()
+        pv = (rng.random((B, P)) > 0.02).astype(np.uint8)
+        row_seq = np.sort(rng.integers(0, B, Q)).astype(np.int32)
+        row_pos = (7 + kp * P - 1 - rng.integers(0, 40, Q)).astype(np.int32)
+        args = (dev(q), dev(w), D ** -0.5, dev(tile_pool_cache(k_pool)), dev(torch.from_numpy(ps)),
+                dev(torch.from_numpy(pv)), dev(gamma), dev(beta), 1e-5, dev(torch.from_numpy(row_seq)),
+                dev(torch.from_numpy(row_pos)), kp)
+        scores = ops().dsa_index_scores(*args)
+        ref = ops().dsa_topk_pools_expand(scores, K, args[9], args[4], kp, W)
+        cases.append((args, K, W, ref, ops().dsa_index_topk_workspace_bytes(Q, P, K)))
+    ws = ops().topk_workspace(max(c[4] for c in cases))
+    for args, K, W, (ids_a, tok_a), _ in cases + cases:
+        ids_b, tok_b = ops().dsa_index_topk_pools_expand(*args, K, W, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ids_a, ids_b)
+        assert torch.equal(tok_a, tok_b)
+    from dsa_decode_amd._lib import DSA_TOPK_COUNTER_BYTES
+    assert not ws[:DSA_TOPK_COUNTER_BYTES].any()
+
+
 def test_bound_call_keeps_its_buffers_and_sizes_its_workspace():
     # a pre-bound top-k made from temporaries (output created inline, no
     # workspace given, on the decode shape whose split rows need a workspace)
