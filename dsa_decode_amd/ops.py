@@ -191,10 +191,12 @@ def dsa_index_topk_workspace_bytes(Q: int, P_max: int, K: int) -> int:
 def dsa_index_topk_pools_expand(q, w, scale: float, k_pool, pool_start, pool_valid, ln_gamma, ln_beta,
                                 ln_eps: float, row_seq, row_pos, kpool: int, K: int, W: int, pool_ids=None,
                                 token_ids=None, workspace=None):
-    """dsa_index_scores then dsa_topk_pools_expand over row blocks whose scores
-    fit 64 MiB -> (pool_ids [Q, K], token_ids [Q, W]), bit-identical to the two
-    calls.  A workspace passed in must come from topk_workspace (the top-k
-    counters at its start must be zero)."""
+    """dsa_index_scores then dsa_topk_pools_expand without the [Q, P_max] score
+    tensor -> (pool_ids [Q, K], token_ids [Q, W]), bit-identical to the two
+    calls: on the many-row score kernel's shapes the kernel keeps per-row
+    candidate lists instead of scores, elsewhere the rows run in blocks of at
+    most 64 MiB of scores.  A workspace passed in must come from
+    topk_workspace (the top-k counters at its start must be zero)."""
     Q, H, D = q.shape
     B, P_max = pool_start.shape
     _check_pool_cache(k_pool, B, P_max, D)
