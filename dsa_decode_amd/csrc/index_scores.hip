@@ -404,8 +404,10 @@ __global__ __launch_bounds__(kIsThreads) __attribute__((amdgpu_waves_per_eu(2)))
 // keys (the top-k order keys of score and pool index) over its workgroup's
 // pool range in a list of fo.cap keys, leaving out the pools that score below
 // its threshold (dsa_select.hpp: such a key has K larger keys in the row).
-// A list that could not take the next stage is shrunk by a radix select that
-// raises the threshold.  A wave whose list is full after a stage stamps that
+// The wave visits the stages of its range in a scrambled order (below), so
+// that scores trending along the pool index fill the lists no faster than
+// random ones.  A list that could not take the next stage is shrunk by a
+// radix select that raises the threshold.  A wave whose list is full after a stage stamps that
 // stage in LDS, and at the next stage every wave whose list holds more than
 // the target shrinks it too, so that the shrinks overlap rather than each
 // holding the workgroup at the stage barrier (measured on the prefill
@@ -513,6 +515,20 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     constexpr int NU = kGemmStage / 4;           // scores per lane and stage
     u32x4 xk[TW][4];
     uint8_t vl[NU];
+    // FILTER: the wave visits its range's stages in a scrambled order, stage
+    // s -> block s * pstep mod nstage (pstep a prime that does not divide
+    // nstage), so that scores trending along the pool index fill the lists no
+    // faster than scores in random order; a block is still 16 contiguous
+    // tiles, and every workgroup takes the same order.  The block of the next
+    // stage is formed by one addition.
+    int pstep = 1;
+    if (FILTER) {
+      pstep = 37;
+      if (nstage % pstep == 0) pstep = 41;
+      if (nstage % pstep == 0) pstep = 43;
+      pstep %= nstage > 0 ? nstage : 1;
+    }
+    auto next_blk = [&](int b) { b += pstep; return b >= nstage ? b - nstage : b; };
     auto fetch = [&](int s) {
 #pragma unroll
       for (int e = 0; e < TW; ++e) {
@@ -559,8 +575,10 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
     for (int u = 0; u < NU; ++u) vcur[u] = vl[u];
     publish(0);
     __syncthreads();
+    int bc = 0;  // the block of stage s
     for (int s = 0; s < nstage; ++s) {
       const int buf = s & 1;
+      const int bn = next_blk(bc);  // the block of stage s + 1
       if constexpr (FILTER) {
         // a list that could not take this stage's candidates is shrunk first
         // (before the next stage's keys are requested: their registers are
@@ -580,7 +598,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
           fthr_p = none ? 0xffffffffu : 0xffffffffu - uint32_t(fthr);
         }
       }
-      if (s + 1 < nstage) fetch(s + 1);  // in flight while stage s is computed
+      if (s + 1 < nstage) fetch(bn);  // in flight while stage s is computed
       if (mine) {
         float mine_sc[NU];
 #pragma unroll
@@ -641,7 +659,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
           bool any = false;
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+            const int p = (tb + kGemmStage * bc + kg + 4 * u) * 16 + ln;
             keep[u] = p < P_max && vcur[u] != 0 && long(p) * kp <= last_ok && mine_sc[u] > -INFINITY &&
                       (mine_sc[u] > fthr_s || (mine_sc[u] == fthr_s && uint32_t(p) <= fthr_p));
             any = any || keep[u];
@@ -649,7 +667,7 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
           if (__ballot(any)) {
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-              const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+              const int p = (tb + kGemmStage * bc + kg + 4 * u) * 16 + ln;
               const uint64_t m = __ballot(keep[u]);
               const uint32_t at = fn + add + lane_rank(m);
               if (keep[u] && at < uint32_t(fo.cap)) {  // always in range: a shrink leaves <= cap - 256
@@ -666,12 +684,13 @@ __global__ __launch_bounds__(kGemmWaves * 64) void index_scores_gemm(
         } else {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
-            const int p = (tb + kGemmStage * s + kg + 4 * u) * 16 + ln;
+            const int p = (tb + kGemmStage * bc + kg + 4 * u) * 16 + ln;
             if (p < P_max) srow[p] = (vcur[u] != 0 && long(p) * kp <= last_ok) ? mine_sc[u] : -INFINITY;
           }
         }
       }
       __builtin_amdgcn_s_setprio(0);
+      bc = bn;
       if (s + 1 < nstage) {
         publish(s + 1);
 #pragma unroll

@@ -264,6 +264,53 @@ def test_topk_shapes_ties_and_padding(Q, P, K, ties):
     check_topk(s.numpy(), K)
 
 
+def _shaped_score_rows(kind: str, Q: int, P: int, seed: int) -> np.ndarray:
+    """fp32 score rows [Q, P] of a chosen shape along the pool index (each row
+    shifted by its own offset): "rising" (a candidate list keeps growing),
+    "falling", "equal" (one value per row: the order is the pool index alone),
+    "random" (with ties, +-0, -inf holes, a short row and an empty row)."""
+    rng = np.random.default_rng(seed)
+    off = rng.standard_normal((Q, 1)).astype(np.float32)
+    t = np.arange(P, dtype=np.float32)[None, :] / P
+    if kind == "rising":
+        s = off + t
+    elif kind == "falling":
+        s = off - t
+    elif kind == "equal":
+        s = np.broadcast_to(off, (Q, P)).copy()
+    else:
+        s = synth.random_scores(Q, P, seed=seed, tie_levels=64, neg_inf_frac=0.2, signed_zeros=True).numpy()
+        s[0, : P - 100] = -np.inf      # a row with fewer candidates than K
+        s[1, :] = -np.inf              # a row with none
+    return np.ascontiguousarray(s, dtype=np.float32)
+
+
+@pytest.mark.parametrize("kind,Q,P,K", [("rising", 512, 32768, 512), ("falling", 300, 20000, 100),
+                                        ("equal", 256, 32768, 512), ("random", 260, 40000, 512),
+                                        ("random", 300, 9000, 8), ("rising", 256, 16384, 1000),
+                                        ("random", 256, 32768, 2048)])
+def test_topk_shaped_rows_many_rows(kind, Q, P, K):
+    # many rows (one workgroup per row, or chunk and merge launches for rows
+    # over 32768) whose scores rise or fall along the pool index, tie
+    # throughout, or are random with ties, +-0, holes, a short row and an
+    # empty row: bit-exact against the oracle's top-k, with and without
+    # expansion
+    s = _shaped_score_rows(kind, Q, P, seed=Q + P + K)
+    ref = O.topk_pools(s, K)
+    sd = dev(torch.from_numpy(s))
+    got = ops().dsa_topk_pools(sd, K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
+    kp, W = 4, 4 * K + 3
+    ps = dev(torch.from_numpy((3 + kp * np.arange(P, dtype=np.int32))[None, :]))
+    row_seq = dev(torch.zeros(Q, dtype=torch.int32))
+    ids, tok = ops().dsa_topk_pools_expand(sd, K, row_seq, ps, kp, W)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+    np.testing.assert_array_equal(tok.cpu().numpy(),
+                                  O.expand_selection(ref, np.zeros(Q, np.int32), ps.cpu().numpy(), kp, W))
+
+
 def test_topk_workspace_reuse_across_calls_and_shapes():
     # one zero-filled workspace for successive calls of different shapes: each
     # call must leave the counter block at the workspace's start at zero, or
