@@ -715,6 +715,7 @@ def bench_prefill(args) -> int:
     ms = (t1 - t0) * 1e3 / args.steps
     achieved = flops / (score_us * 1e-6) / 1e12
     fused_achieved = flops / (fused_us * 1e-6) / 1e12
+    topk_bytes = Q * P * 4 + Q * K * 4 + Q * W * 4
     # sparse MLA: per (row, listed id) 2*Hm*Dl flops for the logits and as many for the values
     listed = int((tok >= 0).sum().item())
     mla_flops = 4 * wl.Hm * wl.Dl * listed
@@ -732,6 +733,12 @@ def bench_prefill(args) -> int:
         # the unfused score kernel (reference, not in the step)
         "index_scores_gemm": {"launch_us": round(score_us, 2), "achieved": round(achieved, 1),
                               "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
+        # the unfused top-k + expand (reference): it reads the [Q, P] fp32 scores and writes the
+        # pool ids and token ids, against the HBM peak
+        "topk_pools_expand": {"launch_us": round(topk_us, 2), "algorithmic_bytes": topk_bytes,
+                              "achieved": round(topk_bytes / (topk_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s",
+                              "frac": round(topk_bytes / (topk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     dom = "index_topk_pools_expand" if fused_us >= mla_us else "mla_rows64w8_mfma"
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, ip, mi, comp, k_pool, args.cpu_seconds)
