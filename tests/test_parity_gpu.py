@@ -873,7 +873,7 @@ def _shaped_rows_inputs(kind: str, Q: int, P: int, B: int, H: int, seed: int):
 @pytest.mark.parametrize("kind,Q,P,H,K", [("rising", 4096, 32768, 32, 512), ("equal", 2048, 32768, 32, 512),
                                           ("falling", 1024, 32768, 16, 100), ("codebook", 2048, 32768, 32, 512),
                                           ("rising", 1024, 32768, 32, 1024), ("equal", 515, 20000, 16, 8),
-                                          ("codebook", 600, 20003, 32, 512)])
+                                          ("codebook", 600, 20003, 32, 512), ("rising", 2048, 32768, 32, 2048)])
 def test_filtered_index_topk_shaped_score_rows(kind, Q, P, H, K):
     # the filtered path of dsa_index_topk_pools_expand (bf16, D = 128, H = 16
     # or 32, Q > 64: each score-kernel wave keeps a list of its row's
@@ -881,7 +881,8 @@ def test_filtered_index_topk_shaped_score_rows(kind, Q, P, H, K):
     # of dsa_index_scores + dsa_topk_pools_expand and the oracle's top-k and
     # expansion of the same scores.  The cases cover 1 (4096 rows), 2, 4, 7
     # (600 rows of 20003 pools: a partial last tile) and 8 pool ranges per row
-    # (515 rows, the last workgroup partial), K = 8 .. 1024
+    # (515 rows, the last workgroup partial), K = 8 .. 2048 (lists of 8192 keys,
+    # read over several rounds by a shrink)
     # (lists of 2048 and 4096 keys), and score rows that force shrinks every
     # other stage (rising), ties through the index bits (equal, codebook)
     args, row_seq, ps, kp = _shaped_rows_inputs(kind, Q, P, 2, H, seed=Q + K)
