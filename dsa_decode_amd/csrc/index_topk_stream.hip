@@ -27,10 +27,10 @@
 
 namespace dsa {
 
-constexpr long kStreamScoreBytes = 64L << 20;  // fp32 scores held at once
+constexpr long kBlockScoreBytes = 64L << 20;  // fp32 scores held at once
 
-static int stream_rows(int Q, int P_max) {
-  long r = kStreamScoreBytes / (4L * P_max);
+static int block_rows(int Q, int P_max) {
+  long r = kBlockScoreBytes / (4L * P_max);
   if (r >= Q) r = Q;
   else if (r >= 8) r = r / 8 * 8;
   if (r < 1) r = 1;
@@ -38,7 +38,7 @@ static int stream_rows(int Q, int P_max) {
   return int(r);
 }
 
-static size_t stream_align(size_t v) { return (v + 255) & ~size_t(255); }
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // Filtered path: list capacity (a power of two with room for K keys, one
 // score stage of 256 and as much again, so that shrinks are rare).  The path
@@ -64,15 +64,15 @@ static bool filter_fits(int Q, int P_max, int K) {
 // row-blocked call on the same workspace still finds it zero), then the lists,
 // then their lengths.
 static size_t filter_keys_bytes(int Q, int P_max, int K) {
-  return stream_align(size_t(Q) * filter_ranges(Q, P_max, INT_MAX) * list_cap(K) * sizeof(uint64_t));
+  return align256(size_t(Q) * filter_ranges(Q, P_max, INT_MAX) * list_cap(K) * sizeof(uint64_t));
 }
 static size_t filter_bytes(int Q, int P_max, int K) {
   return DSA_TOPK_COUNTER_BYTES + filter_keys_bytes(Q, P_max, K) +
          size_t(Q) * filter_ranges(Q, P_max, INT_MAX) * sizeof(uint32_t);
 }
 
-static size_t stream_topk_bytes(int Q, int P_max, int K) {
-  const int R = stream_rows(Q, P_max);
+static size_t block_topk_bytes(int Q, int P_max, int K) {
+  const int R = block_rows(Q, P_max);
   size_t t = dsa_topk_workspace_bytes(R, P_max, K);
   const int rem = Q % R;
   if (rem) {
@@ -88,8 +88,8 @@ using namespace dsa;
 
 extern "C" size_t dsa_index_topk_workspace_bytes(int Q, int P_max, int K) {
   if (Q <= 0 || P_max <= 0 || K <= 0) return 0;
-  const int R = stream_rows(Q, P_max);
-  const size_t blocked = stream_align(stream_topk_bytes(Q, P_max, K)) + size_t(R) * P_max * sizeof(float);
+  const int R = block_rows(Q, P_max);
+  const size_t blocked = align256(block_topk_bytes(Q, P_max, K)) + size_t(R) * P_max * sizeof(float);
   if (!filter_fits(Q, P_max, K)) return blocked;
   const size_t filtered = filter_bytes(Q, P_max, K);
   return filtered > blocked ? filtered : blocked;
@@ -128,10 +128,10 @@ extern "C" int dsa_index_topk_pools_expand(const void* q, const float* w, float 
     if (st) return st;
     return topk_lists(keys, counts, nseg, cap, Q, P_max, K, pool_ids, row_seq, pool_start, B, kpool, token_ids, W, s);
   }
-  const int R = stream_rows(Q, P_max);
-  const size_t tk_bytes = stream_topk_bytes(Q, P_max, K);
+  const int R = block_rows(Q, P_max);
+  const size_t tk_bytes = block_topk_bytes(Q, P_max, K);
   void* tk_ws = tk_bytes ? workspace : nullptr;
-  float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) + stream_align(tk_bytes));
+  float* sc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(tk_bytes));
   const size_t elt = dtype == DSA_BF16 ? 2 : 4;
   for (int r0 = 0; r0 < Q; r0 += R) {
     const int Rb = Q - r0 < R ? Q - r0 : R;
