@@ -698,6 +698,20 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
   int lbase[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) lbase[kk] = ln * kMlaDl + (4 * (kk ^ (swl >> 2)) + (kg ^ (swl & 3))) * 8;
+  // element offsets of the transposing reads of the value contraction (rows
+  // t0 and t0 + 4 of 16-column block blk; +32 rows for the second 32 tokens)
+  int voff[2][4];
+  {
+    const int t0 = 8 * kg + (ln >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int tt = t0 + 4 * e;
+        const int col = 64 * w + 16 * blk + 4 * (ln & 3);
+        voff[e][blk] = tt * kMlaDl + (((col >> 3) ^ mla_swz(tt)) << 3) + (col & 7);
+      }
+  }
 
   for (int ib = 0; ib < nblk; ++ib) {
     const int cur = ib & 1;
@@ -726,12 +740,12 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
       for (int t = 0; t < 2; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[k]), acc[t]);
     }
     float m = -INFINITY;
+    const uint32_t vm = uint32_t(vmask >> (32 * th + 4 * kg));  // bit 16 t + j: token 32 th + 16 t + 4 kg + j
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tok = 32 * th + 16 * t + 4 * kg + j;
-        acc[t][j] = (vmask >> tok) & 1ull ? acc[t][j] * scale_log2 : -INFINITY;
+        acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
         m = fmaxf(m, acc[t][j]);
       }
     m = fmaxf(m, __shfl_xor(m, 16, kWave));
@@ -782,23 +796,17 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
       for (int kk = 0; kk < 4; ++kk) o[ht][kk] *= alpha;
     }
     // O^T over latent eighth w: A = kv^T (16 dl x 32 tokens, two transposing
-    // reads), B = P^T (32 tokens x 16 heads); addresses recomputed per block
-    int lv = lane;
-    asm volatile("" : "+v"(lv));
-    const int kgv = lv >> 4, lnv = lv & 15;
+    // reads), B = P^T (32 tokens x 16 heads)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pb[4];
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht)
         pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[16 * ht + ln][mla_pidx(ln, 32 * ks + 8 * kg)]));
-      const int t0 = 32 * ks + 8 * kgv + (lnv >> 2), t1 = t0 + 4;
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const int col = 64 * w + 16 * blk + 4 * (lnv & 3);
-        const int pc = col >> 3, off = col & 7;
-        const u32x2 lo = lds_read_tr16(rows + t0 * kMlaDl + ((pc ^ mla_swz(t0)) << 3) + off);
-        const u32x2 hi = lds_read_tr16(rows + t1 * kMlaDl + ((pc ^ mla_swz(t1)) << 3) + off);
+        const u32x2 lo = lds_read_tr16(rows + 32 * ks * kMlaDl + voff[0][blk]);
+        const u32x2 hi = lds_read_tr16(rows + 32 * ks * kMlaDl + voff[1][blk]);
         const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) o[ht][blk] = mfma16x16x32(av, pb[ht], o[ht][blk]);
