@@ -832,6 +832,229 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
+// Many-rows path for 64 heads as a two-stage pipeline over blocks of 32 ids.
+// Waves 0..3 form, for block k, the logits of heads 16w .. 16w+15 (q^T of the
+// 16 heads in registers), each head's running maximum and sum, P, and the
+// factor that rescales what was accumulated; waves 4..7 meanwhile accumulate
+// latent quarter w - 4 of O^T for all 64 heads over block k - 1.  Every SIMD
+// then holds one wave of each kind, so the matrix cores run one wave's
+// contraction while the other forms its softmax, and a block needs a single
+// barrier.  The row's checked ids go into LDS first; rows pass through four
+// LDS buffers: the logits waves gather block k + 2 while blocks k and k - 1
+// are read, with buffer loads to LDS (an absent id reads past the end of the
+// resource and lands as zeros), so the loop's only memory loads are the eight
+// of each block's gather and a counted wait finds the block before.  A tile
+// of 16 heads whose factors are all exactly 1 is not rescaled.
+constexpr int kMlaPipeIds = 32;
+constexpr int kMlaPipeThreads = 512;
+constexpr int kMlaPipeMaxW = 4096;
+constexpr long kMlaPipeMaxT = 1L << 21;  // T_max * 1024 bytes of a sequence's rows below 2^31
+
+struct alignas(16) MlaPipeShared {
+  uint16_t rows[4][kMlaPipeIds][kMlaDl];  // latent rows, pieces swizzled by mla_swz (128 KiB)
+  uint16_t p[2][64][kMlaPipeIds];         // P[head][token] of a block (mla_pidx32), two blocks
+  float alpha[2][64];                     // per head: the rescale factor a block brings
+  float lfin[64];                         // per head: the final sum
+  int32_t ids[kMlaPipeMaxW];              // the row's ids, -1 when absent or out of range
+};
+
+// element index of token tok (< 32) of head h in its P row: the 8-token group
+// g sits at g ^ ((h >> 2) & 3), so the 16-byte reads of 16 heads (lane (ln,
+// kg) reads group kg of head ln) fill every slot of a pass
+__device__ __forceinline__ int mla_pidx32(int h, int tok) {
+  return (((tok >> 3) ^ ((h >> 2) & 3)) << 3) | (tok & 7);
+}
+
+// wait until at most 8 (or none) of this wave's vector-memory loads are in flight
+__device__ __forceinline__ void wait_vm_at_most(bool eight) {
+  if (eight)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu(2))) void mla_rows64_pipe(
+    const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ token_ids, int B, int T_max, int W,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int Hm = 64, NI = kMlaPipeIds;
+  __shared__ MlaPipeShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, ln = lane & 15;
+  const int r = blockIdx.x;
+  const int b = row_seq[r];
+  const bool bok = b >= 0 && b < B;
+  const int32_t* ids_row = token_ids + size_t(r) * W;
+  const int nblk = (W + NI - 1) / NI;  // the host launches this path for 64 < W <= kMlaPipeMaxW
+  const bool logit_wave = w < 4;
+  const int hq = 16 * w + ln;  // logits waves: the head whose logits this lane forms
+
+  for (int c = tid; c < nblk * NI; c += kMlaPipeThreads) {
+    const int v = c < W ? ids_row[c] : -1;
+    sh.ids[c] = (bok && v >= 0 && v < T_max) ? v : -1;
+  }
+  __syncthreads();
+  const auto rs = make_rsrc(kv + size_t(bok ? b : 0) * T_max * kMlaDl, uint32_t(T_max) * (kMlaDl * 2));
+  // rows 8w .. 8w+7 of block blk: 8 loads
+  auto gather = [&](int blk) {
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(&sh.ids[blk * NI + 8 * w]);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(&sh.ids[blk * NI + 8 * w + 4]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 8 * w + i;
+      const int id = __builtin_amdgcn_readfirstlane(int(i < 4 ? v0[i] : v1[i - 4]));
+      const uint32_t off = (id >= 0 ? uint32_t(id) * (kMlaDl * 2) : 0x80000000u) + 16u * uint32_t(lane ^ mla_swz(t));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(&sh.rows[blk & 3][t][0]), 16, off, 0, 0, 0);
+    }
+  };
+
+  if (logit_wave) {
+    u32x4 qv[16];
+    {
+      const uint16_t* qrow = q_lat + (size_t(r) * Hm + hq) * kMlaDl + 8 * kg;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
+    }
+    gather(0);
+    if (nblk > 1) gather(1);
+    // q is in before the loop (the waits the compiler places for it then stay
+    // out of the loop, where they would also wait for gathers in flight)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(qv[j]));
+    wait_vm_at_most(nblk > 1);  // block 0's rows are in
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int swl = mla_swz(ln);
+    int lbase[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) lbase[kk] = ln * kMlaDl + (4 * (kk ^ (swl >> 2)) + (kg ^ (swl & 3))) * 8;
+    float M_run = -INFINITY, l_run = 0.f;
+    for (int k = 0; k <= nblk; ++k) {
+      if (k < nblk) {
+        const bool more = k + 2 < nblk;
+        if (more) gather(k + 2);
+        // logits of tokens 16 t + 4 kg + j (t < 2, j < 4) for head hq
+        const uint16_t* rows = &sh.rows[k & 3][0][0];
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          bf16x8 a[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[kk & 3] + 16 * t * kMlaDl + (kk >> 2) * 128));
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[kk]), acc[t]);
+        }
+        // bit 16 t + j: token 16 t + 4 kg + j
+        const uint32_t vm = uint32_t(__ballot(lane < NI && sh.ids[k * NI + (lane & (NI - 1))] >= 0) >> (4 * kg));
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
+            m = fmaxf(m, acc[t][j]);
+          }
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const float M_new = fmaxf(M_run, m);
+        const float M_use = M_new == -INFINITY ? 0.f : M_new;
+        const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
+        float lh = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(acc[t][j] - M_use);
+            lh += p[j];
+          }
+          *reinterpret_cast<u32x2*>(&sh.p[k & 1][hq][mla_pidx32(hq, 16 * t + 4 * kg)]) =
+              u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+        }
+        lh += __shfl_xor(lh, 16, kWave);
+        lh += __shfl_xor(lh, 32, kWave);
+        l_run = fmaf(l_run, alpha, lh);
+        M_run = M_new;
+        if (kg == 0) sh.alpha[k & 1][hq] = alpha;
+        // block k + 1's rows (gathered one block ago) are in: only this
+        // block's gather may still be in flight
+        wait_vm_at_most(more);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (kg == 0) {
+      sh.lfin[hq] = l_run;
+      if (lse)
+        lse[size_t(r) * Hm + hq] =
+            l_run > 0.f ? (M_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
+    }
+  } else {
+    const int vq = w - 4;  // latent quarter
+    f32x4 o[4][8];         // [head tile][16-wide latent block]
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) o[ht][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // element offsets of the transposing reads (rows t0 and t0 + 4, block blk)
+    int voff[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        const int tt = 8 * kg + (ln >> 2) + 4 * e;
+        const int col = 128 * vq + 16 * blk + 4 * (ln & 3);
+        voff[e][blk] = tt * kMlaDl + (((col >> 3) ^ mla_swz(tt)) << 3) + (col & 7);
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int k = 0; k <= nblk; ++k) {
+      if (k >= 1) {
+        const int kb = k - 1;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const float a = sh.alpha[kb & 1][16 * ht + ln];
+          if (__ballot(a != 1.f)) {
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) o[ht][blk] *= a;
+          }
+        }
+        bf16x8 pb[4];
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+          pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[kb & 1][16 * ht + ln][mla_pidx32(ln, 8 * kg)]));
+        const uint16_t* rows = &sh.rows[kb & 3][0][0];
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+          const u32x2 lo = lds_read_tr16(rows + voff[0][blk]);
+          const u32x2 hi = lds_read_tr16(rows + voff[1][blk]);
+          const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) o[ht][blk] = mfma16x16x32(av, pb[ht], o[ht][blk]);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the sums are in
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int h = 16 * ht + ln;
+      const float l = sh.lfin[h];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      uint16_t* dst = out + (size_t(r) * Hm + h) * kMlaDl + 128 * vq + 4 * kg;
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        u32x2 pkd;
+        pkd[0] = pack2bf(o[ht][blk][0] * inv, o[ht][blk][1] * inv);
+        pkd[1] = pack2bf(o[ht][blk][2] * inv, o[ht][blk][3] * inv);
+        *reinterpret_cast<u32x2*>(dst + blk * 16) = pkd;
+      }
+    }
+    return;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // (logits waves) the sums are out
+}
+
 // Merge split partials: out = sum_s e^{lse_s} O_s / sum_s e^{lse_s}.  One
 // wave per (row, head group, latent quarter, 16-channel block): lane (kg, ln)
 // owns channels 4kg .. 4kg+3 of the block for head ln.  Splits are taken
@@ -1030,6 +1253,11 @@ static int mla_launch(const void* q_lat, const void* kv, const int32_t* row_seq,
     return launch_status();
   }
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  if (pl.rows && Hm == 64 && T_max < kMlaPipeMaxT && W <= kMlaPipeMaxW) {
+    hipLaunchKernelGGL(mla_rows64_pipe, dim3(Q), dim3(kMlaPipeThreads), 0, s, (const uint16_t*)q_lat,
+                       (const uint16_t*)kv, row_seq, token_ids, B, T_max, W, scale_log2, (uint16_t*)out, lse);
+    return launch_status();
+  }
   if (pl.rows && Hm == 64) {
     hipLaunchKernelGGL(mla_rows64w8_mfma, dim3(Q), dim3(kMla8Threads), 0, s, (const uint16_t*)q_lat,
                        (const uint16_t*)kv, row_seq, token_ids, Q, B, T_max, W, scale_log2, (uint16_t*)out,
