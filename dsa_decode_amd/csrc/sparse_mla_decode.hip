@@ -956,8 +956,12 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
             acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
             m = fmaxf(m, acc[t][j]);
           }
-        m = fmaxf(m, __shfl_xor(m, 16, kWave));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        {
+          const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+          const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+        }
         const float M_new = fmaxf(M_run, m);
         const float M_use = M_new == -INFINITY ? 0.f : M_new;
         const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
@@ -973,8 +977,12 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
           *reinterpret_cast<u32x2*>(&sh.p[k & 1][hq][mla_pidx32(hq, 16 * t + 4 * kg)]) =
               u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
         }
-        lh += __shfl_xor(lh, 16, kWave);
-        lh += __shfl_xor(lh, 32, kWave);
+        {
+          const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
+          lh = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+          const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
+          lh = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+        }
         l_run = fmaf(l_run, alpha, lh);
         M_run = M_new;
         if (kg == 0) sh.alpha[k & 1][hq] = alpha;
