@@ -727,7 +727,7 @@ def bench_prefill(args) -> int:
                                     "frac": round(fused_achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "algorithmic_flops": flops,
                                     "kernels": "index_scores_gemm<2, true> + topk_kernel<512, 4, false, true>"},
-        "mla_rows64w8_mfma": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
+        "mla_rows64_pipe": {"launch_us": round(mla_us, 2), "achieved": round(mla_achieved, 1),
                               "frac": round(mla_achieved / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": mla_flops,
                               "listed_ids": listed},
         # the unfused score kernel (reference, not in the step)
@@ -740,7 +740,7 @@ def bench_prefill(args) -> int:
                               "unit": "GB/s",
                               "frac": round(topk_bytes / (topk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
     }
-    dom = "index_topk_pools_expand" if fused_us >= mla_us else "mla_rows64w8_mfma"
+    dom = "index_topk_pools_expand" if fused_us >= mla_us else "mla_rows64_pipe"
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, ip, mi, comp, k_pool, args.cpu_seconds)
     line = {
         "metric": "DSA prefill chunk (index_scores + top-k + expand + sparse MLA) chunks/s; % MFMA roofline",

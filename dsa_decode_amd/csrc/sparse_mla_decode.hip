@@ -82,6 +82,23 @@ __device__ __forceinline__ int mla_pswz(int h) { return (h & 1) | ((h & 2) << 1)
 // element index of token tok of head h in its P row
 __device__ __forceinline__ int mla_pidx(int h, int tok) { return ((((tok >> 3) ^ mla_pswz(h)) << 3) | (tok & 7)); }
 
+// Maximum and sum of v over the four lane groups (kg = 0..3) of the lanes
+// that share ln, in every lane: the swaps of 16- and 32-lane rows (the same
+// register as both operands, so the two results hold the partner rows'
+// values), without a round trip through LDS.
+__device__ __forceinline__ float lane_groups_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_groups_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Transposing LDS read: within each group of 16 lanes, lane i receives element
@@ -299,8 +316,7 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     x[j] = (vmask >> (4 * kg + j)) & 1u ? lg * scale_log2 : -INFINITY;
     m = fmaxf(m, x[j]);
   }
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  m = lane_groups_max(m);
   const float m_use = m == -INFINITY ? 0.f : m;
   float p[4], l = 0.f;
 #pragma unroll
@@ -308,8 +324,7 @@ __global__ __launch_bounds__(kMla2Threads) void mla_decode_mfma(
     p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
     l += p[j];
   }
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  l = lane_groups_sum(l);
   auto& X = sh.x[half];
   // the value operand: P, times the token's scale for fp8 rows (l stays the
   // sum of the unscaled P)
@@ -530,8 +545,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       x[j] = (vmask >> (4 * kg + j)) & 1u ? (acc0[j] + acc1[j]) * scale_log2 : -INFINITY;
       m = fmaxf(m, x[j]);
     }
-    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    m = lane_groups_max(m);
     const float m_use = m == -INFINITY ? 0.f : m;
     float p[4], l = 0.f;
 #pragma unroll
@@ -539,8 +553,7 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2))
       p[j] = __builtin_amdgcn_exp2f(x[j] - m_use);
       l += p[j];
     }
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = lane_groups_sum(l);
     *reinterpret_cast<u32x2*>(&sh.x.p[ln][mla_pidx(ln, 16 * w + 4 * kg)]) =
         u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
     if (kg == 0) {
@@ -748,8 +761,7 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
         acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
         m = fmaxf(m, acc[t][j]);
       }
-    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    m = lane_groups_max(m);
     // the two token halves' maxima meet first, so that P is formed against the
     // block's new running maximum and the value contraction reads it as it is
     // (a factor per half applied as P is read cost more than this barrier)
@@ -773,8 +785,7 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
       *reinterpret_cast<u32x2*>(&sh.p[hq][mla_pidx(hq, 32 * th + 16 * t + 4 * kg)]) =
           u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
     }
-    lh += __shfl_xor(lh, 16, kWave);
-    lh += __shfl_xor(lh, 32, kWave);
+    lh = lane_groups_sum(lh);
     if (kg == 0) sh.l[hq][th] = lh;
     // P and the halves' sums of all 64 heads published: LDS writes done, then
     // the barrier alone (the next block's gather stays in flight)
@@ -956,12 +967,7 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
             acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
             m = fmaxf(m, acc[t][j]);
           }
-        {
-          const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-          const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          m = fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-        }
+        m = lane_groups_max(m);
         const float M_new = fmaxf(M_run, m);
         const float M_use = M_new == -INFINITY ? 0.f : M_new;
         const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
@@ -977,12 +983,7 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
           *reinterpret_cast<u32x2*>(&sh.p[k & 1][hq][mla_pidx32(hq, 16 * t + 4 * kg)]) =
               u32x2{pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
         }
-        {
-          const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
-          lh = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-          const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(lh), __float_as_uint(lh), false, false);
-          lh = __uint_as_float(c[0]) + __uint_as_float(c[1]);
-        }
+        lh = lane_groups_sum(lh);
         l_run = fmaf(l_run, alpha, lh);
         M_run = M_new;
         if (kg == 0) sh.alpha[k & 1][hq] = alpha;
