@@ -540,7 +540,11 @@ def _distinct_ids_below(rng, Q, W, limits, hole_frac=0.0):
 
 
 @pytest.mark.parametrize("Q,Hm,W", [(256, 64, 1000), (1024, 16, 130), (300, 64, 2048), (1030, 16, 200),
-                                    (600, 32, 333)])
+                                    (600, 32, 333),
+                                    # 64 heads: three 32-id blocks (the last holding one id), three
+                                    # full ones, the largest list the pipelined kernel takes, and one
+                                    # id more (the eight-wave kernel)
+                                    (256, 64, 65), (256, 64, 96), (256, 64, 4096), (256, 64, 4097)])
 def test_mla_many_rows_path(Q, Hm, W):
     # enough (row, head group) pairs that each workgroup runs over all of its
     # row's ids with the online softmax (no split partials): ragged last
