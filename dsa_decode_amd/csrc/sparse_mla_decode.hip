@@ -109,6 +109,27 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Eight transposing 16-bit LDS reads (as lds_read_tr16, at LDS byte
+// addresses a[i]) issued together and waited for within the statement (a
+// load written in asm must not be left in flight when the statement ends).
+// The compiler does not see these as reads of LDS that a load-to-LDS may be
+// writing, so it places no wait for such loads before them.
+__device__ __forceinline__ void lds_read_tr16_x8(u32x2 (&v)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Transposing LDS read of 8-bit elements: within each group of 16 lanes, lane
 // i receives byte (i & 7) of the 8-byte words read by lanes 2e + (i >> 3),
 // e = 0..7 (so lanes 2e, 2e+1 reading row e's bytes 0..7 and 8..15 of a
@@ -844,25 +865,32 @@ __global__ __launch_bounds__(kMla8Threads) __attribute__((amdgpu_waves_per_eu(2)
 }
 
 // Many-rows path for 64 heads as a two-stage pipeline over blocks of 32 ids.
-// Waves 0..3 form, for block k, the logits of heads 16w .. 16w+15 (q^T of the
-// 16 heads in registers), each head's running maximum and sum, P, and the
-// factor that rescales what was accumulated; waves 4..7 meanwhile accumulate
-// latent quarter w - 4 of O^T for all 64 heads over block k - 1.  Every SIMD
-// then holds one wave of each kind, so the matrix cores run one wave's
-// contraction while the other forms its softmax, and a block needs a single
-// barrier.  The row's checked ids go into LDS first; rows pass through four
-// LDS buffers: the logits waves gather block k + 2 while blocks k and k - 1
-// are read, with buffer loads to LDS (an absent id reads past the end of the
-// resource and lands as zeros), so the loop's only memory loads are the eight
-// of each block's gather and a counted wait finds the block before.  A tile
-// of 16 heads whose factors are all exactly 1 is not rescaled.
+// Waves 0..3 form, for block k, the softmax of heads 16w .. 16w+15 (each
+// head's running maximum and sum, P, and the factor that rescales what was
+// accumulated) while they issue block k + 1's logits (q^T of the 16 heads in
+// registers), so that the matrix cores run under the softmax's chain; waves
+// 4..7 meanwhile accumulate latent quarter w - 4 of O^T for all 64 heads over
+// block k - 1.  Every SIMD holds one wave of each kind and a block needs a
+// single barrier.  The row's checked ids go into LDS first; rows pass through
+// four LDS buffers, laid out by latent quarter: the value wave of quarter q,
+// once it has read its quarter of block k - 1, gathers its quarter of block
+// k + 3 into the same buffer (buffer loads to LDS, four rows' quarters per
+// load; an absent id reads past the end of the resource and lands as zeros),
+// so no wave waits for another before overwriting, and a counted wait finds
+// the block needed next.  Each head's P is formed against a reference that
+// moves only when a block's maximum exceeds it by more than 8 (log2 units),
+// so P <= 2^8 and the rescale factor is exactly 1 for most blocks; O and the
+// sum share the reference, so the result and lse are those of the running
+// maximum.  A tile of 16 heads whose factors are all exactly 1 is not
+// rescaled.
 constexpr int kMlaPipeIds = 32;
 constexpr int kMlaPipeThreads = 512;
 constexpr int kMlaPipeMaxW = 4096;
 constexpr long kMlaPipeMaxT = 1L << 21;  // T_max * 1024 bytes of a sequence's rows below 2^31
 
 struct alignas(16) MlaPipeShared {
-  uint16_t rows[4][kMlaPipeIds][kMlaDl];  // latent rows, pieces swizzled by mla_swz (128 KiB)
+  uint16_t rows[4][4][kMlaPipeIds][128];  // [buffer][latent quarter][token][128], 16-byte pieces
+                                          // swizzled by mla_swz (128 KiB)
   uint16_t p[2][64][kMlaPipeIds];         // P[head][token] of a block (mla_pidx32), two blocks
   float alpha[2][64];                     // per head: the rescale factor a block brings
   float lfin[64];                         // per head: the final sum
@@ -898,65 +926,49 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
   const bool bok = b >= 0 && b < B;
   const int32_t* ids_row = token_ids + size_t(r) * W;
   const int nblk = (W + NI - 1) / NI;  // the host launches this path for 64 < W <= kMlaPipeMaxW
-  const bool logit_wave = w < 4;
-  const int hq = 16 * w + ln;  // logits waves: the head whose logits this lane forms
-
   for (int c = tid; c < nblk * NI; c += kMlaPipeThreads) {
     const int v = c < W ? ids_row[c] : -1;
     sh.ids[c] = (bok && v >= 0 && v < T_max) ? v : -1;
   }
   __syncthreads();
-  const auto rs = make_rsrc(kv + size_t(bok ? b : 0) * T_max * kMlaDl, uint32_t(T_max) * (kMlaDl * 2));
-  // rows 8w .. 8w+7 of block blk: 8 loads
-  auto gather = [&](int blk) {
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(&sh.ids[blk * NI + 8 * w]);
-    const u32x4 v1 = *reinterpret_cast<const u32x4*>(&sh.ids[blk * NI + 8 * w + 4]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = 8 * w + i;
-      const int id = __builtin_amdgcn_readfirstlane(int(i < 4 ? v0[i] : v1[i - 4]));
-      const uint32_t off = (id >= 0 ? uint32_t(id) * (kMlaDl * 2) : 0x80000000u) + 16u * uint32_t(lane ^ mla_swz(t));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(&sh.rows[blk & 3][t][0]), 16, off, 0, 0, 0);
-    }
-  };
 
-  if (logit_wave) {
+  if (w < 4) {
+    const int hq = 16 * w + ln;  // the head whose logits this lane forms
     u32x4 qv[16];
     {
       const uint16_t* qrow = q_lat + (size_t(r) * Hm + hq) * kMlaDl + 8 * kg;
 #pragma unroll
       for (int j = 0; j < 16; ++j) qv[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * j);
     }
-    gather(0);
-    if (nblk > 1) gather(1);
-    // q is in before the loop (the waits the compiler places for it then stay
-    // out of the loop, where they would also wait for gathers in flight)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(qv[j]));
-    wait_vm_at_most(nblk > 1);  // block 0's rows are in
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int swl = mla_swz(ln);
     int lbase[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) lbase[kk] = ln * kMlaDl + (4 * (kk ^ (swl >> 2)) + (kg ^ (swl & 3))) * 8;
+    for (int kk = 0; kk < 4; ++kk) lbase[kk] = ln * 128 + (4 * (kk ^ (swl >> 2)) + (kg ^ (swl & 3))) * 8;
+    // logits of tokens 16 t + 4 kg + j (t < 2, j < 4) of block blk for head hq
+    auto logits = [&](int blk, f32x4 (&acc)[2]) {
+      const uint16_t* rows = &sh.rows[blk & 3][0][0][0];
+      acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        bf16x8 a[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[kk & 3] + 16 * t * 128 + (kk >> 2) * (NI * 128)));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[kk]), acc[t]);
+      }
+    };
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // blocks 0 and 1 are in
+    f32x4 cur[2];
+    logits(0, cur);
     float M_run = -INFINITY, l_run = 0.f;
     for (int k = 0; k <= nblk; ++k) {
       if (k < nblk) {
-        const bool more = k + 2 < nblk;
-        if (more) gather(k + 2);
-        // logits of tokens 16 t + 4 kg + j (t < 2, j < 4) for head hq
-        const uint16_t* rows = &sh.rows[k & 3][0][0];
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          bf16x8 a[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            a[t] = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + lbase[kk & 3] + 16 * t * kMlaDl + (kk >> 2) * 128));
-#pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] = mfma16x16x32(a[t], as_bf16x8(qv[kk]), acc[t]);
-        }
+        // block k + 1's logits (read from a stale buffer past the last block,
+        // and then not used)
+        f32x4 nxt[2];
+        logits(k + 1, nxt);
         // bit 16 t + j: token 16 t + 4 kg + j
         const uint32_t vm = uint32_t(__ballot(lane < NI && sh.ids[k * NI + (lane & (NI - 1))] >= 0) >> (4 * kg));
         float m = -INFINITY;
@@ -964,20 +976,23 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            acc[t][j] = (vm >> (16 * t + j)) & 1u ? acc[t][j] * scale_log2 : -INFINITY;
-            m = fmaxf(m, acc[t][j]);
+            cur[t][j] = (vm >> (16 * t + j)) & 1u ? cur[t][j] * scale_log2 : -INFINITY;
+            m = fmaxf(m, cur[t][j]);
           }
         m = lane_groups_max(m);
-        const float M_new = fmaxf(M_run, m);
+        // the reference moves when the block's maximum exceeds it by more than
+        // 8 (M_run = -inf: any finite maximum)
+        const bool upd = m > M_run + 8.f;
+        const float alpha = !upd ? 1.f : (M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - m));
+        const float M_new = upd ? m : M_run;
         const float M_use = M_new == -INFINITY ? 0.f : M_new;
-        const float alpha = M_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M_run - M_use);
         float lh = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           float p[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(acc[t][j] - M_use);
+            p[j] = __builtin_amdgcn_exp2f(cur[t][j] - M_use);
             lh += p[j];
           }
           *reinterpret_cast<u32x2*>(&sh.p[k & 1][hq][mla_pidx32(hq, 16 * t + 4 * kg)]) =
@@ -987,9 +1002,8 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
         l_run = fmaf(l_run, alpha, lh);
         M_run = M_new;
         if (kg == 0) sh.alpha[k & 1][hq] = alpha;
-        // block k + 1's rows (gathered one block ago) are in: only this
-        // block's gather may still be in flight
-        wait_vm_at_most(more);
+        cur[0] = nxt[0];
+        cur[1] = nxt[1];
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
@@ -1001,21 +1015,40 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
     }
   } else {
     const int vq = w - 4;  // latent quarter
-    f32x4 o[4][8];         // [head tile][16-wide latent block]
+    const auto rs = make_rsrc(kv + size_t(bok ? b : 0) * T_max * kMlaDl, uint32_t(T_max) * (kMlaDl * 2));
+    // quarter vq of the 32 rows of block blk, four rows per load (lane i: row
+    // 4g + i / 16, piece slot i % 16): 8 loads
+    auto gather = [&](int blk) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int t = 4 * g + (lane >> 4);
+        const int id = sh.ids[blk * NI + t];
+        const uint32_t off = (id >= 0 ? uint32_t(id) * (kMlaDl * 2) : 0x80000000u) +
+                             16u * uint32_t(16 * vq + ((lane & 15) ^ mla_swz(t)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(&sh.rows[blk & 3][vq][4 * g][0]), 16, off, 0, 0, 0);
+      }
+    };
+    f32x4 o[4][8];  // [head tile][16-wide latent block]
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) o[ht][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // element offsets of the transposing reads (rows t0 and t0 + 4, block blk)
-    int voff[2][8];
+    // byte offsets (in a buffer) of the transposing reads: rows t0 and t0 + 4,
+    // 16-column block blk of quarter vq
+    uint32_t voff[2][8];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int blk = 0; blk < 8; ++blk) {
         const int tt = 8 * kg + (ln >> 2) + 4 * e;
-        const int col = 128 * vq + 16 * blk + 4 * (ln & 3);
-        voff[e][blk] = tt * kMlaDl + (((col >> 3) ^ mla_swz(tt)) << 3) + (col & 7);
+        const int col = 16 * blk + 4 * (ln & 3);
+        voff[e][blk] = 2u * uint32_t(vq * (NI * 128) + tt * 128 + (((col >> 3) ^ mla_swz(tt)) << 3) + (col & 7));
       }
+    gather(0);
+    if (nblk > 1) gather(1);
+    if (nblk > 2) gather(2);
+    wait_vm_at_most(nblk > 2);  // blocks 0 and 1 are in
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     for (int k = 0; k <= nblk; ++k) {
       if (k >= 1) {
@@ -1032,16 +1065,33 @@ __global__ __launch_bounds__(kMlaPipeThreads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht)
           pb[ht] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sh.p[kb & 1][16 * ht + ln][mla_pidx32(ln, 8 * kg)]));
-        const uint16_t* rows = &sh.rows[kb & 3][0][0];
+        const uint32_t rb = uint32_t(reinterpret_cast<uintptr_t>(&sh.rows[kb & 3][0][0][0]));
+        u32x2 tv[2][8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          uint32_t ad[8];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            ad[2 * bb] = rb + voff[0][4 * hb + bb];
+            ad[2 * bb + 1] = rb + voff[1][4 * hb + bb];
+          }
+          lds_read_tr16_x8(tv[hb], ad);
+        }
+        // this wave is done with its quarter of the buffer: block k + 3's goes in
+        if (kb + 4 < nblk) gather(kb + 4);
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-          const u32x2 lo = lds_read_tr16(rows + voff[0][blk]);
-          const u32x2 hi = lds_read_tr16(rows + voff[1][blk]);
+          const u32x2 lo = tv[blk >> 2][2 * (blk & 3)], hi = tv[blk >> 2][2 * (blk & 3) + 1];
           const bf16x8 av = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) o[ht][blk] = mfma16x16x32(av, pb[ht], o[ht][blk]);
         }
+      } else if (3 < nblk) {
+        gather(3);  // the fourth buffer is free from the start
       }
+      // block k + 2's quarter is in (the logits waves read it in the next
+      // block): only block k + 3's gather may still be in flight
+      wait_vm_at_most(k + 3 < nblk);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the sums are in
