@@ -178,46 +178,41 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     int max_new, T* __restrict__ k_pool, int32_t* __restrict__ pool_start,
     uint8_t* __restrict__ pool_valid, int32_t* __restrict__ n_pools, int32_t* __restrict__ first_valid) {
   const int b = blockIdx.x, tid = threadIdx.x;
-  __shared__ int s_f, s_lo, s_hi, s_form;
+  __shared__ int s_f;
   int L = seq_len[b];
   L = L < 0 ? 0 : (L > T_max ? T_max : L);
   int f0 = first_valid[b];
+  int n0 = n_pools[b];  // read with the other state, not after the scan
   f0 = f0 < 0 ? 0 : (f0 > L ? L : f0);
+  n0 = n0 < 0 ? 0 : (n0 > P_max ? P_max : n0);
   const uint8_t* v = valid + size_t(b) * T_max;
-  if (tid == 0) s_f = L;
-  __syncthreads();
-  // first valid token at or after f0 (windows of 16 tokens per thread)
-  for (int base = f0; base < L; base += kAppendThreads * 16) {
-    const int t0 = base + tid * 16;
-    int found = L;
-    for (int i = 0; i < 16; ++i) {
-      const int t = t0 + i;
-      if (t < L && v[t] != 0) { found = t; break; }
-    }
-    if (found < L) atomicMin(&s_f, found);
+  int f = f0;
+  if (!(f0 < L && v[f0] != 0)) {  // uniform; a still-valid anchor (the usual case) needs no scan
+    if (tid == 0) s_f = L;
     __syncthreads();
-    const int fw = s_f;
-    __syncthreads();
-    if (fw < L) break;  // uniform
-  }
-  if (tid == 0) {
-    const int f = s_f;
-    int n0 = n_pools[b];
-    n0 = n0 < 0 ? 0 : (n0 > P_max ? P_max : n0);
-    const int start = (f == f0) ? n0 : 0;  // a new anchor: no pool existed before it
-    const int P_new = f < L ? (L - f) / KP : 0;
-    if (P_new >= start) {
-      s_lo = start;
-      s_hi = min(P_new, start + max_new);
-      s_form = 1;
-    } else {
-      s_lo = P_new;
-      s_hi = start;
-      s_form = 0;
+    // first valid token at or after f0 (windows of 16 tokens per thread)
+    for (int base = f0; base < L; base += kAppendThreads * 16) {
+      const int t0 = base + tid * 16;
+      int found = L;
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + i;
+        if (t < L && v[t] != 0) { found = t; break; }
+      }
+      if (found < L) atomicMin(&s_f, found);
+      __syncthreads();
+      const int fw = s_f;
+      __syncthreads();
+      if (fw < L) break;  // uniform
     }
+    f = s_f;
   }
-  __syncthreads();
-  const int f = s_f, lo = s_lo, hi = s_hi, form = s_form;
+  // the pools to form (or, for a length that shrank, to clear); the same
+  // values in every thread
+  const int start = (f == f0) ? n0 : 0;  // a new anchor: no pool existed before it
+  const int P_new = f < L ? (L - f) / KP : 0;
+  const int form = P_new >= start ? 1 : 0;
+  const int lo = form ? start : P_new;
+  const int hi = form ? min(P_new, start + max_new) : start;
   const int groups = D >> 3;
   const int P_tiles = pool_tiles(P_max);
   const long items = long(hi - lo) * groups;
@@ -232,6 +227,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
       empty_piece<T>(b, p, c0, P_tiles, D, P_max, k_pool, pool_start, pool_valid);
     }
   }
+  __syncthreads();  // every wave has read the old state
   if (tid == 0) {
     first_valid[b] = f;
     n_pools[b] = form ? hi : lo;
